@@ -1,0 +1,163 @@
+/*
+ * jetlong.h -- C ABI of the MI355X (gfx950) Jet-Long bifocal RoPE attention
+ * library (libjetlong.so).
+ *
+ * Method: "Jet-Long: Efficient Long-Context Extension with Dynamic Bifocal
+ * RoPE", §3.  For a call that holds L tokens, a query at position q and a key
+ * at position k (0-based, k <= q) score
+ *     local  (q - k <= w0):  RoPE(x_q, q)    . RoPE(x_k, k)        (§3, Eq. 1)
+ *     remote (q - k >  w0):  RoPE(x_q, f(q)) . RoPE(x_k, f(k))
+ * with f(x) = floor(x / G) (§3.1, Eq. 3) and G = max(1, ceil(L / w_pretrained))
+ * (§3.1, Eq. 2).  The cache holds RoPE(x_k, k) and is never rewritten (§3.2,
+ * Eq. 4); the remote view is formed on the fly by rotating stored vectors by
+ * f(p) - p (§3.2, Eq. 5).  The two views are merged exactly inside one online
+ * softmax, which is the inclusion-exclusion merge of §3.3 (Eq. 6) with the
+ * overlap term cancelled by masking instead of subtraction.
+ *
+ * Conventions (readings where the pages are silent):
+ *   - RoPE pairs channel i with channel i + D/2, theta_i = base^(-2i/D).
+ *   - Query head h reads KV head h / (Hq / Hkv).
+ *   - sm_scale multiplies the raw dot product; softmax and LSE are fp32,
+ *     LSE is a natural logarithm.
+ *
+ * Memory: every pointer argument named q, k, v, out, lse, k_cache, v_cache,
+ * table and workspace is a DEVICE pointer, owned by the caller, and must be
+ * 16-byte aligned.  Tensors are dense row-major in the layout given at each
+ * call.  The library never allocates device memory, keeps no per-call state
+ * and never synchronises: work is enqueued on `hip_stream` (a hipStream_t;
+ * NULL = the default stream) and the call returns.
+ *
+ * Errors: every argument is validated on the host before any HIP call.  A
+ * non-zero return leaves every output untouched; jl_last_error() then
+ * describes the failure (thread-local, valid until the next call on that
+ * thread).  JL_EHIP is returned if a kernel launch fails.
+ */
+#ifndef JETLONG_H
+#define JETLONG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define JL_API __attribute__((visibility("default")))
+#else
+#define JL_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    JL_OK = 0,
+    JL_EINVAL = 1,        /* bad shape, value or pointer                        */
+    JL_EUNSUPPORTED = 2,  /* valid but not implemented (head_dim, dtype, GQA)   */
+    JL_EHIP = 3,          /* HIP runtime / launch failure                       */
+    JL_ESPACE = 4         /* table or workspace smaller than required           */
+};
+
+enum { JL_F32 = 0, JL_BF16 = 1 };
+
+/* Message for the last non-OK return on this thread ("" if none). */
+JL_API const char* jl_last_error(void);
+
+/* Library ABI version (increments on any signature or layout change). */
+JL_API int jl_version(void);
+
+/*
+ * jl_schedule -- §3.1 Eq. (2) and the correction-angle table for §3.2 Eq. (5).
+ *
+ *   *G_out = max(1, ceil(L / w_pretrained)).
+ *   *table_bytes_needed = bytes of a table covering correction offsets
+ *       n = p - f(p) for every position p < L, for this head_dim.
+ *
+ * If `table` is non-NULL, the call also enqueues on `hip_stream` a float64
+ * kernel that fills the table for (head_dim, rope_base) covering p < L.  The
+ * table does not depend on G or w_pretrained, so one table built for the
+ * largest length serves every later call with L no larger and the same
+ * head_dim and rope_base (decode steps that cross a G change included).
+ *
+ * Table layout (opaque to callers; documented for completeness): a 64-byte
+ * header {magic, head_dim, n_cover, rope_base}, then fp32 (cos, sin) pairs
+ * TL[l][i] = (cos, sin)(l * theta_i) for l < 512 and
+ * TH[h][i] = (cos, sin)(512 * h * theta_i) for h <= (L-1)/512, i < D/2, all
+ * angles formed in float64 and rounded once to fp32.
+ *
+ * With table == NULL no HIP call is made.  Errors: L < 1, w_pretrained < 1,
+ * head_dim not in {64, 128} (JL_EUNSUPPORTED), rope_base <= 1 or not finite,
+ * G_out == NULL -> JL_EINVAL; table_bytes < needed -> JL_ESPACE.
+ */
+JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base,
+                int64_t* G_out, void* table, size_t table_bytes,
+                size_t* table_bytes_needed, void* hip_stream);
+
+/*
+ * jl_bifocal_prefill -- causal bifocal attention over a whole sequence
+ * (§3 Eq. 1 with §3.1 Eqs. 2-3, §3.2 Eq. 5, §3.3 Eq. 6).
+ *
+ *   q   [B, L, Hq,  D]  in_dtype   stored RoPE(x, p) for positions p = 0..L-1
+ *   k   [B, L, Hkv, D]  in_dtype   stored RoPE(x, p)
+ *   v   [B, L, Hkv, D]  in_dtype
+ *   out [B, L, Hq,  D]  out_dtype
+ *   lse [B, Hq, L]      fp32 natural-log softmax denominators, or NULL
+ *
+ * G is computed from this call's L.  dtypes: in = JL_F32 -> out = JL_F32;
+ * in = JL_BF16 -> out in {JL_BF16, JL_F32}.  D in {64, 128}; Hq / Hkv in
+ * {1, 2, 4, 8}.  `table` must have been filled by jl_schedule for this D and
+ * rope_base with coverage >= L; if its header does not match (D, rope_base,
+ * coverage) the kernels write NaN to `out` (the host cannot read it).
+ *
+ * Errors: JL_EINVAL for B, L, Hq, Hkv < 1, Hq % Hkv != 0, w0 < 0,
+ * w_pretrained < 1, sm_scale not finite or <= 0, NULL or misaligned pointers;
+ * JL_EUNSUPPORTED for other D, dtype pairs or GQA ratios; JL_ESPACE if
+ * table_bytes is below jl_schedule's requirement for L.
+ */
+JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Hq,
+                       int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained,
+                       double rope_base, float sm_scale, const void* table,
+                       size_t table_bytes, void* hip_stream);
+
+/*
+ * jl_bifocal_decode_workspace -- bytes of fp32 scratch that jl_bifocal_decode
+ * needs for a step that attends L keys (split-KV partials).  Pure host call.
+ */
+JL_API int jl_bifocal_decode_workspace(int64_t B, int64_t Hq, int64_t D, int64_t L, size_t* bytes);
+
+/*
+ * jl_bifocal_decode -- one generation step (§3.2: cached keys are read under
+ * the G of the current length; the cache is not rewritten).
+ *
+ *   q        [B, 1, Hq, D]      bf16, the new token's query at position L-1
+ *   k_cache  [B, Lmax, Hkv, D]  bf16, rows 0..L-1 valid (the caller has
+ *   v_cache  [B, Lmax, Hkv, D]  bf16   already written the new row L-1)
+ *   out      [B, 1, Hq, D]      out_dtype (JL_BF16 or JL_F32)
+ *   lse      [B, Hq]            fp32 natural log, or NULL
+ *
+ * L counts every key including the new one; G = max(1, ceil(L/w_pretrained)).
+ * Keys with (L-1) - k <= w0 are local, the rest remote.  `workspace` must
+ * hold jl_bifocal_decode_workspace(B, Hq, D, L) bytes.  in_dtype must be
+ * JL_BF16.  Errors as for prefill, plus L > Lmax -> JL_EINVAL and a short
+ * workspace -> JL_ESPACE.
+ */
+JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                      float* lse, int in_dtype, int out_dtype, int64_t B, int64_t L,
+                      int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                      int64_t w_pretrained, double rope_base, float sm_scale,
+                      const void* table, size_t table_bytes, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
+
+/*
+ * jl_table_fill_host -- fill a HOST buffer with the same table jl_schedule
+ * writes on the device (same layout, same float64 formulas compiled for the
+ * host).  Lets the table builder be checked without a GPU.  Errors as for
+ * jl_schedule.
+ */
+JL_API int jl_table_fill_host(int64_t L, int64_t head_dim, double rope_base, void* table,
+                       size_t table_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JETLONG_H */

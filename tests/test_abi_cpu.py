@@ -1,0 +1,140 @@
+"""CPU checks of libjetlong.so: it loads, exports every symbol the header
+declares, rejects bad arguments before touching HIP, computes G, and builds
+the correction table exactly as an independent NumPy float64 computation."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import zero_shot_rope_jl_amd as jl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000   # aligned, never dereferenced: every call below fails validation
+
+
+def header_symbols():
+    with open(os.path.join(ROOT, "include", "jetlong.h")) as fh:
+        txt = fh.read()
+    return sorted(set(re.findall(r"JL_API\s+[\w\s\*]+?\b(jl_\w+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    syms = header_symbols()
+    assert syms == sorted(["jl_last_error", "jl_version", "jl_schedule", "jl_bifocal_prefill",
+                           "jl_bifocal_decode_workspace", "jl_bifocal_decode", "jl_table_fill_host"])
+    for s in syms:
+        assert hasattr(jl.lib, s), s
+    assert jl.jl_version() == 1
+
+
+def test_schedule_golden_and_table_size():
+    with open(os.path.join(ROOT, "tests", "golden", "schedule_examples.json")) as fh:
+        for e in json.load(fh)["examples"]:
+            G, need = jl.jl_schedule(e["L"], e["w_pretrained"], 128, 1e6)
+            assert G == e["G"], e["cite"]
+            assert need == 64 + (512 + -(-e["L"] // 512)) * 64 * 8
+
+
+def _sched(L=100, w=10, D=128, base=1e4, G=True, table=None, tbytes=0):
+    g = ctypes.c_int64(-7)
+    need = ctypes.c_size_t(0)
+    rc = jl.lib.jl_schedule(L, w, D, base, ctypes.byref(g) if G else None, table, tbytes,
+                            ctypes.byref(need), None)
+    return rc, g.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=0), jl.JL_EINVAL), (dict(w=0), jl.JL_EINVAL), (dict(D=96), jl.JL_EUNSUPPORTED),
+    (dict(base=1.0), jl.JL_EINVAL), (dict(base=float("nan")), jl.JL_EINVAL), (dict(G=False), jl.JL_EINVAL),
+    (dict(table=FAKE, tbytes=10), jl.JL_ESPACE), (dict(table=FAKE + 4, tbytes=1 << 30), jl.JL_EINVAL),
+])
+def test_schedule_validation(kw, code):
+    rc, g = _sched(**kw)
+    assert rc == code
+    assert jl.jl_last_error()
+    assert g == -7            # output untouched
+
+
+def _prefill(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, L=256, Hq=4,
+             Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE, tb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_prefill(a["q"], a["k"], a["v"], a["out"], a["lse"], a["i"], a["o"], a["B"],
+                                     a["L"], a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"], a["base"],
+                                     a["sc"], a["table"], a["tb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), jl.JL_EINVAL), (dict(table=None), jl.JL_EINVAL), (dict(out=FAKE + 2), jl.JL_EINVAL),
+    (dict(lse=FAKE + 4), jl.JL_EINVAL), (dict(B=0), jl.JL_EINVAL), (dict(L=0), jl.JL_EINVAL),
+    (dict(Hq=3), jl.JL_EINVAL), (dict(w0=-1), jl.JL_EINVAL), (dict(wp=0), jl.JL_EINVAL),
+    (dict(sc=0.0), jl.JL_EINVAL), (dict(sc=float("inf")), jl.JL_EINVAL), (dict(i=5), jl.JL_EINVAL),
+    (dict(L=(1 << 30) + 1), jl.JL_EINVAL), (dict(D=96), jl.JL_EUNSUPPORTED),
+    (dict(i=jl.JL_F32, o=jl.JL_BF16), jl.JL_EUNSUPPORTED), (dict(Hq=32, Hkv=2), jl.JL_EUNSUPPORTED),
+    (dict(Hq=6, Hkv=2), jl.JL_EUNSUPPORTED), (dict(tb=100), jl.JL_ESPACE), (dict(base=0.5), jl.JL_EINVAL),
+])
+def test_prefill_validation(over, code):
+    assert _prefill(**over) == code
+    assert jl.jl_last_error()
+
+
+def _decode(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, L=600, Lmax=700,
+             Hq=8, Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE, tb=1 << 30, ws=FAKE,
+             wsb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_decode(a["q"], a["k"], a["v"], a["out"], a["lse"], a["i"], a["o"], a["B"],
+                                    a["L"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"],
+                                    a["base"], a["sc"], a["table"], a["tb"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ws=None), jl.JL_EINVAL), (dict(Lmax=599), jl.JL_EINVAL), (dict(i=jl.JL_F32, o=jl.JL_F32),
+                                                                    jl.JL_EUNSUPPORTED),
+    (dict(Hq=64, Hkv=2), jl.JL_EUNSUPPORTED), (dict(wsb=16), jl.JL_ESPACE), (dict(tb=64), jl.JL_ESPACE),
+    (dict(w0=-3), jl.JL_EINVAL), (dict(D=32), jl.JL_EUNSUPPORTED), (dict(k=FAKE + 8), jl.JL_EINVAL),
+])
+def test_decode_validation(over, code):
+    assert _decode(**over) == code
+    assert jl.jl_last_error()
+
+
+def test_decode_workspace_size():
+    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 131328) == 32 * 257 * 130 * 4
+    assert jl.jl_bifocal_decode_workspace(2, 4, 64, 1) == 2 * 4 * 1 * 66 * 4
+    with pytest.raises(jl.JetLongError):
+        jl.jl_bifocal_decode_workspace(1, 4, 96, 10)
+
+
+@pytest.mark.parametrize("D,base,L", [(64, 1e4, 512), (128, 1e6, 131328), (128, 5e5, 1)])
+def test_host_table_matches_numpy_float64(D, base, L):
+    buf = jl.jl_table_fill_host(L, D, base)
+    hdr = buf[:64]
+    assert hdr[:4].view(np.uint32)[0] == 0x424C544A
+    assert hdr[4:8].view(np.int32)[0] == D
+    assert hdr[8:16].view(np.int64)[0] == L
+    assert hdr[16:24].view(np.float64)[0] == base
+    nh = -(-L // 512)
+    ent = buf[64:].view(np.float32).reshape(512 + nh, D // 2, 2)
+    theta = base ** (-(2.0 * np.arange(D // 2)) / D)          # independent float64 definition
+    n = np.concatenate([np.arange(512), 512 * np.arange(nh)]).astype(np.float64)
+    ang = n[:, None] * theta[None, :]
+    want = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    ulp = np.spacing(np.abs(want).astype(np.float32))
+    assert np.all(np.abs(ent - want) <= ulp)
+    # composing the two levels reproduces cos/sin(n theta) for every offset n < L
+    ns = np.arange(L) if L <= 4096 else np.unique(np.r_[np.arange(600), np.random.default_rng(0).integers(0, L, 4000), L - 1])
+    lo, hi = ent[ns % 512].astype(np.float64), ent[512 + ns // 512].astype(np.float64)
+    c = hi[..., 0] * lo[..., 0] - hi[..., 1] * lo[..., 1]
+    s = hi[..., 1] * lo[..., 0] + hi[..., 0] * lo[..., 1]
+    a2 = ns[:, None].astype(np.float64) * theta[None, :]
+    assert np.max(np.abs(c - np.cos(a2))) < 3e-7 and np.max(np.abs(s - np.sin(a2))) < 3e-7
+
+
+def test_binding_has_no_cpu_fallback():
+    import zero_shot_rope_jl_amd.binding as b
+    src = open(b.__file__).read()
+    assert "oracle" not in src and "numpy.einsum" not in src and "softmax" not in src

@@ -1,0 +1,185 @@
+"""GPU parity: libjetlong.so against the float64 oracle on the same seeded
+inputs.  Small cases compare every output; the full-size workloads compare
+sampled rows (structural rows at the window and schedule edges plus seeded
+uniform rows) in the launch configuration the benchmark uses."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+import zero_shot_rope_jl_amd as jl
+from gpu_common import (TOL_BF16, TOL_F32, assert_bf16_out_close, max_err, prefill, require_gpu,
+                        to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def small_workload(L, Hq, Hkv, D, w_pre, w0, base=1e4, B=1, dtype="bf16", seed=7, scale=1.0):
+    return si.Workload(f"small{L}", dtype, B, L, Hq, Hkv, D, w0, w_pre, base, seed, global_scale=scale)
+
+
+def run_case(w, out_dtypes=(torch.bfloat16, torch.float32)):
+    require_gpu()
+    x = si.make_prefill_inputs(w)
+    q, k, v = (to_dev(x[n], w.dtype) for n in "qkv")
+    ref, ref_lse = oracle.bifocal_attention(x["q64"], x["k64"], x["v64"], w.w0, w.w_pretrained,
+                                            w.rope_base, w.sm_scale)
+    table = jl.alloc_table(w.L, w.D, w.rope_base)
+    res = {}
+    for od in out_dtypes:
+        out, lse = prefill(q, k, v, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, od, table)
+        res[od] = (out.float().cpu().numpy(), lse.cpu().numpy())
+    return ref, ref_lse, res
+
+
+# ------------------------------------------------------------ tiny fp32
+def test_tiny_fp32_matches_oracle_1e5():
+    w = si.WORKLOADS["tiny"]
+    ref, ref_lse, res = run_case(w, out_dtypes=(torch.float32,))
+    out, lse = res[torch.float32]
+    print("tiny fp32 max err", max_err(out, ref), "lse", max_err(lse, ref_lse))
+    assert max_err(out, ref) <= TOL_F32
+    assert max_err(lse, ref_lse) <= TOL_F32
+
+
+# --------------------------------------------------- small bf16 sweep
+SMALL = [  # (L, Hq, Hkv, D, w_pre, w0, B)
+    (1000, 8, 2, 128, 300, 64, 1),     # G=4, GQA 4, ragged tail
+    (777, 4, 4, 64, 256, 100, 1),      # G=4, no GQA, D=64
+    (1537, 16, 2, 128, 512, 200, 1),   # G=4, GQA 8
+    (640, 2, 1, 128, 128, 0, 1),       # w0=0: only the diagonal is local
+    (300, 4, 2, 64, 1000, 30, 1),      # G=1 identity regime
+    (513, 4, 2, 128, 64, 600, 1),      # w0 >= L: all local
+    (1, 4, 2, 128, 1, 0, 1),           # a single token
+    (65, 4, 2, 64, 1, 3, 1),           # w_pre=1: G=L, f=0
+    (2048, 8, 2, 128, 512, 256, 2),    # batch 2, G=4
+    (1200, 8, 4, 128, 400, 63, 1),     # G=3, w0 not tile aligned
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"L{c[0]}_H{c[1]}x{c[2]}_D{c[3]}_wp{c[4]}_w0{c[5]}_B{c[6]}"
+                                             for c in SMALL])
+def test_small_bf16_matches_oracle(case):
+    L, Hq, Hkv, D, w_pre, w0, B = case
+    w = small_workload(L, Hq, Hkv, D, w_pre, w0, B=B, seed=L + Hq)
+    ref, ref_lse, res = run_case(w)
+    o32, l32 = res[torch.float32]
+    o16, l16 = res[torch.bfloat16]
+    print(case, "fp32-out err", max_err(o32, ref), "bf16-out err", max_err(o16, ref), "lse", max_err(l32, ref_lse))
+    assert max_err(o32, ref) <= TOL_BF16
+    assert max_err(l32, ref_lse) <= TOL_BF16
+    assert_bf16_out_close(o16, ref)
+    assert np.array_equal(l16, l32)   # the statistics do not depend on the output dtype
+
+
+@pytest.mark.parametrize("case", [(700, 4, 2, 64, 200, 50), (333, 8, 2, 128, 100, 17)])
+def test_small_fp32_matches_oracle(case):
+    L, Hq, Hkv, D, w_pre, w0 = case
+    w = small_workload(L, Hq, Hkv, D, w_pre, w0, dtype="f32", seed=L)
+    ref, ref_lse, res = run_case(w, out_dtypes=(torch.float32,))
+    out, lse = res[torch.float32]
+    print(case, "fp32 err", max_err(out, ref))
+    assert max_err(out, ref) <= TOL_F32
+    assert max_err(lse, ref_lse) <= TOL_F32
+
+
+# ------------------------------------------------- exact invariants on GPU
+def test_identity_regime_independent_of_w0_bitwise():
+    require_gpu()
+    w = small_workload(1024, 8, 2, 128, 1024, 0, seed=3)
+    x = si.make_prefill_inputs(w, want_f64=False)
+    q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    table = jl.alloc_table(w.L, w.D, w.rope_base)
+    outs = [prefill(q, k, v, w0, w.w_pretrained, w.rope_base, w.sm_scale, torch.bfloat16, table)[0]
+            for w0 in (0, 100, 2048)]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_run_to_run_bitwise_determinism():
+    require_gpu()
+    w = small_workload(3000, 8, 2, 128, 1000, 128, seed=4)
+    x = si.make_prefill_inputs(w, want_f64=False)
+    q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    a, la = prefill(q, k, v, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, torch.bfloat16)
+    b, lb = prefill(q, k, v, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, torch.bfloat16)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_device_table_equals_host_table():
+    require_gpu()
+    for (L, D, base) in [(512, 64, 1e4), (131328, 128, 1e6)]:
+        t = jl.alloc_table(L, D, base)
+        torch.cuda.synchronize()
+        dev = t.cpu().numpy()
+        host = jl.jl_table_fill_host(L, D, base)
+        assert np.array_equal(dev[:32], host[:32])
+        a = dev[64:].view(np.float32)
+        b = host[64:].view(np.float32)
+        assert np.all(np.abs(a - b) <= np.spacing(np.abs(b)))
+
+
+def test_mismatched_table_poisons_output():
+    require_gpu()
+    w = small_workload(256, 4, 2, 128, 64, 16, seed=5)
+    x = si.make_prefill_inputs(w, want_f64=False)
+    q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    wrong_base = jl.alloc_table(w.L, w.D, 5e5)
+    out, lse = prefill(q, k, v, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, torch.float32, wrong_base)
+    assert torch.isnan(out).all() and torch.isnan(lse).all()
+
+
+# ------------------------------------------------------- decode (small)
+def make_cache(B, Lmax, Hkv, D, seed):
+    rng = np.random.default_rng(seed)
+    kc = si.bf16_bits_from_f32(rng.standard_normal((B, Lmax, Hkv, D), dtype=np.float32))
+    vc = si.bf16_bits_from_f32(rng.standard_normal((B, Lmax, Hkv, D), dtype=np.float32))
+    q = si.bf16_bits_from_f32(rng.standard_normal((B, 1, 8, D), dtype=np.float32))
+    return q, kc, vc
+
+
+@pytest.mark.parametrize("L", [1, 5, 100, 511, 512, 513, 1024, 1537, 2000])
+def test_small_decode_matches_oracle(L):
+    require_gpu()
+    B, Lmax, Hq, Hkv, D, w_pre, w0, base = 2, 2000, 8, 2, 128, 300, 100, 1e4
+    qb, kb, vb = make_cache(B, Lmax, Hkv, D, 11)
+    q, kc, vc = to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16")
+    table = jl.alloc_table(Lmax, D, base)
+    ws = jl.alloc_decode_workspace(B, Hq, D, Lmax)
+    scale = 1 / math.sqrt(D)
+    f64 = lambda a: si.f32_from_bf16_bits(a).astype(np.float64)
+    ref, ref_lse = oracle.decode_attention(f64(qb)[:, 0], f64(kb), f64(vb), L, w0, w_pre, base, scale)
+    for od in (torch.float32, torch.bfloat16):
+        out = torch.empty((B, 1, Hq, D), dtype=od, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        jl.jl_bifocal_decode(q, kc, vc, out, lse, L, w0, w_pre, base, scale, table, ws)
+        torch.cuda.synchronize()
+        o = out.float().cpu().numpy()[:, 0]
+        print(L, od, "decode err", max_err(o, ref), "lse", max_err(lse.cpu().numpy(), ref_lse))
+        if od == torch.float32:
+            assert max_err(o, ref) <= TOL_BF16
+        else:
+            assert_bf16_out_close(o, ref)
+        assert max_err(lse.cpu().numpy(), ref_lse) <= TOL_BF16
+
+
+def test_decode_equals_prefill_last_row():
+    require_gpu()
+    w = small_workload(1500, 8, 2, 128, 400, 128, seed=21)
+    x = si.make_prefill_inputs(w, want_f64=False)
+    q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    table = jl.alloc_table(w.L, w.D, w.rope_base)
+    full, lse_full = prefill(q, k, v, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, torch.float32, table)
+    ws = jl.alloc_decode_workspace(1, w.Hq, w.D, w.L)
+    out = torch.empty((1, 1, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, w.Hq), dtype=torch.float32, device="cuda")
+    jl.jl_bifocal_decode(q[:, -1:].contiguous(), k, v, out, lse, w.L, w.w0, w.w_pretrained, w.rope_base,
+                         w.sm_scale, table, ws)
+    torch.cuda.synchronize()
+    d = max_err(out[:, 0].cpu().numpy(), full[:, -1].cpu().numpy())
+    print("decode vs prefill row", d)
+    assert d <= 5e-3
+    assert max_err(lse.cpu().numpy(), lse_full[:, :, -1].cpu().numpy()) <= 5e-3

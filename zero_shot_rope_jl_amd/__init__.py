@@ -1,0 +1,16 @@
+"""Python binding of libjetlong.so, the gfx950 Jet-Long bifocal RoPE attention
+library ("Jet-Long: Efficient Long-Context Extension with Dynamic Bifocal
+RoPE", §3).
+
+The functions carry the C ABI's names and only marshal arguments: shapes,
+dtypes, device pointers and the current HIP stream are read from torch
+tensors and passed to the library, which does every step of the computation
+in its own kernels.  There is no fallback: if the library is missing the
+import fails, and a non-OK return code raises :class:`JetLongError`.
+"""
+from .binding import (  # noqa: F401
+    JL_BF16, JL_F32, JL_OK, JL_EINVAL, JL_EUNSUPPORTED, JL_EHIP, JL_ESPACE,
+    JetLongError, lib, lib_path, jl_version, jl_last_error, jl_schedule,
+    jl_bifocal_prefill, jl_bifocal_decode, jl_bifocal_decode_workspace,
+    jl_table_fill_host, alloc_table, alloc_decode_workspace,
+)

@@ -1,0 +1,188 @@
+"""ctypes binding of include/jetlong.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(PKG, "libjetlong.so")
+
+JL_OK, JL_EINVAL, JL_EUNSUPPORTED, JL_EHIP, JL_ESPACE = 0, 1, 2, 3, 4
+JL_F32, JL_BF16 = 0, 1
+
+
+class JetLongError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"jetlong error {code}: {message}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"{lib_path} is missing: build it with `python -m zero_shot_rope_jl_amd.build` "
+            "(there is no non-HIP fallback)")
+    L = ctypes.CDLL(lib_path)
+    i64, sz, vp, cp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_char_p
+    L.jl_last_error.restype = cp
+    L.jl_last_error.argtypes = []
+    L.jl_version.restype = ctypes.c_int
+    L.jl_schedule.restype = ctypes.c_int
+    L.jl_schedule.argtypes = [i64, i64, i64, ctypes.c_double, ctypes.POINTER(i64), vp, sz,
+                              ctypes.POINTER(sz), vp]
+    L.jl_table_fill_host.restype = ctypes.c_int
+    L.jl_table_fill_host.argtypes = [i64, i64, ctypes.c_double, vp, sz]
+    L.jl_bifocal_prefill.restype = ctypes.c_int
+    L.jl_bifocal_prefill.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                     i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp]
+    L.jl_bifocal_decode_workspace.restype = ctypes.c_int
+    L.jl_bifocal_decode_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(sz)]
+    L.jl_bifocal_decode.restype = ctypes.c_int
+    L.jl_bifocal_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                    i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
+    return L
+
+
+lib = _load()
+
+
+def jl_last_error() -> str:
+    return lib.jl_last_error().decode()
+
+
+def jl_version() -> int:
+    return lib.jl_version()
+
+
+def _check(rc: int) -> None:
+    if rc != JL_OK:
+        raise JetLongError(rc, jl_last_error())
+
+
+# ------------------------------------------------------------ torch helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return JL_BF16
+    if t.dtype == torch.float32:
+        return JL_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_device(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+# ------------------------------------------------------------------ the ABI
+def jl_schedule(L: int, w_pretrained: int, head_dim: int = 128, rope_base: float = 1e6,
+                table=None, stream=None):
+    """G = max(1, ceil(L / w_pretrained)) and the table size for (L, head_dim).
+
+    If ``table`` (a uint8 device tensor) is given, the correction table for
+    (head_dim, rope_base) covering L positions is filled on the stream.
+    Returns (G, table_bytes_needed)."""
+    G = ctypes.c_int64(0)
+    need = ctypes.c_size_t(0)
+    if table is not None:
+        _need_device(table)
+        rc = lib.jl_schedule(L, w_pretrained, head_dim, rope_base, ctypes.byref(G), _ptr(table),
+                             table.numel() * table.element_size(), ctypes.byref(need), _stream(stream))
+    else:
+        rc = lib.jl_schedule(L, w_pretrained, head_dim, rope_base, ctypes.byref(G), None, 0,
+                             ctypes.byref(need), None)
+    _check(rc)
+    return G.value, need.value
+
+
+def jl_table_fill_host(L: int, head_dim: int, rope_base: float):
+    """Host-built table (numpy uint8 array) with the device table's layout."""
+    import numpy as np
+    need = ctypes.c_size_t(0)
+    _check(lib.jl_schedule(L, 1, head_dim, rope_base, ctypes.byref(ctypes.c_int64(0)), None, 0,
+                           ctypes.byref(need), None))
+    buf = np.zeros(need.value, dtype=np.uint8)
+    _check(lib.jl_table_fill_host(L, head_dim, rope_base, buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes))
+    return buf
+
+
+def alloc_table(L: int, head_dim: int, rope_base: float, device="cuda", stream=None):
+    """Allocate a device table with torch and fill it through jl_schedule."""
+    torch = _torch()
+    _, need = jl_schedule(L, 1, head_dim, rope_base)
+    t = torch.empty(need, dtype=torch.uint8, device=device)
+    jl_schedule(L, 1, head_dim, rope_base, table=t, stream=stream)
+    return t
+
+
+def jl_bifocal_prefill(q, k, v, out, lse, w0: int, w_pretrained: int, rope_base: float,
+                       sm_scale: float, table, stream=None):
+    """q [B,L,Hq,D], k/v [B,L,Hkv,D], out [B,L,Hq,D], lse [B,Hq,L] fp32 or None."""
+    _need_device(q, k, v, out, lse, table)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, L, Hkv, D) or tuple(v.shape) != (B, L, Hkv, D):
+        raise ValueError("k and v must be [B, L, Hkv, D] matching q")
+    if tuple(out.shape) != (B, L, Hq, D):
+        raise ValueError("out must be [B, L, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq, L) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq, L]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    _check(lib.jl_bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
+                                  _dtype_code(out), B, L, Hq, Hkv, D, w0, w_pretrained, rope_base,
+                                  sm_scale, _ptr(table), table.numel() * table.element_size(),
+                                  _stream(stream)))
+    return out, lse
+
+
+def jl_bifocal_decode_workspace(B: int, Hq: int, D: int, L: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.jl_bifocal_decode_workspace(B, Hq, D, L, ctypes.byref(n)))
+    return n.value
+
+
+def alloc_decode_workspace(B: int, Hq: int, D: int, Lmax: int, device="cuda"):
+    torch = _torch()
+    n = jl_bifocal_decode_workspace(B, Hq, D, Lmax)
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def jl_bifocal_decode(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrained: int,
+                      rope_base: float, sm_scale: float, table, workspace, stream=None):
+    """q [B,1,Hq,D] bf16, caches [B,Lmax,Hkv,D] bf16, out [B,1,Hq,D], lse [B,Hq] or None."""
+    _need_device(q, k_cache, v_cache, out, lse, table, workspace)
+    B, one, Hq, D = q.shape
+    _, Lmax, Hkv, Dk = k_cache.shape
+    if one != 1 or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B:
+        raise ValueError("q must be [B,1,Hq,D] and the caches [B,Lmax,Hkv,D]")
+    if tuple(out.shape) != (B, 1, Hq, D):
+        raise ValueError("out must be [B, 1, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq]")
+    _check(lib.jl_bifocal_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                 _dtype_code(q), _dtype_code(out), B, L, Lmax, Hq, Hkv, D, w0,
+                                 w_pretrained, rope_base, sm_scale, _ptr(table),
+                                 table.numel() * table.element_size(), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse

@@ -1,0 +1,221 @@
+// C ABI of libjetlong.so: argument validation (host only, before any HIP
+// call), the schedule of Jet-Long §3.1 Eq. (2), and kernel dispatch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "internal.h"
+#include "jetlong.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+constexpr int64_t kMaxLen = int64_t(1) << 30;   // positions are int32 in the kernels
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t group_size(int64_t L, int64_t w_pretrained) {
+    const int64_t g = (L + w_pretrained - 1) / w_pretrained;   // ceil, L >= 1
+    return g < 1 ? 1 : g;
+}
+
+int check_rope(int64_t head_dim, double rope_base) {
+    if (head_dim != 64 && head_dim != 128)
+        return fail(JL_EUNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)head_dim);
+    if (!std::isfinite(rope_base) || !(rope_base > 1.0))
+        return fail(JL_EINVAL, "rope_base must be finite and > 1 (got %g)", rope_base);
+    return JL_OK;
+}
+
+int check_attention_common(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                           int64_t w_pretrained, double rope_base, float sm_scale, int in_dtype,
+                           int out_dtype) {
+    if (B < 1 || L < 1 || Hq < 1 || Hkv < 1)
+        return fail(JL_EINVAL, "B, L, Hq, Hkv must be >= 1 (got %lld, %lld, %lld, %lld)", (long long)B,
+                    (long long)L, (long long)Hq, (long long)Hkv);
+    if (L > kMaxLen) return fail(JL_EINVAL, "L %lld exceeds 2^30", (long long)L);
+    if (B > 65535) return fail(JL_EINVAL, "B %lld exceeds 65535", (long long)B);
+    if (Hq % Hkv != 0) return fail(JL_EINVAL, "Hq %% Hkv != 0 (%lld, %lld)", (long long)Hq, (long long)Hkv);
+    if (w0 < 0) return fail(JL_EINVAL, "w0 must be >= 0 (got %lld)", (long long)w0);
+    if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1 (got %lld)", (long long)w_pretrained);
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+        return fail(JL_EINVAL, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
+    if ((in_dtype != JL_F32 && in_dtype != JL_BF16) || (out_dtype != JL_F32 && out_dtype != JL_BF16))
+        return fail(JL_EINVAL, "unknown dtype code (in %d, out %d)", in_dtype, out_dtype);
+    if (int rc = check_rope(D, rope_base)) return rc;
+    if (in_dtype == JL_F32 && out_dtype != JL_F32)
+        return fail(JL_EUNSUPPORTED, "f32 input requires f32 output");
+    return JL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+JL_API const char* jl_last_error(void) { return g_err.c_str(); }
+
+JL_API int jl_version(void) { return 1; }
+
+JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
+                       void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
+    g_err.clear();
+    if (!G_out) return fail(JL_EINVAL, "G_out is NULL");
+    if (L < 1 || L > kMaxLen) return fail(JL_EINVAL, "L must be in [1, 2^30] (got %lld)", (long long)L);
+    if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1 (got %lld)", (long long)w_pretrained);
+    if (int rc = check_rope(head_dim, rope_base)) return rc;
+    const size_t need = jl::table_bytes_for(L, (int)head_dim);
+    if (table_bytes_needed) *table_bytes_needed = need;
+    if (table) {
+        if (!aligned16(table)) return fail(JL_EINVAL, "table must be 16-byte aligned");
+        if (table_bytes < need)
+            return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
+    }
+    *G_out = group_size(L, w_pretrained);
+    if (!table) return JL_OK;
+    (void)hipGetLastError();
+    hipError_t e = jl::launch_table_fill(table, L, (int)head_dim, rope_base, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(JL_EHIP, "table fill launch failed: %s", hipGetErrorString(e));
+    return JL_OK;
+}
+
+JL_API int jl_table_fill_host(int64_t L, int64_t head_dim, double rope_base, void* table, size_t table_bytes) {
+    g_err.clear();
+    if (!table) return fail(JL_EINVAL, "table is NULL");
+    if (L < 1 || L > kMaxLen) return fail(JL_EINVAL, "L must be in [1, 2^30] (got %lld)", (long long)L);
+    if (int rc = check_rope(head_dim, rope_base)) return rc;
+    const size_t need = jl::table_bytes_for(L, (int)head_dim);
+    if (table_bytes < need) return fail(JL_ESPACE, "table holds %zu bytes, %zu needed", table_bytes, need);
+    jl::table_fill_host(table, L, (int)head_dim, rope_base);
+    return JL_OK;
+}
+
+JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int in_dtype,
+                              int out_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                              int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
+                              size_t table_bytes, void* hip_stream) {
+    g_err.clear();
+    if (!q || !k || !v || !out || !table) return fail(JL_EINVAL, "q, k, v, out and table must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(table) ||
+        !aligned16(lse))
+        return fail(JL_EINVAL, "device pointers must be 16-byte aligned");
+    if (int rc = check_attention_common(B, L, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, in_dtype,
+                                        out_dtype))
+        return rc;
+    const int64_t R = Hq / Hkv;
+    if (R != 1 && R != 2 && R != 4 && R != 8)
+        return fail(JL_EUNSUPPORTED, "GQA ratio Hq/Hkv = %lld not supported (1, 2, 4, 8)", (long long)R);
+    const size_t need = jl::table_bytes_for(L, (int)D);
+    if (table_bytes < need)
+        return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
+    const int BQ = 256 / (int)R;
+    const int64_t n_qtiles = (L + BQ - 1) / BQ;
+    if (n_qtiles * Hkv * B > 0x7fffffffLL) return fail(JL_EINVAL, "grid too large");
+
+    jl::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.lse = lse;
+    p.table = static_cast<const jl::TableHeader*>(table);
+    p.TL = reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes);
+    p.TH = p.TL + (size_t)jl::kTableLow * (size_t)(D / 2);
+    p.B = B;
+    p.L = L;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.R = (int)R;
+    p.BQ = BQ;
+    p.n_qtiles = (int)n_qtiles;
+    p.w0 = w0 < L ? w0 : L;   // any w0 >= L-1 makes every pair local
+    p.G = group_size(L, w_pretrained);
+    p.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    p.rope_base = rope_base;
+    p.head_dim = (int)D;
+    (void)hipGetLastError();
+    hipError_t e = jl::launch_prefill(p, in_dtype, out_dtype, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(JL_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+    return JL_OK;
+}
+
+JL_API int jl_bifocal_decode_workspace(int64_t B, int64_t Hq, int64_t D, int64_t L, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(JL_EINVAL, "bytes is NULL");
+    if (B < 1 || Hq < 1 || L < 1 || L > kMaxLen) return fail(JL_EINVAL, "B, Hq, L must be >= 1 and L <= 2^30");
+    if (D != 64 && D != 128) return fail(JL_EUNSUPPORTED, "head_dim %lld not supported", (long long)D);
+    const int64_t n_split = (L + jl::kDecodeChunk - 1) / jl::kDecodeChunk;
+    *bytes = (size_t)B * (size_t)Hq * (size_t)n_split * (size_t)(D + 2) * sizeof(float);
+    return JL_OK;
+}
+
+JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                             int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq,
+                             int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained, double rope_base,
+                             float sm_scale, const void* table, size_t table_bytes, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+    g_err.clear();
+    if (!q || !k_cache || !v_cache || !out || !table || !workspace)
+        return fail(JL_EINVAL, "q, k_cache, v_cache, out, table and workspace must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(table) ||
+        !aligned16(workspace) || !aligned16(lse))
+        return fail(JL_EINVAL, "device pointers must be 16-byte aligned");
+    if (int rc = check_attention_common(B, L, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, in_dtype,
+                                        out_dtype))
+        return rc;
+    if (Lmax < L || Lmax > kMaxLen)
+        return fail(JL_EINVAL, "need L <= Lmax <= 2^30 (L=%lld, Lmax=%lld)", (long long)L, (long long)Lmax);
+    if (in_dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "decode reads a bf16 cache only");
+    const int64_t R = Hq / Hkv;
+    if (R != 1 && R != 2 && R != 4 && R != 8 && R != 16)
+        return fail(JL_EUNSUPPORTED, "GQA ratio Hq/Hkv = %lld not supported (1..16, power of 2)", (long long)R);
+    const size_t need = jl::table_bytes_for(L, (int)D);
+    if (table_bytes < need)
+        return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
+    size_t ws_need = 0;
+    jl_bifocal_decode_workspace(B, Hq, D, L, &ws_need);
+    if (workspace_bytes < ws_need)
+        return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace_bytes, ws_need);
+    if (Hkv > 65535) return fail(JL_EINVAL, "Hkv exceeds 65535");
+
+    jl::DecodeParams p;
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.out = out;
+    p.lse = lse;
+    p.ws = static_cast<float*>(workspace);
+    p.table = static_cast<const jl::TableHeader*>(table);
+    p.TL = reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes);
+    p.TH = p.TL + (size_t)jl::kTableLow * (size_t)(D / 2);
+    p.B = B;
+    p.L = L;
+    p.Lmax = Lmax;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.R = (int)R;
+    p.n_split = (int)((L + jl::kDecodeChunk - 1) / jl::kDecodeChunk);
+    p.w0 = w0 < L ? w0 : L;
+    p.G = group_size(L, w_pretrained);
+    p.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    p.rope_base = rope_base;
+    p.head_dim = (int)D;
+    (void)hipGetLastError();
+    hipError_t e = jl::launch_decode(p, out_dtype, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(JL_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+    return JL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Shared device-side definitions for the gfx950 Jet-Long kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kTableMagic = 0x424C544Au;  // "JTLB"
+constexpr int kTableLow = 512;                  // TL rows: offsets 0..511
+constexpr int kTableHeaderBytes = 64;
+
+// Device/host view of the correction-angle table header.
+struct TableHeader {
+    uint32_t magic;
+    int32_t head_dim;
+    int64_t n_cover;     // covers offsets n < n_cover
+    double rope_base;
+    int64_t n_high;      // rows of TH
+    int64_t pad[4];
+};
+static_assert(sizeof(TableHeader) == kTableHeaderBytes, "header size");
+
+__host__ __device__ inline int64_t table_high_rows(int64_t n_cover) {
+    return (n_cover + kTableLow - 1) / kTableLow;
+}
+
+__host__ __device__ inline size_t table_bytes_for(int64_t n_cover, int head_dim) {
+    return (size_t)kTableHeaderBytes +
+           (size_t)(kTableLow + table_high_rows(n_cover)) * (size_t)(head_dim / 2) * 8u;
+}
+
+// cos/sin of n * theta_i, theta_i = base^(-2i/D), from the two-level table:
+// n = 512*h + l, angle addition in fp32 (each factor rounded once from fp64).
+__device__ inline float2 corr_angle(const float2* __restrict__ TL, const float2* __restrict__ TH,
+                                    int half, int n, int i) {
+    const float2 lo = TL[(n & (kTableLow - 1)) * half + i];
+    const float2 hi = TH[(n >> 9) * half + i];
+    return make_float2(hi.x * lo.x - hi.y * lo.y, hi.y * lo.x + hi.x * lo.y);
+}
+
+// Rotate the pair (x, y) by the angle -n*theta (cs = cos, sn = sin of +n*theta).
+// The correction offset f(p) - p is -n with n = p - floor(p/G) >= 0.
+__device__ inline void rotate_back(float& x, float& y, float2 cs) {
+    const float nx = x * cs.x + y * cs.y;
+    const float ny = y * cs.x - x * cs.y;
+    x = nx;
+    y = ny;
+}
+
+__device__ inline float bf16_to_f32(__bf16 v) { return (float)v; }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline float wave_max_xor32(float x) {
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+
+}  // namespace jl

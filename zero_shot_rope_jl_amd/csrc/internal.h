@@ -1,0 +1,60 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace jl {
+
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    const TableHeader* table;
+    const float2* TL;
+    const float2* TH;
+    int64_t B, L, Hq, Hkv;
+    int R;              // Hq / Hkv
+    int BQ;             // query positions per workgroup (256 / R)
+    int n_qtiles;
+    int64_t w0;
+    int64_t G;
+    float sm_scale_log2;  // sm_scale * log2(e)
+    double rope_base;
+    int head_dim;
+};
+
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    float* ws;
+    const TableHeader* table;
+    const float2* TL;
+    const float2* TH;
+    int64_t B, L, Lmax, Hq, Hkv;
+    int R;
+    int n_split;
+    int64_t w0;
+    int64_t G;
+    float sm_scale_log2;
+    double rope_base;
+    int head_dim;
+};
+
+constexpr int kDecodeChunk = 512;   // keys per decode split (per workgroup)
+
+hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double rope_base,
+                             hipStream_t stream);
+void table_fill_host(void* table, int64_t n_cover, int head_dim, double rope_base);
+
+hipError_t launch_prefill(const PrefillParams& p, int in_dtype, int out_dtype, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int out_dtype, hipStream_t stream);
+
+}  // namespace jl
