@@ -1,0 +1,209 @@
+"""Benchmark of the Jet-Long bifocal attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload (seeded synthetic inputs, synth_inputs.py):
+  * prefill: B=1, L=131072, 32 query / 8 KV heads, D=128, bf16, pretrained
+    window 32768 (G=4), w0=4096, RoPE base 1e6 -- the 128K point;
+  * decode: a bf16 cache of 131072 keys, then 256 steps of one new token
+    each (L = 131073 .. 131328, G=5), same head shape.
+
+A prefill step is one jl_bifocal_prefill call over the whole 128K sequence;
+a decode step is one jl_bifocal_decode call (the new token's k/v rows are
+written into the cache before timing, as the caller's projection would).  Inputs are resident in HBM before timing starts.  One
+JSON line is printed: ``value`` is prefill TFLOP/s (algorithmic causal
+FLOPs 4*B*Hq*D*L(L+1)/2 over the measured time); decode microseconds per
+step and its HBM roofline ride in ``decode``; the CPU oracle is timed on a
+bounded row sample in ``cpu_baseline``.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "bifocal prefill TFLOP/s @128K (% MFMA peak); decode µs/step @128K (% HBM BW)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-passes", type=int, default=2, help="timed passes over the 256 decode steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=128, help="query rows in the CPU-oracle sample")
+    ap.add_argument("--skip-decode", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(torch, arr, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def prefill_flops(w) -> float:
+    return 4.0 * w.B * w.Hq * w.D * w.L * (w.L + 1) / 2.0
+
+
+def bench_prefill(torch, jl, si, args, w, x):
+    q, k, v = (to_dev(torch, x[n], w.dtype) for n in "qkv")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device="cuda")
+    table = jl.alloc_table(w.L, w.D, w.rope_base)
+    torch.cuda.synchronize()
+
+    def step():
+        jl.jl_bifocal_prefill(q, k, v, out, lse, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] prefill warmup done, timing {args.steps} steps")
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    assert torch.isfinite(out[:, :: 4096].float()).all(), "non-finite prefill output"
+    flops = prefill_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] prefill {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {wall:.2f}s)")
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return ms, tflops, flops
+
+
+def bench_decode(torch, jl, si, args):
+    dw = si.DECODE_WORKLOAD
+    log(f"[bench] generating {dw.name} cache")
+    kc_np, vc_np = si.make_decode_prompt(dw)
+    kc, vc = to_dev(torch, kc_np, "bf16"), to_dev(torch, vc_np, "bf16")
+    del kc_np, vc_np
+    steps = [si.make_decode_step(dw, s) for s in range(1, dw.steps + 1)]
+    qs = to_dev(torch, np.stack([s[0] for s in steps]), "bf16")     # [S, B, 1, Hq, D]
+    ks = to_dev(torch, np.stack([s[1] for s in steps]), "bf16")
+    vs = to_dev(torch, np.stack([s[2] for s in steps]), "bf16")
+    table = jl.alloc_table(dw.Lmax, dw.D, dw.rope_base)
+    ws = jl.alloc_decode_workspace(dw.B, dw.Hq, dw.D, dw.Lmax)
+    out = torch.empty((dw.B, 1, dw.Hq, dw.D), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    # Each step's new k/v row is written before timing: writing the row is the
+    # caller's job (the projection that produces it), and step s reads only
+    # rows < prompt_len + s, so rows of later steps do not change its result.
+    kc[:, dw.prompt_len:dw.Lmax].copy_(ks[:, :, 0].transpose(0, 1))
+    vc[:, dw.prompt_len:dw.Lmax].copy_(vs[:, :, 0].transpose(0, 1))
+
+    def one_pass():
+        for s in range(dw.steps):
+            L = dw.prompt_len + s + 1
+            jl.jl_bifocal_decode(qs[s], kc, vc, out, None, L, dw.w0, dw.w_pretrained, dw.rope_base,
+                                 dw.sm_scale, table, ws)
+
+    one_pass()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.decode_passes):
+        one_pass()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / (args.decode_passes * dw.steps)
+    mean_L = dw.prompt_len + (dw.steps + 1) / 2.0
+    bytes_step = 2.0 * dw.B * mean_L * dw.Hkv * dw.D * 2
+    gbs = bytes_step / (us * 1e-6) / 1e9
+    log(f"[bench] decode {us:.2f} us/step, {gbs:.0f} GB/s")
+    del kc, vc
+    torch.cuda.empty_cache()
+    return dw, us, gbs, bytes_step
+
+
+def cpu_baseline(si, w, x, n_rows):
+    """The float64 oracle on a bounded sample of the same workload: all 32
+    heads at n_rows seeded uniform query rows (all keys of each row)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    f64 = (lambda a: si.f32_from_bf16_bits(a).astype(np.float64)) if w.dtype == "bf16" else \
+        (lambda a: a.astype(np.float64))
+    rng = np.random.Generator(np.random.PCG64([w.seed, 99]))
+    rows = np.sort(rng.choice(w.L, size=n_rows, replace=False))
+    q64 = np.zeros((w.B, w.L, w.Hq, w.D))
+    q64[:, rows] = f64(x["q"][:, rows])
+    k64, v64 = f64(x["k"]), f64(x["v"])
+    t0 = time.perf_counter()
+    oracle.bifocal_attention(q64, k64, v64, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, rows=rows)
+    sec = time.perf_counter() - t0
+    flops = float(sum(4.0 * w.B * w.Hq * w.D * (r + 1) for r in rows))
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{w.name}: {n_rows} seeded uniform query rows x all {w.Hq} heads over their causal keys "
+                      f"(float64 NumPy oracle incl. the remote view of all {w.L} keys), {sec:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported "
+              "(every kernel here runs on one GPU's share of the work)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth_inputs as si
+    import zero_shot_rope_jl_amd as jl
+    assert torch.cuda.is_available(), "no GPU"
+    log(f"[bench] library {jl.lib_path}")
+
+    w = si.WORKLOADS["ext128k"]
+    log(f"[bench] generating {w.name} inputs")
+    x = si.make_prefill_inputs(w, want_f64=False)
+    ms, tflops, flops = bench_prefill(torch, jl, si, args, w, x)
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bifocal prefill, B1 L131072 Hq32 Hkv8 D128 bf16, w_pretrained 32768 (G=4), "
+                               "w0 4096, RoPE base 1e6; decode: 131072-key cache + 256 steps (G=5)",
+                   "global_batch": w.B, "seq_len": w.L, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops},
+    }
+    if not args.skip_decode:
+        dw, us, gbs, bytes_step = bench_decode(torch, jl, si, args)
+        result["decode"] = {
+            "us_per_step": round(us, 3), "unit": "µs/step", "steps_timed": args.decode_passes * dw.steps,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "bytes_per_step": bytes_step},
+        }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle sample")
+        result["cpu_baseline"] = cpu_baseline(si, w, x, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

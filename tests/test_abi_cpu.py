@@ -103,7 +103,8 @@ def test_decode_validation(over, code):
 
 
 def test_decode_workspace_size():
-    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 131328) == 32 * 257 * 130 * 4
+    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 131328) == 32 * 64 * 130 * 4
+    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 1000) == 32 * 4 * 130 * 4
     assert jl.jl_bifocal_decode_workspace(2, 4, 64, 1) == 2 * 4 * 1 * 66 * 4
     with pytest.raises(jl.JetLongError):
         jl.jl_bifocal_decode_workspace(1, 4, 96, 10)
@@ -138,3 +139,11 @@ def test_binding_has_no_cpu_fallback():
     import zero_shot_rope_jl_amd.binding as b
     src = open(b.__file__).read()
     assert "oracle" not in src and "numpy.einsum" not in src and "softmax" not in src
+
+
+def test_single_hip_runtime_in_process():
+    # the library must bind to the HIP runtime torch already loaded: two
+    # runtimes in one process leave the second without a device
+    with open("/proc/self/maps") as fh:
+        libs = {l.split()[-1] for l in fh if "libamdhip64" in l}
+    assert len(libs) == 1, libs

@@ -183,3 +183,26 @@ def test_decode_equals_prefill_last_row():
     print("decode vs prefill row", d)
     assert d <= 5e-3
     assert max_err(lse.cpu().numpy(), lse_full[:, :, -1].cpu().numpy()) <= 5e-3
+
+
+@pytest.mark.parametrize("L", [8193, 16385, 20000])
+def test_decode_many_splits_matches_oracle(L):
+    require_gpu()
+    B, Lmax, Hq, Hkv, D, w_pre, w0, base = 1, 20000, 32, 8, 128, 4096, 1000, 1e6
+    rng = np.random.default_rng(L)
+    bits = lambda shape: si.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32))
+    qb, kb, vb = bits((B, 1, Hq, D)), bits((B, Lmax, Hkv, D)), bits((B, Lmax, Hkv, D))
+    table = jl.alloc_table(Lmax, D, base)
+    ws = jl.alloc_decode_workspace(B, Hq, D, Lmax)
+    out = torch.empty((B, 1, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    scale = 1 / math.sqrt(D)
+    jl.jl_bifocal_decode(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), out, lse, L, w0, w_pre,
+                         base, scale, table, ws)
+    torch.cuda.synchronize()
+    f64 = lambda a: si.f32_from_bf16_bits(a).astype(np.float64)
+    ref, ref_lse = oracle.decode_attention(f64(qb)[:, 0], f64(kb), f64(vb), L, w0, w_pre, base, scale)
+    e = max_err(out.cpu().numpy()[:, 0], ref)
+    print(L, "decode err", e)
+    assert e <= TOL_BF16
+    assert max_err(lse.cpu().numpy(), ref_lse) <= TOL_BF16

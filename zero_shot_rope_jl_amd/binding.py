@@ -18,6 +18,14 @@ class JetLongError(RuntimeError):
 
 
 def _load():
+    # PyTorch-ROCm ships its own HIP runtime (torch/lib/libamdhip64.so).  If
+    # libjetlong.so were loaded first, the process would map two HIP/HSA
+    # runtimes and the second to initialise would find no device; importing
+    # torch first lets the library bind to torch's already-loaded runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(lib_path):
         raise ImportError(
             f"{lib_path} is missing: build it with `python -m zero_shot_rope_jl_amd.build` "

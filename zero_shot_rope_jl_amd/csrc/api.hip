@@ -156,8 +156,7 @@ JL_API int jl_bifocal_decode_workspace(int64_t B, int64_t Hq, int64_t D, int64_t
     if (!bytes) return fail(JL_EINVAL, "bytes is NULL");
     if (B < 1 || Hq < 1 || L < 1 || L > kMaxLen) return fail(JL_EINVAL, "B, Hq, L must be >= 1 and L <= 2^30");
     if (D != 64 && D != 128) return fail(JL_EUNSUPPORTED, "head_dim %lld not supported", (long long)D);
-    const int64_t n_split = (L + jl::kDecodeChunk - 1) / jl::kDecodeChunk;
-    *bytes = (size_t)B * (size_t)Hq * (size_t)n_split * (size_t)(D + 2) * sizeof(float);
+    *bytes = (size_t)B * (size_t)Hq * (size_t)jl::decode_max_splits(L) * (size_t)(D + 2) * sizeof(float);
     return JL_OK;
 }
 
@@ -206,7 +205,7 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.R = (int)R;
-    p.n_split = (int)((L + jl::kDecodeChunk - 1) / jl::kDecodeChunk);
+    jl::decode_split_plan(L, &p.n_split, &p.wave_chunk);
     p.w0 = w0 < L ? w0 : L;
     p.G = group_size(L, w_pretrained);
     p.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);

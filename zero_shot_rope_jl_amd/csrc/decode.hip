@@ -6,15 +6,25 @@
 // never rewritten.  The query sits at position L-1; keys with
 // (L-1) - k <= w0 use the stored vectors, the rest the corrected views (Eq. 1).
 //
-// Split kernel: workgroup = (split of 512 keys, KV head, batch), 4 waves;
-// each wave owns 32 consecutive keys per iteration.  K is read straight from
-// HBM into MFMA A-operand registers (rows = keys) and rotated there; V goes
-// through wave-private LDS, transposed, to be the A operand of
-// O^T += V^T P^T.  The R query heads of the KV head are the MFMA N columns
-// (16x16x32 bf16), so each K/V byte is read once per step for all R heads.
+// Split kernel: workgroup = (split, KV head, batch), 4 waves; each wave
+// streams its own contiguous key range, 32 keys per iteration, with the next
+// iteration's K and V already in flight.  K goes straight from HBM into MFMA
+// A-operand registers (rows = keys); V goes through wave-private LDS,
+// transposed, to be the A operand of O^T += V^T P^T.  The R query heads of
+// the KV head are the MFMA N columns (16x16x32 bf16), so each K/V byte is read
+// once per step for all R heads.
+//
+// Correction without per-key table traffic: for the 32 keys starting at
+// kbase, n(k) = k - floor(k/G) = nb + dn with nb = n(kbase) and 0 <= dn < 32,
+// and R(-n) = R(-nb) R(-dn).  Because R(a)x . y = x . R(-a)y, the remote score
+//     R(-n_q) q . R(-n_k) k  =  [R(nb) R(-n_q) q] . [R(-dn) k],
+// so the query absorbs the per-iteration base rotation (64 angles, one per
+// lane, from the two-level table) and each key is rotated only by dn, whose
+// cos/sin rows 0..32 sit in LDS.
+//
 // Each workgroup leaves one fp32 partial (acc[D], m, l) per query head; the
-// combine kernel merges the partials of a head with the log-sum-exp rule
-// (§3.3 Eq. 6 with disjoint key sets).
+// combine kernel merges a head's partials with the log-sum-exp rule (§3.3
+// Eq. 6 with disjoint key sets).
 #include <math.h>
 
 #include "internal.h"
@@ -23,23 +33,68 @@ namespace jl {
 
 namespace {
 
-constexpr int kDecThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kDecThreads = kDecodeWaves * 64;
 constexpr int kWaveKeys = 32;
-constexpr int kIterKeys = kWaves * kWaveKeys;
 constexpr int VSTR = kWaveKeys + 8;   // V^T row stride (keys) in LDS
+constexpr int JROWS = kWaveKeys + 1;  // cos/sin(dn * theta) for dn = 0..32
+
+// LDS ordering between lanes of one wave (write -> read, read -> write):
+// wait for this wave's LDS operations and stop the compiler moving memory
+// accesses across this point.
+__device__ inline void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int D>
+struct DecodeTile {
+    static constexpr int NC = D / 32;    // 32-dim K chunks of the QK^T MFMA
+    static constexpr int KPL = D / 16;   // keys per lane in the V transpose
+    bf16x8 k[2][NC];                     // rows of the two 16-key blocks
+    bf16x8 v[KPL];                       // V rows for the transpose
+};
+
+template <int D>
+__device__ inline void load_k(DecodeTile<D>& t, const __bf16* __restrict__ kc, int64_t cache_b, int64_t row,
+                              int kbase, int kend, int colh, int gq) {
+    constexpr int NC = DecodeTile<D>::NC;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        // A-operand row colh of block blk holds key 8*(colh/4) + 4*blk + colh%4:
+        // C rows then give P^T slots in natural key order
+        const int key = kbase + 8 * (colh >> 2) + 4 * blk + (colh & 3);
+        const bool ok = key < kend;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            t.k[blk][c] = ok ? *reinterpret_cast<const bf16x8*>(kc + cache_b + (int64_t)key * row + 32 * c + 8 * gq)
+                             : bf16x8{};
+    }
+}
+
+template <int D>
+__device__ inline void load_v(DecodeTile<D>& t, const __bf16* __restrict__ vc, int64_t cache_b, int64_t row,
+                              int kbase, int kend, int lane) {
+    constexpr int KPL = DecodeTile<D>::KPL;
+    const int dg = lane % (D / 8);
+    const int kg = lane / (D / 8);
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+        const int key = kbase + kg * KPL + e;
+        t.v[e] = key < kend ? *reinterpret_cast<const bf16x8*>(vc + cache_b + (int64_t)key * row + dg * 8)
+                            : bf16x8{};
+    }
+}
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeParams p) {
     constexpr int HALF = D / 2;
-    constexpr int NC = D / 32;        // 32-dim K chunks of the QK^T MFMA
+    constexpr int NC = D / 32;
     constexpr int NDB = D / 16;       // 16-dim blocks of O^T
-    constexpr int KPL = D / 16;       // keys per lane in the V transpose
+    constexpr int KPL = D / 16;
     typedef __bf16 VW __attribute__((ext_vector_type(KPL)));
 
-    __shared__ __attribute__((aligned(16))) __bf16 sVt[kWaves][D * VSTR];
-    __shared__ float s_m[kWaves][16];
-    __shared__ float s_l[kWaves][16];
+    __shared__ __attribute__((aligned(16))) __bf16 sVt[kDecodeWaves][D * VSTR];
+    __shared__ __attribute__((aligned(16))) float2 sJ[JROWS * HALF];
+    __shared__ __attribute__((aligned(16))) float2 sBase[kDecodeWaves][HALF];
+    __shared__ float s_m[kDecodeWaves][16];
+    __shared__ float s_l[kDecodeWaves][16];
     __shared__ int s_bad;
 
     const int tid = threadIdx.x;
@@ -53,7 +108,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     const int b = blockIdx.z;
     const int L = (int)p.L;
     const int Hq = (int)p.Hq;
-    const int Hkv = (int)p.Hkv;
     const int R = p.R;
     const int G = (int)p.G;
     const int qpos = L - 1;
@@ -64,7 +118,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     const __bf16* __restrict__ vc = static_cast<const __bf16*>(p.v);
     const float2* __restrict__ TL = p.TL;
     const float2* __restrict__ TH = p.TH;
-    const int64_t row = (int64_t)Hkv * D;
+    const int64_t row = p.Hkv * D;
     const int64_t cache_b = (int64_t)b * p.Lmax * row + (int64_t)g * D;
 
     if (tid == 0) {
@@ -72,19 +126,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
         s_bad = !(th->magic == kTableMagic && th->head_dim == D && th->rope_base == p.rope_base &&
                   th->n_cover >= p.L);
     }
+    // rows 0..32 of the low table are cos/sin(dn * theta_i)
+    for (int i = tid; i < JROWS * HALF; i += kDecThreads) sJ[i] = TL[i];
     __syncthreads();
+    const bool bad = s_bad;
 
     const bool hvalid = colh < R;
     const int head = g * R + (hvalid ? colh : 0);
 
-    // ---- query fragments (B operand of S^T = K Q^T) -----------------------
-    bf16x8 qf[NC], qr[NC];
+    // ---- query: stored fragments and the corrected view ---------------------
+    // B operand of S^T = K Q^T: fragment c holds dims 32c + 8gq + [0, 8).  The
+    // corrected view R(-n_q) q is kept in bf16 (the MFMA operand precision).
+    bf16x8 qf[NC], qrem[NC];
     {
         const __bf16* qp = static_cast<const __bf16*>(p.q) + ((int64_t)b * Hq + head) * D;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < NC; ++c) {
             qf[c] = hvalid ? *reinterpret_cast<const bf16x8*>(qp + 32 * c + 8 * gq) : bf16x8{};
-        if (G > 1 && !s_bad) {
+            qrem[c] = qf[c];
+        }
+        if (G > 1 && !bad) {
             const int nq = qpos - qpos / G;
 #pragma unroll
             for (int c = 0; c < NC / 2; ++c)
@@ -92,12 +153,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
                 for (int j = 0; j < 8; ++j) {
                     float x = (float)qf[c][j], y = (float)qf[c + NC / 2][j];
                     rotate_back(x, y, corr_angle(TL, TH, HALF, nq, 32 * c + 8 * gq + j));
-                    qr[c][j] = (__bf16)x;
-                    qr[c + NC / 2][j] = (__bf16)y;
+                    qrem[c][j] = (__bf16)x;
+                    qrem[c + NC / 2][j] = (__bf16)y;
                 }
-        } else {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) qr[c] = qf[c];
         }
     }
 
@@ -106,119 +164,131 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int kstart = split * kDecodeChunk;
-    const int kend = min(L, kstart + kDecodeChunk);
+    const int wstart = (split * kDecodeWaves + wave) * p.wave_chunk;
+    const int wend = bad ? wstart : min(L, wstart + p.wave_chunk);
     __bf16* myV = sVt[wave];
+    float2* myBase = sBase[wave];
 
-    for (int it0 = kstart; it0 < kend && !s_bad; it0 += kIterKeys) {
-        const int kbase = it0 + wave * kWaveKeys;
-        const bool active = kbase < kend;
-        // ---- V rows -> V^T (this wave's 32 keys) ---------------------------
+    // One register tile: each half is reloaded for the next step as soon as
+    // this step has consumed it, so loads stay in flight during the compute.
+    DecodeTile<D> cur;
+    if (wstart < wend) {
+        load_k<D>(cur, kc, cache_b, row, wstart, wend, colh, gq);
+        load_v<D>(cur, vc, cache_b, row, wstart, wend, lane);
+    }
+    for (int kbase = wstart; kbase < wend; kbase += kWaveKeys) {
+        const int knext = kbase + kWaveKeys;
+        // ---- V rows -> V^T in this wave's LDS slice --------------------------
         {
             const int dg = lane % (D / 8);
             const int kg = lane / (D / 8);
-            bf16x8 vv[KPL];
-#pragma unroll
-            for (int e = 0; e < KPL; ++e) {
-                const int key = kbase + kg * KPL + e;
-                vv[e] = key < kend ? *reinterpret_cast<const bf16x8*>(vc + cache_b + (int64_t)key * row + dg * 8)
-                                   : bf16x8{};
-            }
+            wave_lds_sync();   // previous iteration's V^T reads are done
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
                 VW w;
 #pragma unroll
-                for (int e = 0; e < KPL; ++e) w[e] = vv[e][d];
+                for (int e = 0; e < KPL; ++e) w[e] = cur.v[e][d];
                 *reinterpret_cast<VW*>(&myV[(dg * 8 + d) * VSTR + kg * KPL]) = w;
             }
         }
-        float s[2][4];
-        if (active) {
-            const bool w_loc = (G == 1) || (kbase + kWaveKeys - 1 >= kloc);
-            const bool w_rem = (G > 1) && (kbase < kloc);
+        // V registers are free: start the next step's V loads
+        if (knext < wend) load_v<D>(cur, vc, cache_b, row, knext, wend, lane);
+
+        const bool w_loc = (G == 1) || (kbase + kWaveKeys - 1 >= kloc);
+        const bool w_rem = (G > 1) && (kbase < kloc);
+        bf16x8 qit[NC];
+        int nb = 0;
+        if (w_rem) {
+            // per-iteration base rotation, one frequency per lane
+            nb = kbase - kbase / G;
+            if (lane < HALF) myBase[lane] = corr_angle(TL, TH, HALF, nb, lane);
+            wave_lds_sync();
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                // A-operand row colh holds key 8*(colh/4) + 4*blk + colh%4, so
-                // that C rows give P^T slots in natural key order
-                const int key = kbase + 8 * (colh >> 2) + 4 * blk + (colh & 3);
-                const bool ok = key < kend;
-                bf16x8 kf[NC];
+            for (int c = 0; c < NC / 2; ++c)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float2 cs = myBase[32 * c + 8 * gq + j];
+                    const float x = (float)qrem[c][j], y = (float)qrem[c + NC / 2][j];
+                    qit[c][j] = (__bf16)(x * cs.x - y * cs.y);
+                    qit[c + NC / 2][j] = (__bf16)(x * cs.y + y * cs.x);
+                }
+        }
+
+        float s[2][4];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x4 sl = f32x4{}, sr = f32x4{};
+            if (w_loc) {
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
-                    kf[c] = ok ? *reinterpret_cast<const bf16x8*>(kc + cache_b + (int64_t)key * row + 32 * c + 8 * gq)
-                               : bf16x8{};
-                f32x4 sl = f32x4{}, sr = f32x4{};
-                if (w_loc) {
-#pragma unroll
-                    for (int c = 0; c < NC; ++c) sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[c], sl, 0, 0, 0);
-                }
-                if (w_rem) {
-                    const int n = ok ? key - key / G : 0;
-#pragma unroll
-                    for (int c = 0; c < NC / 2; ++c)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            float x = (float)kf[c][j], y = (float)kf[c + NC / 2][j];
-                            rotate_back(x, y, corr_angle(TL, TH, HALF, n, 32 * c + 8 * gq + j));
-                            kf[c][j] = (__bf16)x;
-                            kf[c + NC / 2][j] = (__bf16)y;
-                        }
-#pragma unroll
-                    for (int c = 0; c < NC; ++c) sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qr[c], sr, 0, 0, 0);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int kk = kbase + 8 * gq + 4 * blk + i;   // key of C row gq*4+i
-                    float v;
-                    if (w_loc && w_rem) v = kk >= kloc ? sl[i] : sr[i];
-                    else v = w_loc ? sl[i] : sr[i];
-                    s[blk][i] = kk < kend ? v * scale2 : -INFINITY;
-                }
+                    sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[blk][c], qf[c], sl, 0, 0, 0);
             }
-            // online softmax per head column: 8 values here, 4 quads per head
-            float mx = -INFINITY;
+            if (w_rem) {
+                const int key = kbase + 8 * (colh >> 2) + 4 * blk + (colh & 3);
+                const int dn = (key < wend) ? (key - key / G) - nb : 0;
+                bf16x8 kr[NC];
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
+                for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[blk][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);   // finite: key kbase is valid
-            const float alpha = fast_exp2(m_run - m_new);
-            float ls = 0.f;
+                    for (int j = 0; j < 8; ++j) {
+                        float x = (float)cur.k[blk][c][j], y = (float)cur.k[blk][c + NC / 2][j];
+                        rotate_back(x, y, sJ[dn * HALF + 32 * c + 8 * gq + j]);
+                        kr[c][j] = (__bf16)x;
+                        kr[c + NC / 2][j] = (__bf16)y;
+                    }
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pv = fast_exp2(s[blk][i] - m_new);
-                    s[blk][i] = pv;
-                    ls += pv;
-                }
-            l_run = l_run * alpha + ls;
-            m_run = m_new;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-        }
-        __syncthreads();   // V^T visible
-        if (active) {
-            bf16x8 Bp;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                Bp[j] = (__bf16)s[0][j];
-                Bp[j + 4] = (__bf16)s[1][j];
+                for (int c = 0; c < NC; ++c) sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[c], qit[c], sr, 0, 0, 0);
             }
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16x8 A = *reinterpret_cast<const bf16x8*>(&myV[(16 * db + colh) * VSTR + 8 * gq]);
-                acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bp, acc[db], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const int kk = kbase + 8 * gq + 4 * blk + i;   // key of C row gq*4+i
+                float v;
+                if (w_loc && w_rem) v = kk >= kloc ? sl[i] : sr[i];
+                else v = w_loc ? sl[i] : sr[i];
+                s[blk][i] = kk < wend ? v * scale2 : -INFINITY;
             }
         }
-        __syncthreads();   // V^T reads done before the next overwrite
+        // K registers are free: start the next step's K loads
+        if (knext < wend) load_k<D>(cur, kc, cache_b, row, knext, wend, colh, gq);
+
+        // ---- online softmax per head column: 8 values here, 4 quads per head --
+        float mx = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[blk][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);   // finite: key kbase is valid
+        const float alpha = fast_exp2(m_run - m_new);
+        float ls = 0.f;
+        bf16x8 Bp;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = fast_exp2(s[blk][i] - m_new);
+                ls += pv;
+                Bp[4 * blk + i] = (__bf16)pv;
+            }
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+
+        // ---- O^T += V^T P^T ------------------------------------------------------
+        wave_lds_sync();   // V^T written by the other lanes of this wave
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const bf16x8 A = *reinterpret_cast<const bf16x8*>(&myV[(16 * db + colh) * VSTR + 8 * gq]);
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bp, acc[db], 0, 0, 0);
+        }
     }
 
     // ---- merge the 4 waves, write this split's partial --------------------
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
+    __syncthreads();   // every wave is done with its V^T slice
     float* s_acc = reinterpret_cast<float*>(&sVt[0][0]);   // [wave][16 heads][D]
     if (gq == 0) {
         s_m[wave][colh] = m_run;
@@ -229,26 +299,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
 #pragma unroll
         for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + colh) * D + 16 * db + 4 * gq + i] = acc[db][i];
     __syncthreads();
-    float* ws = p.ws;
     for (int idx = tid; idx < R * D; idx += kDecThreads) {
         const int r = idx / D, d = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+        for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][r]);
         float a = 0.f, l = 0.f;
-        if (!s_bad) {
+        if (!bad) {
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float f = fast_exp2(s_m[w][r] - M);
+            for (int w = 0; w < kDecodeWaves; ++w) {
+                const float m = s_m[w][r];
+                const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);   // waves without keys
                 a += f * s_acc[(w * 16 + r) * D + d];
                 l += f * s_l[w][r];
             }
         } else {
-            a = NAN;
-            l = NAN;
-            M = NAN;
+            a = l = M = NAN;
         }
-        float* o = ws + (((int64_t)b * Hq + g * R + r) * p.n_split + split) * (D + 2);
+        float* o = p.ws + (((int64_t)b * Hq + g * R + r) * p.n_split + split) * (D + 2);
         o[d] = a;
         if (d == 0) {
             o[D] = M;
@@ -257,25 +325,52 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecodeParams 
     }
 }
 
+// Log-sum-exp merge of one head's split partials: one workgroup per (head,
+// batch); split weights are computed once into LDS, then each thread sums a
+// dimension over a strided subset of splits.
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
+    constexpr int PARTS = 256 / D;
+    __shared__ float sW[kDecodeMaxSplits];
+    __shared__ float sRed[256];
+    __shared__ float sM, sL;
     const int head = blockIdx.x;
     const int b = blockIdx.y;
-    const int d = threadIdx.x;
+    const int tid = threadIdx.x;
     const int ns = p.n_split;
     const float* base = p.ws + ((int64_t)b * p.Hq + head) * ns * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * (D + 2) + D]);
-    float a = 0.f, l = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float f = fast_exp2(base[s * (D + 2) + D] - M);
-        a += f * base[s * (D + 2) + d];
-        l += f * base[s * (D + 2) + D + 1];
+    if (tid < 64) {
+        // one wave: max and weighted sum of l over <= 64 splits
+        const float m = tid < ns ? base[tid * (D + 2) + D] : -INFINITY;
+        float M = m;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float w = tid < ns ? fast_exp2(m - M) : 0.f;
+        float l = tid < ns ? w * base[tid * (D + 2) + D + 1] : 0.f;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+        if (tid < kDecodeMaxSplits) sW[tid] = w;
+        if (tid == 0) {
+            sM = M;
+            sL = l;
+        }
     }
-    const int64_t o = ((int64_t)b * p.Hq + head) * D + d;
-    if constexpr (OUT_BF16) static_cast<__bf16*>(p.out)[o] = (__bf16)(a / l);
-    else static_cast<float*>(p.out)[o] = a / l;
-    if (d == 0 && p.lse) p.lse[(int64_t)b * p.Hq + head] = (M + log2f(l)) * 0.69314718055994531f;
+    __syncthreads();
+    const int d = tid % D, part = tid / D;
+    float a = 0.f;
+    for (int s = part; s < ns; s += PARTS) a += sW[s] * base[s * (D + 2) + d];
+    sRed[tid] = a;
+    __syncthreads();
+    if (tid < D) {
+        float t = 0.f;
+#pragma unroll
+        for (int q = 0; q < PARTS; ++q) t += sRed[q * D + tid];
+        const float l = sL;
+        const int64_t o = ((int64_t)b * p.Hq + head) * D + tid;
+        if constexpr (OUT_BF16) static_cast<__bf16*>(p.out)[o] = (__bf16)(t / l);
+        else static_cast<float*>(p.out)[o] = t / l;
+        if (tid == 0 && p.lse) p.lse[(int64_t)b * p.Hq + head] = (sM + log2f(l)) * 0.69314718055994531f;
+    }
 }
 
 template <int D, bool OUT_BF16>
@@ -284,7 +379,7 @@ hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(p.Hq, p.B), dim3(D), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(p.Hq, p.B), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
