@@ -79,9 +79,9 @@ JL_API int jl_version(void);
  *
  * Table layout (opaque to callers; documented for completeness): a 64-byte
  * header {magic, head_dim, n_cover, rope_base}, then fp32 (cos, sin) pairs
- * TL[l][i] = (cos, sin)(l * theta_i) for l < 512 and
- * TH[h][i] = (cos, sin)(512 * h * theta_i) for h <= (L-1)/512, i < D/2, all
- * angles formed in float64 and rounded once to fp32.
+ * TF[n][i] = (cos, sin)(n * theta_i) for n < L, i < D/2, each angle formed in
+ * float64 and rounded once to fp32 (L * D * 4 bytes: 64 MiB for L = 128K,
+ * D = 128).
  *
  * With table == NULL no HIP call is made.  Errors: L < 1, w_pretrained < 1,
  * head_dim not in {64, 128} (JL_EUNSUPPORTED), rope_base <= 1 or not finite,

@@ -117,9 +117,10 @@ def test_device_table_equals_host_table():
         dev = t.cpu().numpy()
         host = jl.jl_table_fill_host(L, D, base)
         assert np.array_equal(dev[:32], host[:32])
-        a = dev[64:].view(np.float32)
+        a = dev[64:].view(np.float32).astype(np.float64)
         b = host[64:].view(np.float32)
-        assert np.all(np.abs(a - b) <= np.spacing(np.abs(b)))
+        # device (OCML) and host (libm) float64 cos/sin may round differently
+        assert np.all(np.abs(a - b) <= np.spacing(np.abs(b)).astype(np.float64) + 1e-10)
 
 
 def test_mismatched_table_poisons_output():

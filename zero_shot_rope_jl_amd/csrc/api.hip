@@ -131,8 +131,7 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
     p.out = out;
     p.lse = lse;
     p.table = static_cast<const jl::TableHeader*>(table);
-    p.TL = reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes);
-    p.TH = p.TL + (size_t)jl::kTableLow * (size_t)(D / 2);
+    p.TF = reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes);
     p.B = B;
     p.L = L;
     p.Hq = Hq;
@@ -197,8 +196,7 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
     p.lse = lse;
     p.ws = static_cast<float*>(workspace);
     p.table = static_cast<const jl::TableHeader*>(table);
-    p.TL = reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes);
-    p.TH = p.TL + (size_t)jl::kTableLow * (size_t)(D / 2);
+    p.TF = reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes);
     p.B = B;
     p.L = L;
     p.Lmax = Lmax;

@@ -13,37 +13,23 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr uint32_t kTableMagic = 0x424C544Au;  // "JTLB"
-constexpr int kTableLow = 512;                  // TL rows: offsets 0..511
+constexpr uint32_t kTableMagic = 0x324C544Au;  // "JTL2"
 constexpr int kTableHeaderBytes = 64;
 
-// Device/host view of the correction-angle table header.
+// Device/host view of the correction-angle table header.  The header is
+// followed by rows TF[n][i] = (cos, sin)(n * theta_i), n < n_cover, i < D/2,
+// each angle formed in float64 and rounded once to fp32.
 struct TableHeader {
     uint32_t magic;
     int32_t head_dim;
     int64_t n_cover;     // covers offsets n < n_cover
     double rope_base;
-    int64_t n_high;      // rows of TH
-    int64_t pad[4];
+    int64_t pad[5];
 };
 static_assert(sizeof(TableHeader) == kTableHeaderBytes, "header size");
 
-__host__ __device__ inline int64_t table_high_rows(int64_t n_cover) {
-    return (n_cover + kTableLow - 1) / kTableLow;
-}
-
 __host__ __device__ inline size_t table_bytes_for(int64_t n_cover, int head_dim) {
-    return (size_t)kTableHeaderBytes +
-           (size_t)(kTableLow + table_high_rows(n_cover)) * (size_t)(head_dim / 2) * 8u;
-}
-
-// cos/sin of n * theta_i, theta_i = base^(-2i/D), from the two-level table:
-// n = 512*h + l, angle addition in fp32 (each factor rounded once from fp64).
-__device__ inline float2 corr_angle(const float2* __restrict__ TL, const float2* __restrict__ TH,
-                                    int half, int n, int i) {
-    const float2 lo = TL[(n & (kTableLow - 1)) * half + i];
-    const float2 hi = TH[(n >> 9) * half + i];
-    return make_float2(hi.x * lo.x - hi.y * lo.y, hi.y * lo.x + hi.x * lo.y);
+    return (size_t)kTableHeaderBytes + (size_t)n_cover * (size_t)(head_dim / 2) * 8u;
 }
 
 // Rotate the pair (x, y) by the angle -n*theta (cs = cos, sn = sin of +n*theta).

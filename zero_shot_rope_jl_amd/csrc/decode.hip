@@ -19,8 +19,8 @@
 // and R(-n) = R(-nb) R(-dn).  Because R(a)x . y = x . R(-a)y, the remote score
 //     R(-n_q) q . R(-n_k) k  =  [R(nb) R(-n_q) q] . [R(-dn) k],
 // so the query absorbs the per-iteration base rotation (64 angles, one per
-// lane, from the two-level table) and each key is rotated only by dn, whose
-// cos/sin rows 0..32 sit in LDS.
+// lane, one table row) and each key is rotated only by dn, whose cos/sin rows
+// 0..32 sit in LDS.
 //
 // Each workgroup leaves one fp32 partial (acc[D], m, l) per query head; the
 // combine kernel merges a head's partials with the log-sum-exp rule (§3.3
@@ -116,8 +116,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const float scale2 = p.sm_scale_log2;
     const __bf16* __restrict__ kc = static_cast<const __bf16*>(p.k);
     const __bf16* __restrict__ vc = static_cast<const __bf16*>(p.v);
-    const float2* __restrict__ TL = p.TL;
-    const float2* __restrict__ TH = p.TH;
+    const float2* __restrict__ TF = p.TF;
     const int64_t row = p.Hkv * D;
     const int64_t cache_b = (int64_t)b * p.Lmax * row + (int64_t)g * D;
 
@@ -126,8 +125,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         s_bad = !(th->magic == kTableMagic && th->head_dim == D && th->rope_base == p.rope_base &&
                   th->n_cover >= p.L);
     }
-    // rows 0..32 of the low table are cos/sin(dn * theta_i)
-    for (int i = tid; i < JROWS * HALF; i += kDecThreads) sJ[i] = TL[i];
+    // rows 0..32 of the table are cos/sin(dn * theta_i); only rows < L are
+    // guaranteed to exist and dn <= L-1, so copy no further
+    for (int i = tid; i < min(JROWS, L) * HALF; i += kDecThreads) sJ[i] = TF[i];
     __syncthreads();
     const bool bad = s_bad;
 
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     float x = (float)qf[c][j], y = (float)qf[c + NC / 2][j];
-                    rotate_back(x, y, corr_angle(TL, TH, HALF, nq, 32 * c + 8 * gq + j));
+                    rotate_back(x, y, TF[(int64_t)nq * HALF + 32 * c + 8 * gq + j]);
                     qrem[c][j] = (__bf16)x;
                     qrem[c + NC / 2][j] = (__bf16)y;
                 }
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         if (w_rem) {
             // per-iteration base rotation, one frequency per lane
             nb = kbase - kbase / G;
-            if (lane < HALF) myBase[lane] = corr_angle(TL, TH, HALF, nb, lane);
+            if (lane < HALF) myBase[lane] = TF[(int64_t)nb * HALF + lane];
             wave_lds_sync();
 #pragma unroll
             for (int c = 0; c < NC / 2; ++c)

@@ -15,8 +15,7 @@ struct PrefillParams {
     void* out;
     float* lse;
     const TableHeader* table;
-    const float2* TL;
-    const float2* TH;
+    const float2* TF;   // (cos, sin)(n theta_i) rows, n < coverage
     int64_t B, L, Hq, Hkv;
     int R;              // Hq / Hkv
     int BQ;             // query positions per workgroup (256 / R)
@@ -36,8 +35,7 @@ struct DecodeParams {
     float* lse;
     float* ws;
     const TableHeader* table;
-    const float2* TL;
-    const float2* TH;
+    const float2* TF;   // (cos, sin)(n theta_i) rows, n < coverage
     int64_t B, L, Lmax, Hq, Hkv;
     int R;
     int n_split;        // workgroups per (batch, KV head)

@@ -10,16 +10,23 @@
 // Work decomposition
 //   workgroup = 8 waves = 256 query rows = R query heads x (256/R) positions
 //               of one KV head; wave = 32 positions of one query head.
-//   key tiles of 64 are staged in LDS: K as stored (local view) and/or K
-//   rotated by its correction (remote view) -- the rotation runs once per
-//   workgroup per tile on the global->LDS path -- and V transposed.
+//   The workgroup walks its key tiles (64 keys) in two phases: a remote
+//   phase over every tile that holds a remote pair, with K rotated by its
+//   correction on the global->LDS path and Q held in its corrected view, then
+//   a local phase over every tile that holds a local pair, with stored K and
+//   Q.  A tile that straddles the window edge is visited once per phase under
+//   a mask, so only one Q view is ever live in registers and every other
+//   tile runs without per-element masking.
+//   Pipeline: LDS is double-buffered; the next tile's K, V and correction
+//   rows are loaded into registers before the current tile's MFMAs and
+//   written (rotated, V transposed) to the other buffer after them, so one
+//   barrier per tile suffices.
 //   Each wave computes S^T = K Q^T with MFMA (keys on the M axis, queries on
 //   N), so a query's 64 scores sit in one lane pair: the row max needs one
 //   cross-half exchange and the row sum none until the end.  P^T is already
-//   in the B-operand layout of O^T += V^T P^T.
-//   Tile classes per wave: local-only, remote-only or straddling (both
-//   products, per-element select on q - k <= w0); tiles above the diagonal
-//   are skipped.
+//   in the B-operand layout of O^T += V^T P^T.  The running max is only
+//   raised (and the accumulator rescaled) when a tile's max exceeds it by
+//   more than 2^8, which keeps every probability below 256.
 #include <math.h>
 
 #include <type_traits>
@@ -31,7 +38,8 @@ namespace jl {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int BN = 64;   // keys per tile
+constexpr int BN = 64;                  // keys per tile
+constexpr float kRescaleSlack = 8.0f;   // log2 units
 
 template <bool BF16> struct Elem;
 template <> struct Elem<true> { using T = __bf16; };
@@ -47,6 +55,20 @@ struct PrefillLayout {
     static constexpr int V_ELEMS = BF16 ? D * VSTR : BN * VSTR;
     static constexpr int PPT = HALF * BN / kThreads;        // rotation pairs per thread
     static constexpr int NQ = BF16 ? D / 16 : D / 8;        // Q fragments per lane
+    static constexpr int KPT = BN * D / (kThreads * 4);     // bf16 V transpose: keys per thread
+    static constexpr int FPT = D / 8;                       // f32 V copy: floats per thread
+};
+
+// Registers holding one tile on its way from HBM to LDS.
+template <int D, bool BF16>
+struct Stage {
+    using Lay = PrefillLayout<D, BF16>;
+    using T = typename Elem<BF16>::T;
+    typedef T KV __attribute__((ext_vector_type(Lay::PPT)));
+    typedef float FV __attribute__((ext_vector_type(Lay::FPT)));
+    KV x, y;                      // pair halves: dims f0.. and HALF + f0..
+    float4 cs[Lay::PPT / 2];      // correction (cos, sin) of the pairs (remote view)
+    typename std::conditional<BF16, bf16x4[Lay::KPT], FV>::type v;
 };
 
 template <int D, bool BF16, bool OUT_BF16>
@@ -59,10 +81,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     constexpr int PPT = Lay::PPT;
     constexpr int NQ = Lay::NQ;
     constexpr int NDB = D / 32;   // 32-dim blocks of O^T
+    constexpr int W = BF16 ? 8 : 4;   // dims per Q fragment and lane half
+    using St = Stage<D, BF16>;
+    using QF = typename std::conditional<BF16, bf16x8, f32x4>::type;
 
-    __shared__ __attribute__((aligned(16))) T sKloc[Lay::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) T sKrem[Lay::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) T sV[Lay::V_ELEMS];
+    __shared__ __attribute__((aligned(16))) T sK[2][Lay::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) T sV[2][Lay::V_ELEMS];
     __shared__ int s_bad;
 
     const int tid = threadIdx.x;
@@ -101,9 +125,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const T* __restrict__ qg = static_cast<const T*>(p.q);
     const T* __restrict__ kg = static_cast<const T*>(p.k);
     const T* __restrict__ vg = static_cast<const T*>(p.v);
-    const float2* __restrict__ TL = p.TL;
-    const float2* __restrict__ TH = p.TH;
+    const float2* __restrict__ TF = p.TF;
     const int64_t kv_row = (int64_t)Hkv * D;
+    const int64_t kv_b = (int64_t)b * L * kv_row + (int64_t)g * D;
 
     if (tid == 0) {
         const TableHeader* th = p.table;
@@ -124,39 +148,120 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         return;
     }
 
-    // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------
+    // ---- pass schedule (uniform over the workgroup) -------------------------
+    // tile kt covers keys [64kt, 64kt + 63]; the last one is padded with zero
+    // rows beyond L, which every mask below excludes.
+    const int nkt = q_hi / BN + 1;
+    int nR = 0;    // remote phase: tiles [0, nR) hold a pair with q - k > w0
+    int nL0 = 0;   // local phase: tiles [nL0, nkt) hold a pair with 0 <= q - k <= w0
+    if (G > 1) {
+        nR = q_hi - w0 > 0 ? min(nkt, (q_hi - w0 + BN - 1) / BN) : 0;
+        nL0 = q0 - w0 - (BN - 1) > 0 ? (q0 - w0) / BN : 0;
+    }
+    const int NP = nR + (nkt - nL0);
+
+    // ---- query fragments (B operand of S^T = K Q^T) -------------------------
     // bf16: fragment c holds dims 16c + 8hh + [0, 8); f32: fragment t holds
     // dims 8t + 4hh + [0, 4).  Partner dims (+D/2) sit in fragment c + NQ/2.
-    using QF = typename std::conditional<BF16, bf16x8, f32x4>::type;
-    QF qf[NQ], qr[NQ];
-    {
+    QF qv[NQ];
+    auto load_q = [&](bool remote_view) {
         const bool ok = wave_active && my_q < L;
         const int64_t qo = (((int64_t)b * L + (ok ? my_q : 0)) * Hq + head) * D;
-        constexpr int W = BF16 ? 8 : 4;
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-            const int d0 = c * 2 * W + W * hh;
-            if (ok) qf[c] = *reinterpret_cast<const QF*>(qg + qo + d0);
-            else qf[c] = QF{};
-        }
-        if (G > 1) {
-            const int nq = ok ? my_q - my_q / G : 0;
+        for (int c = 0; c < NQ; ++c)
+            qv[c] = ok ? *reinterpret_cast<const QF*>(qg + qo + c * 2 * W + W * hh) : QF{};
+        if (remote_view) {
+            const int64_t nq = ok ? my_q - my_q / G : 0;
 #pragma unroll
-            for (int c = 0; c < NQ / 2; ++c) {
+            for (int c = 0; c < NQ / 2; ++c)
 #pragma unroll
                 for (int j = 0; j < W; ++j) {
-                    float x = (float)qf[c][j];
-                    float y = (float)qf[c + NQ / 2][j];
-                    rotate_back(x, y, corr_angle(TL, TH, HALF, nq, c * 2 * W + W * hh + j));
-                    qr[c][j] = (T)x;
-                    qr[c + NQ / 2][j] = (T)y;
+                    float x = (float)qv[c][j];
+                    float y = (float)qv[c + NQ / 2][j];
+                    rotate_back(x, y, TF[nq * HALF + c * 2 * W + W * hh + j]);
+                    qv[c][j] = (T)x;
+                    qv[c + NQ / 2][j] = (T)y;
                 }
+        }
+    };
+
+    // ---- staging of one tile: HBM -> registers -> LDS -----------------------
+    St st;
+    const int kr = tid >> 3;             // K: key row of this thread
+    const int f0 = (tid & 7) * PPT;      // K: first frequency of this thread
+    auto stage_load = [&](int pi) {
+        const bool rem = pi < nR;
+        const int k0 = (rem ? pi : nL0 + (pi - nR)) * BN;
+        const int kpos = k0 + kr;
+        const bool ok = kpos < L;
+        const int64_t ko = kv_b + (int64_t)(ok ? kpos : 0) * kv_row;
+        if (ok) {
+            st.x = *reinterpret_cast<const typename St::KV*>(kg + ko + f0);
+            st.y = *reinterpret_cast<const typename St::KV*>(kg + ko + HALF + f0);
+        } else {
+            st.x = typename St::KV{};
+            st.y = typename St::KV{};
+        }
+        if (rem) {
+            const int64_t n = ok ? kpos - kpos / G : 0;
+            const float4* t4 = reinterpret_cast<const float4*>(TF + n * HALF + f0);
+#pragma unroll
+            for (int j = 0; j < PPT / 2; ++j) st.cs[j] = t4[j];
+        }
+        if constexpr (BF16) {
+            constexpr int KPT = Lay::KPT;
+            const int dg = tid % (D / 4);
+            const int kgp = tid / (D / 4);
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const int kpos2 = k0 + kgp * KPT + e;
+                st.v[e] = kpos2 < L ? *reinterpret_cast<const bf16x4*>(vg + kv_b + (int64_t)kpos2 * kv_row + dg * 4)
+                                    : bf16x4{};
             }
         } else {
-#pragma unroll
-            for (int c = 0; c < NQ; ++c) qr[c] = qf[c];
+            const int kpos2 = k0 + kr;
+            st.v = kpos2 < L ? *reinterpret_cast<const typename St::FV*>(vg + kv_b + (int64_t)kpos2 * kv_row +
+                                                                          (tid & 7) * Lay::FPT)
+                             : typename St::FV{};
         }
-    }
+    };
+    auto stage_store = [&](int pi, int buf) {
+        const bool rem = pi < nR;
+        T* K = sK[buf];
+        if (rem) {
+            typename St::KV xr, yr;
+            const float2* cs = reinterpret_cast<const float2*>(st.cs);
+#pragma unroll
+            for (int j = 0; j < PPT; ++j) {
+                float x = (float)st.x[j], y = (float)st.y[j];
+                rotate_back(x, y, cs[j]);
+                xr[j] = (T)x;
+                yr[j] = (T)y;
+            }
+            *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + f0]) = xr;
+            *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + HALF + f0]) = yr;
+        } else {
+            *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + f0]) = st.x;
+            *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + HALF + f0]) = st.y;
+        }
+        T* V = sV[buf];
+        if constexpr (BF16) {
+            // transposed: V[d][key], natural key order
+            constexpr int KPT = Lay::KPT;
+            typedef __bf16 VW __attribute__((ext_vector_type(KPT)));
+            const int dg = tid % (D / 4);
+            const int kgp = tid / (D / 4);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                VW w;
+#pragma unroll
+                for (int e = 0; e < KPT; ++e) w[e] = st.v[e][d];
+                *reinterpret_cast<VW*>(&V[(dg * 4 + d) * VSTR + kgp * KPT]) = w;
+            }
+        } else {
+            *reinterpret_cast<typename St::FV*>(&V[kr * VSTR + (tid & 7) * Lay::FPT]) = st.v;
+        }
+    };
 
     f32x16 acc[NDB];
 #pragma unroll
@@ -164,145 +269,70 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    const int nkt = q_hi / BN + 1;
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int k0 = kt * BN;
-        const int k1 = min(k0 + BN, L) - 1;
-        const bool wg_loc = (G == 1) || (q0 - k1 <= w0);
-        const bool wg_rem = (G > 1) && (q_hi - k0 > w0);
-
-        __syncthreads();   // previous tile's LDS reads are done
-        // ---- K: stored view and/or corrected view --------------------------
-        {
-            typedef T KV __attribute__((ext_vector_type(PPT)));
-            const int kr = tid >> 3;             // key row in tile
-            const int f0 = (tid & 7) * PPT;      // first frequency index
-            const int kpos = k0 + kr;
-            const bool ok = kpos < L;
-            const int64_t ko = ((int64_t)b * L + (ok ? kpos : 0)) * kv_row + (int64_t)g * D;
-            KV xv = KV{}, yv = KV{};
-            if (ok) {
-                xv = *reinterpret_cast<const KV*>(kg + ko + f0);
-                yv = *reinterpret_cast<const KV*>(kg + ko + HALF + f0);
-            }
-            if (wg_loc) {
-                *reinterpret_cast<KV*>(&sKloc[kr * KSTR + f0]) = xv;
-                *reinterpret_cast<KV*>(&sKloc[kr * KSTR + HALF + f0]) = yv;
-            }
-            if (wg_rem) {
-                const int n = ok ? kpos - kpos / G : 0;
-                KV xr, yr;
-#pragma unroll
-                for (int j = 0; j < PPT; ++j) {
-                    float x = (float)xv[j], y = (float)yv[j];
-                    rotate_back(x, y, corr_angle(TL, TH, HALF, n, f0 + j));
-                    xr[j] = (T)x;
-                    yr[j] = (T)y;
-                }
-                *reinterpret_cast<KV*>(&sKrem[kr * KSTR + f0]) = xr;
-                *reinterpret_cast<KV*>(&sKrem[kr * KSTR + HALF + f0]) = yr;
-            }
-        }
-        // ---- V ---------------------------------------------------------------
-        if constexpr (BF16) {
-            // transposed: sV[d][key], natural key order; each thread moves a
-            // KPT-key x 4-dim block (8-byte row reads, KPT*2-byte column writes)
-            constexpr int KPT = BN * D / (kThreads * 4);
-            typedef __bf16 VW __attribute__((ext_vector_type(KPT)));
-            const int dg = tid % (D / 4);
-            const int kgp = tid / (D / 4);
-            bf16x4 vv[KPT];
-#pragma unroll
-            for (int e = 0; e < KPT; ++e) {
-                const int kpos = k0 + kgp * KPT + e;
-                const int64_t vo = ((int64_t)b * L + kpos) * kv_row + (int64_t)g * D + dg * 4;
-                vv[e] = kpos < L ? *reinterpret_cast<const bf16x4*>(vg + vo) : bf16x4{};
-            }
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                VW w;
-#pragma unroll
-                for (int e = 0; e < KPT; ++e) w[e] = vv[e][d];
-                *reinterpret_cast<VW*>(&sV[(dg * 4 + d) * VSTR + kgp * KPT]) = w;
-            }
+    // ---- one pass: S^T, softmax update, O^T ----------------------------------
+    auto compute = [&](int pi, int buf) {
+        if (!wave_active) return;
+        const bool rem = pi < nR;
+        const int k0 = (rem ? pi : nL0 + (pi - nR)) * BN;
+        const int k1 = k0 + BN - 1;
+        bool act, masked;
+        int nkb;
+        if (rem) {
+            act = p_hi - k0 > w0;
+            masked = p0 - k1 <= w0;                        // some local pair here
+            nkb = act ? min(2, (p_hi - w0 - 1 - k0) / 32 + 1) : 0;
         } else {
-            constexpr int FPT = D / 8;   // floats per thread, 8 threads per key row
-            typedef float VW __attribute__((ext_vector_type(FPT)));
-            const int kr = tid >> 3;
-            const int c0 = (tid & 7) * FPT;
-            const int kpos = k0 + kr;
-            const int64_t vo = ((int64_t)b * L + kpos) * kv_row + (int64_t)g * D + c0;
-            *reinterpret_cast<VW*>(&sV[kr * VSTR + c0]) =
-                kpos < L ? *reinterpret_cast<const VW*>(vg + vo) : VW{};
+            act = k0 <= p_hi && (G == 1 || p0 - k1 <= w0);
+            masked = k1 > p0 || (G > 1 && p_hi - k0 > w0);  // causal edge or remote pairs
+            nkb = act ? min(2, (p_hi - k0) / 32 + 1) : 0;
         }
-        __syncthreads();
+        if (!act) return;
+        const T* K = sK[buf];
+        const T* V = sV[buf];
 
-        if (!wave_active || k0 > p_hi) continue;
-        const bool w_loc = (G == 1) || (p0 - k1 <= w0);
-        const bool w_rem = (G > 1) && (p_hi - k0 > w0);
-        const int nkb = min(2, (p_hi - k0) / 32 + 1);   // 32-key blocks with a causal key
-
-        // ---- S^T = K Q^T ---------------------------------------------------------
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (kb >= nkb) break;
-            f32x16 sl = f32x16{}, sr = f32x16{};
+            f32x16 a = f32x16{};
             if constexpr (BF16) {
                 // A-operand row `col` holds key 32kb + sigma(col); sigma makes the
                 // C rows land so that P^T feeds the PV MFMA in natural key order.
-                const int a = col >> 3, hp = (col >> 2) & 1, e = col & 3;
-                const int krow = 32 * kb + 16 * (a >> 1) + 8 * hp + 4 * (a & 1) + e;
-                if (w_loc) {
+                const int a3 = col >> 3, hp = (col >> 2) & 1, e = col & 3;
+                const int krow = 32 * kb + 16 * (a3 >> 1) + 8 * hp + 4 * (a3 & 1) + e;
 #pragma unroll
-                    for (int c = 0; c < NQ; ++c) {
-                        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sKloc[krow * KSTR + 16 * c + 8 * hh]);
-                        sl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[c], sl, 0, 0, 0);
-                    }
-                }
-                if (w_rem) {
-#pragma unroll
-                    for (int c = 0; c < NQ; ++c) {
-                        const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sKrem[krow * KSTR + 16 * c + 8 * hh]);
-                        sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qr[c], sr, 0, 0, 0);
-                    }
+                for (int c = 0; c < NQ; ++c) {
+                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(&K[krow * KSTR + 16 * c + 8 * hh]);
+                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[c], a, 0, 0, 0);
                 }
             } else {
                 const int krow = 32 * kb + col;
-                if (w_loc) {
 #pragma unroll
-                    for (int t = 0; t < NQ; ++t) {
-                        const f32x4 A = *reinterpret_cast<const f32x4*>(&sKloc[krow * KSTR + 8 * t + 4 * hh]);
+                for (int t = 0; t < NQ; ++t) {
+                    const f32x4 A = *reinterpret_cast<const f32x4*>(&K[krow * KSTR + 8 * t + 4 * hh]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            sl = __builtin_amdgcn_mfma_f32_32x32x2f32(A[e], qf[t][e], sl, 0, 0, 0);
-                    }
-                }
-                if (w_rem) {
-#pragma unroll
-                    for (int t = 0; t < NQ; ++t) {
-                        const f32x4 A = *reinterpret_cast<const f32x4*>(&sKrem[krow * KSTR + 8 * t + 4 * hh]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            sr = __builtin_amdgcn_mfma_f32_32x32x2f32(A[e], qr[t][e], sr, 0, 0, 0);
-                    }
+                    for (int e = 0; e < 4; ++e) a = __builtin_amdgcn_mfma_f32_32x32x2f32(A[e], qv[t][e], a, 0, 0, 0);
                 }
             }
-            // select the view per element, apply the causal mask, scale to log2
+            s[kb] = a;
+        }
+        if (masked) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                int koff;
-                if constexpr (BF16) koff = 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
-                else koff = 32 * kb + (i >> 2) * 8 + hh * 4 + (i & 3);
-                const int key = k0 + koff;
-                float vsc;
-                if (w_loc && w_rem) vsc = (my_q - key <= w0) ? sl[i] : sr[i];
-                else vsc = w_loc ? sl[i] : sr[i];
-                s[kb][i] = (key > my_q) ? -INFINITY : vsc * scale2;
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb >= nkb) break;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    int koff;
+                    if constexpr (BF16) koff = 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
+                    else koff = 32 * kb + (i >> 2) * 8 + hh * 4 + (i & 3);
+                    const int dq = my_q - (k0 + koff);
+                    const bool keep = rem ? dq > w0 : (dq >= 0 && (G == 1 || dq <= w0));
+                    if (!keep) s[kb][i] = -INFINITY;
+                }
             }
         }
 
-        // ---- online softmax (base 2) ---------------------------------------------
+        // ---- online softmax (base 2, lazily rescaled) ----------------------------
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -310,24 +340,27 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
         }
-        mx = wave_max_xor32(mx);
-        const float m_new = fmaxf(m_run, mx);     // finite: key 0 is in the first tile
-        const float alpha = fast_exp2(m_run - m_new);
-        float ls = 0.f;
+        mx = wave_max_xor32(mx) * scale2;
+        const bool raise = mx > m_run + kRescaleSlack;
+        if (__any(raise)) {
+            const float m_new = raise ? mx : m_run;
+            const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;   // 0 when m_run = -inf
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;   // rows with no key yet
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (kb >= nkb) break;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float pv = fast_exp2(s[kb][i] - m_new);
+                const float pv = fast_exp2(fmaf(s[kb][i], scale2, -m_use));
                 s[kb][i] = pv;
-                ls += pv;
+                l_run += pv;
             }
         }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
 
         // ---- O^T += V^T P^T ----------------------------------------------------
         if constexpr (BF16) {
@@ -339,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
                 for (int j = 0; j < 8; ++j) Bp[j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(&sV[(db * 32 + col) * VSTR + 16 * kc + 8 * hh]);
+                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(&V[(db * 32 + col) * VSTR + 16 * kc + 8 * hh]);
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bp, acc[db], 0, 0, 0);
                 }
             }
@@ -352,11 +385,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
                     const int key = 32 * kb + (i >> 2) * 8 + hh * 4 + (i & 3);
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(sV[key * VSTR + db * 32 + col],
-                                                                       s[kb][i], acc[db], 0, 0, 0);
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(V[key * VSTR + db * 32 + col], s[kb][i],
+                                                                       acc[db], 0, 0, 0);
                 }
             }
         }
+    };
+
+    // ---- software pipeline over the passes --------------------------------------
+    load_q(nR > 0);
+    stage_load(0);
+    stage_store(0, 0);
+    __syncthreads();
+    for (int pi = 0; pi < NP; ++pi) {
+        const int buf = pi & 1;
+        if (pi + 1 < NP) stage_load(pi + 1);
+        if (pi == nR && nR > 0) load_q(false);   // switch to the local view
+        compute(pi, buf);
+        if (pi + 1 < NP) stage_store(pi + 1, buf ^ 1);
+        __syncthreads();
     }
 
     // ---- epilogue ---------------------------------------------------------------

@@ -1,8 +1,8 @@
 // Correction-angle table for the on-the-fly RoPE correction (Jet-Long §3.2,
-// Eq. 5): (cos, sin)(n * theta_i) for offsets n = p - floor(p/G), split as
-// n = 512*h + l so that two small fp32 tables cover every offset below the
-// coverage.  Angles are formed in float64 and rounded once to fp32; the table
-// does not depend on G.
+// Eq. 5): (cos, sin)(n * theta_i) for every offset n = p - floor(p/G) below
+// the coverage.  Angles are formed in float64 and rounded once to fp32; the
+// table does not depend on G, so one table serves every G and every L up to
+// its coverage.
 #include <math.h>
 #include <string.h>
 
@@ -23,22 +23,14 @@ __host__ __device__ inline TableHeader make_header(int64_t n_cover, int D, doubl
     h.head_dim = D;
     h.n_cover = n_cover;
     h.rope_base = base;
-    h.n_high = table_high_rows(n_cover);
     return h;
 }
 
-__global__ void table_fill_kernel(char* table, int64_t n_cover, int D, double base,
-                                  int64_t n_high) {
+__global__ void table_fill_kernel(char* table, int64_t n_cover, int D, double base) {
     const int half = D / 2;
-    const int64_t rows = kTableLow + n_high;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     float2* ent = reinterpret_cast<float2*>(table + kTableHeaderBytes);
-    if (idx < rows * half) {
-        const int64_t row = idx / half;
-        const int i = (int)(idx % half);
-        const int64_t n = row < kTableLow ? row : (row - kTableLow) * kTableLow;
-        ent[idx] = table_entry(base, D, n, i);
-    }
+    if (idx < n_cover * half) ent[idx] = table_entry(base, D, idx / half, (int)(idx % half));
     if (idx == 0) {
         *reinterpret_cast<TableHeader*>(table) = make_header(n_cover, D, base);
     }
@@ -46,25 +38,21 @@ __global__ void table_fill_kernel(char* table, int64_t n_cover, int D, double ba
 
 hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double rope_base,
                              hipStream_t stream) {
-    const int64_t n_high = table_high_rows(n_cover);
-    const int64_t total = (kTableLow + n_high) * (head_dim / 2);
+    const int64_t total = n_cover * (head_dim / 2);
     const int threads = 256;
     const int blocks = (int)((total + threads - 1) / threads);
     hipLaunchKernelGGL(table_fill_kernel, dim3(blocks), dim3(threads), 0, stream,
-                       static_cast<char*>(table), n_cover, head_dim, rope_base, n_high);
+                       static_cast<char*>(table), n_cover, head_dim, rope_base);
     return hipGetLastError();
 }
 
 void table_fill_host(void* table, int64_t n_cover, int head_dim, double rope_base) {
     const int half = head_dim / 2;
-    const int64_t n_high = table_high_rows(n_cover);
     TableHeader h = make_header(n_cover, head_dim, rope_base);
     memcpy(table, &h, sizeof(h));
     float2* ent = reinterpret_cast<float2*>(static_cast<char*>(table) + kTableHeaderBytes);
-    for (int64_t row = 0; row < kTableLow + n_high; ++row) {
-        const int64_t n = row < kTableLow ? row : (row - kTableLow) * kTableLow;
-        for (int i = 0; i < half; ++i) ent[row * half + i] = table_entry(rope_base, head_dim, n, i);
-    }
+    for (int64_t n = 0; n < n_cover; ++n)
+        for (int i = 0; i < half; ++i) ent[n * half + i] = table_entry(rope_base, head_dim, n, i);
 }
 
 }  // namespace jl
