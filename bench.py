@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=128, help="query rows in the CPU-oracle sample")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 512 MiB device-to-device copy (reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -175,6 +177,14 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     log(f"[bench] library {jl.lib_path}")
 
+    if args.copy_calibration:
+        n = 512 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes done")
+        del src, dst
     w = si.WORKLOADS["ext128k"]
     log(f"[bench] generating {w.name} inputs")
     x = si.make_prefill_inputs(w, want_f64=False)

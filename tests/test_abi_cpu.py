@@ -96,6 +96,7 @@ def _decode(**over):
                                                                     jl.JL_EUNSUPPORTED),
     (dict(Hq=64, Hkv=2), jl.JL_EUNSUPPORTED), (dict(wsb=16), jl.JL_ESPACE), (dict(tb=64), jl.JL_ESPACE),
     (dict(w0=-3), jl.JL_EINVAL), (dict(D=32), jl.JL_EUNSUPPORTED), (dict(k=FAKE + 8), jl.JL_EINVAL),
+    (dict(Hq=6, Hkv=3), jl.JL_EUNSUPPORTED),
 ])
 def test_decode_validation(over, code):
     assert _decode(**over) == code
@@ -103,8 +104,8 @@ def test_decode_validation(over, code):
 
 
 def test_decode_workspace_size():
-    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 131328) == 32 * 64 * 130 * 4
-    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 1000) == 32 * 4 * 130 * 4
+    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 131328) == 32 * 256 * 130 * 4
+    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 1000) == 32 * 32 * 130 * 4
     assert jl.jl_bifocal_decode_workspace(2, 4, 64, 1) == 2 * 4 * 1 * 66 * 4
     with pytest.raises(jl.JetLongError):
         jl.jl_bifocal_decode_workspace(1, 4, 96, 10)

@@ -187,6 +187,8 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
     if (workspace_bytes < ws_need)
         return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace_bytes, ws_need);
     if (Hkv > 65535) return fail(JL_EINVAL, "Hkv exceeds 65535");
+    if (Hkv % 8 != 0 && 8 % Hkv != 0)
+        return fail(JL_EUNSUPPORTED, "decode needs Hkv dividing 8 or a multiple of 8 (got %lld)", (long long)Hkv);
 
     jl::DecodeParams p;
     p.q = q;
@@ -203,7 +205,8 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.R = (int)R;
-    jl::decode_split_plan(L, &p.n_split, &p.wave_chunk);
+    jl::decode_split_plan(B, Hkv, L, &p.n_split, &p.wave_chunk);
+    p.heads_per_wg = jl::decode_heads_per_wg(Hkv);
     p.w0 = w0 < L ? w0 : L;
     p.G = group_size(L, w_pretrained);
     p.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);

@@ -6,9 +6,12 @@
 // never rewritten.  The query sits at position L-1; keys with
 // (L-1) - k <= w0 use the stored vectors, the rest the corrected views (Eq. 1).
 //
-// Split kernel: workgroup = (split, KV head, batch), 4 waves; each wave
-// streams its own contiguous key range, 32 keys per iteration, with the next
-// iteration's K and V already in flight.  K goes straight from HBM into MFMA
+// Split kernel: workgroup = (key range, KV-head group, batch), 8 waves; wave w
+// handles KV head w % WH over sub-range w / WH of the workgroup's keys, so the
+// waves of a workgroup read whole key rows (all heads are contiguous in the
+// cache) and the grid holds about one workgroup per compute unit.  A wave
+// streams its keys 32 per iteration with the next iteration's K and V in
+// flight.  K goes straight from HBM into MFMA
 // A-operand registers (rows = keys); V goes through wave-private LDS,
 // transposed, to be the A operand of O^T += V^T P^T.  The R query heads of
 // the KV head are the MFMA N columns (16x16x32 bf16), so each K/V byte is read
@@ -91,7 +94,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     typedef __bf16 VW __attribute__((ext_vector_type(KPL)));
 
     __shared__ __attribute__((aligned(16))) __bf16 sVt[kDecodeWaves][D * VSTR];
-    __shared__ __attribute__((aligned(16))) float2 sJ[JROWS * HALF];
+    constexpr int JSTR = HALF + 2;    // padded row: rows start on different LDS banks
+    __shared__ __attribute__((aligned(16))) float2 sJ[JROWS * JSTR];
     __shared__ __attribute__((aligned(16))) float2 sBase[kDecodeWaves][HALF];
     __shared__ float s_m[kDecodeWaves][16];
     __shared__ float s_l[kDecodeWaves][16];
@@ -104,7 +108,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const int gq = lane >> 4;     // lane quad
 
     const int split = blockIdx.x;
-    const int g = blockIdx.y;
+    const int WH = p.heads_per_wg;
+    const int NW = kDecodeWaves / WH;   // waves per head
+    const int hw = wave % WH;
+    const int sub = wave / WH;
+    const int g = blockIdx.y * WH + hw;
     const int b = blockIdx.z;
     const int L = (int)p.L;
     const int Hq = (int)p.Hq;
@@ -127,7 +135,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     }
     // rows 0..32 of the table are cos/sin(dn * theta_i); only rows < L are
     // guaranteed to exist and dn <= L-1, so copy no further
-    for (int i = tid; i < min(JROWS, L) * HALF; i += kDecThreads) sJ[i] = TF[i];
+    for (int i = tid; i < min(JROWS, L) * HALF; i += kDecThreads) sJ[(i / HALF) * JSTR + i % HALF] = TF[i];
     __syncthreads();
     const bool bad = s_bad;
 
@@ -164,10 +172,16 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int wstart = (split * kDecodeWaves + wave) * p.wave_chunk;
+    const int wstart = (split * NW + sub) * p.wave_chunk;
     const int wend = bad ? wstart : min(L, wstart + p.wave_chunk);
     __bf16* myV = sVt[wave];
     float2* myBase = sBase[wave];
+
+    // cos/sin(nb * theta_lane) of the current step's base offset nb = n(kbase):
+    // read once, then advanced by the step's offset increment (<= 32) from the
+    // LDS rows, so no step waits on a table load.
+    float2 base = make_float2(1.f, 0.f);
+    if (lane < HALF && wstart < wend && G > 1) base = TF[(int64_t)(wstart - wstart / G) * HALF + lane];
 
     // One register tile: each half is reloaded for the next step as soon as
     // this step has consumed it, so loads stay in flight during the compute.
@@ -201,7 +215,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         if (w_rem) {
             // per-iteration base rotation, one frequency per lane
             nb = kbase - kbase / G;
-            if (lane < HALF) myBase[lane] = TF[(int64_t)nb * HALF + lane];
+            if (lane < HALF) myBase[lane] = base;
             wave_lds_sync();
 #pragma unroll
             for (int c = 0; c < NC / 2; ++c)
@@ -232,7 +246,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         float x = (float)cur.k[blk][c][j], y = (float)cur.k[blk][c + NC / 2][j];
-                        rotate_back(x, y, sJ[dn * HALF + 32 * c + 8 * gq + j]);
+                        rotate_back(x, y, sJ[dn * JSTR + 32 * c + 8 * gq + j]);
                         kr[c][j] = (__bf16)x;
                         kr[c + NC / 2][j] = (__bf16)y;
                     }
@@ -283,9 +297,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
             const bf16x8 A = *reinterpret_cast<const bf16x8*>(&myV[(16 * db + colh) * VSTR + 8 * gq]);
             acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bp, acc[db], 0, 0, 0);
         }
+        if (w_rem && knext < wend && lane < HALF) {
+            const int step = (knext - knext / G) - nb;   // 0 <= step <= 32, step < L
+            const float2 j2 = sJ[step * JSTR + lane];
+            base = make_float2(base.x * j2.x - base.y * j2.y, base.y * j2.x + base.x * j2.y);
+        }
     }
 
-    // ---- merge the 4 waves, write this split's partial --------------------
+    // ---- merge the NW waves of each head, write this split's partials -------
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
     __syncthreads();   // every wave is done with its V^T slice
@@ -299,15 +318,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
 #pragma unroll
         for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + colh) * D + 16 * db + 4 * gq + i] = acc[db][i];
     __syncthreads();
-    for (int idx = tid; idx < R * D; idx += kDecThreads) {
-        const int r = idx / D, d = idx % D;
+    for (int idx = tid; idx < WH * R * D; idx += kDecThreads) {
+        const int hx = idx / (R * D), r = (idx / D) % R, d = idx % D;
         float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, s_m[w][r]);
+        for (int u = 0; u < NW; ++u) M = fmaxf(M, s_m[u * WH + hx][r]);
         float a = 0.f, l = 0.f;
         if (!bad) {
-#pragma unroll
-            for (int w = 0; w < kDecodeWaves; ++w) {
+            for (int u = 0; u < NW; ++u) {
+                const int w = u * WH + hx;
                 const float m = s_m[w][r];
                 const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);   // waves without keys
                 a += f * s_acc[(w * 16 + r) * D + d];
@@ -316,7 +334,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         } else {
             a = l = M = NAN;
         }
-        float* o = p.ws + (((int64_t)b * Hq + g * R + r) * p.n_split + split) * (D + 2);
+        const int hq = (blockIdx.y * WH + hx) * R + r;
+        float* o = p.ws + (((int64_t)b * Hq + hq) * p.n_split + split) * (D + 2);
         o[d] = a;
         if (d == 0) {
             o[D] = M;
@@ -325,61 +344,77 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     }
 }
 
-// Log-sum-exp merge of one head's split partials: one workgroup per (head,
-// batch); split weights are computed once into LDS, then each thread sums a
-// dimension over a strided subset of splits.
+// Log-sum-exp merge of one head's split partials (up to 256 splits):
+// workgroup = (head, batch, 32-dim block) of 1024 threads.  Split weights go
+// to LDS once; each thread then sums one dimension over every 32nd split,
+// all of its (at most 8) loads issued together.
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
-    constexpr int PARTS = 256 / D;
+__global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeParams p) {
     __shared__ float sW[kDecodeMaxSplits];
-    __shared__ float sRed[256];
+    __shared__ float sRed[1024];
     __shared__ float sM, sL;
     const int head = blockIdx.x;
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int ns = p.n_split;
     const float* base = p.ws + ((int64_t)b * p.Hq + head) * ns * (D + 2);
-    if (tid < 64) {
-        // one wave: max and weighted sum of l over <= 64 splits
-        const float m = tid < ns ? base[tid * (D + 2) + D] : -INFINITY;
-        float M = m;
+    const float m = tid < ns ? base[tid * (D + 2) + D] : -INFINITY;
+    const float lsplit = tid < ns ? base[tid * (D + 2) + D + 1] : 0.f;
+    float M = m;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        const float w = tid < ns ? fast_exp2(m - M) : 0.f;
-        float l = tid < ns ? w * base[tid * (D + 2) + D + 1] : 0.f;
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (lane == 0) sRed[wave] = M;
+    __syncthreads();
+    M = sRed[0];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-        if (tid < kDecodeMaxSplits) sW[tid] = w;
-        if (tid == 0) {
-            sM = M;
-            sL = l;
-        }
-    }
+    for (int w = 1; w < 16; ++w) M = fmaxf(M, sRed[w]);
+    const float wgt = tid < ns ? fast_exp2(m - M) : 0.f;
+    if (tid < kDecodeMaxSplits) sW[tid] = wgt;
+    float l = wgt * lsplit;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
     __syncthreads();
-    const int d = tid % D, part = tid / D;
-    float a = 0.f;
-    for (int s = part; s < ns; s += PARTS) a += sW[s] * base[s * (D + 2) + d];
-    sRed[tid] = a;
+    if (lane == 0) sRed[wave] = l;
     __syncthreads();
-    if (tid < D) {
+    if (tid == 0) {
         float t = 0.f;
 #pragma unroll
-        for (int q = 0; q < PARTS; ++q) t += sRed[q * D + tid];
-        const float l = sL;
-        const int64_t o = ((int64_t)b * p.Hq + head) * D + tid;
-        if constexpr (OUT_BF16) static_cast<__bf16*>(p.out)[o] = (__bf16)(t / l);
-        else static_cast<float*>(p.out)[o] = t / l;
-        if (tid == 0 && p.lse) p.lse[(int64_t)b * p.Hq + head] = (sM + log2f(l)) * 0.69314718055994531f;
+        for (int w = 0; w < 16; ++w) t += sRed[w];
+        sM = M;
+        sL = t;
+    }
+    const int d = blockIdx.z * 32 + (tid & 31);
+    const int part = tid >> 5;   // 32 interleaved split groups
+    float a = 0.f;
+#pragma unroll
+    for (int u = 0; u < kDecodeMaxSplits / 32; ++u) {
+        const int s = part + 32 * u;
+        if (s < ns) a += sW[s] * base[s * (D + 2) + d];
+    }
+    __syncthreads();
+    sRed[tid] = a;
+    __syncthreads();
+    if (tid < 32) {
+        float t = 0.f;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) t += sRed[q * 32 + tid];
+        const float lt = sL;
+        const int64_t o = ((int64_t)b * p.Hq + head) * D + d;
+        if constexpr (OUT_BF16) static_cast<__bf16*>(p.out)[o] = (__bf16)(t / lt);
+        else static_cast<float*>(p.out)[o] = t / lt;
+        if (blockIdx.z == 0 && tid == 0 && p.lse) p.lse[(int64_t)b * p.Hq + head] = (sM + log2f(lt)) * 0.69314718055994531f;
     }
 }
 
 template <int D, bool OUT_BF16>
 hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16>), dim3(p.n_split, p.Hkv, p.B), dim3(kDecThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16>), dim3(p.n_split, p.Hkv / p.heads_per_wg, p.B),
+                       dim3(kDecThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(p.Hq, p.B), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(p.Hq, p.B, D / 32), dim3(1024), 0, stream, p);
     return hipGetLastError();
 }
 

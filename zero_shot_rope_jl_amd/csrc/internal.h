@@ -38,8 +38,9 @@ struct DecodeParams {
     const float2* TF;   // (cos, sin)(n theta_i) rows, n < coverage
     int64_t B, L, Lmax, Hq, Hkv;
     int R;
-    int n_split;        // workgroups per (batch, KV head)
+    int n_split;        // workgroups per (batch, KV-head group)
     int wave_chunk;     // consecutive keys per wave (multiple of 32)
+    int heads_per_wg;   // KV heads per workgroup (waves per head = 8 / heads_per_wg)
     int64_t w0;
     int64_t G;
     float sm_scale_log2;
@@ -47,21 +48,29 @@ struct DecodeParams {
     int head_dim;
 };
 
-// Decode split plan: at most kDecodeMaxSplits workgroups of 4 waves per
-// (batch, KV head); each wave streams one contiguous range of keys.
-constexpr int kDecodeMaxSplits = 64;
-constexpr int kDecodeWaves = 4;
+// Decode split plan.  A workgroup has 8 waves that cover up to 8 KV heads
+// (wave w -> head w % WH, key sub-range w / WH) over one key range, so each
+// key row (all heads contiguous) is streamed whole; the grid holds about one
+// workgroup per compute unit.
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeTargetWGs = 256;
+constexpr int kDecodeMaxSplits = 256;
 
 inline int64_t decode_max_splits(int64_t L) {
-    const int64_t n = (L + 255) / 256;
+    const int64_t n = (L + 31) / 32;
     return n < kDecodeMaxSplits ? n : kDecodeMaxSplits;
 }
 
-inline void decode_split_plan(int64_t L, int* n_split, int* wave_chunk) {
-    const int64_t nmax = decode_max_splits(L);
-    int64_t per_wave = (L + nmax * kDecodeWaves - 1) / (nmax * kDecodeWaves);
+inline int decode_heads_per_wg(int64_t Hkv) { return Hkv >= kDecodeWaves ? kDecodeWaves : (int)Hkv; }
+
+inline void decode_split_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* wave_chunk) {
+    const int64_t WH = decode_heads_per_wg(Hkv);
+    const int64_t NW = kDecodeWaves / WH;
+    const int64_t groups = B * (Hkv / WH);
+    const int64_t n_target = groups >= kDecodeTargetWGs ? 1 : kDecodeTargetWGs / groups;
+    int64_t per_wave = (L + n_target * NW - 1) / (n_target * NW);
     per_wave = (per_wave + 31) / 32 * 32;
-    const int64_t chunk = per_wave * kDecodeWaves;
+    const int64_t chunk = per_wave * NW;
     *n_split = (int)((L + chunk - 1) / chunk);
     *wave_chunk = (int)per_wave;
 }

@@ -19,14 +19,16 @@
 //   tile runs without per-element masking.
 //   Pipeline: LDS is double-buffered; the next tile's K, V and correction
 //   rows are loaded into registers before the current tile's MFMAs and
-//   written (rotated, V transposed) to the other buffer after them, so one
-//   barrier per tile suffices.
+//   written (K rotated where needed) to the other buffer after them, so one
+//   barrier per tile suffices.  V stays row-major in LDS; the PV MFMA reads
+//   its V^T operand with the transposing LDS load (ds_read_b64_tr_b16).
 //   Each wave computes S^T = K Q^T with MFMA (keys on the M axis, queries on
 //   N), so a query's 64 scores sit in one lane pair: the row max needs one
 //   cross-half exchange and the row sum none until the end.  P^T is already
 //   in the B-operand layout of O^T += V^T P^T.  The running max is only
 //   raised (and the accumulator rescaled) when a tile's max exceeds it by
 //   more than 2^8, which keeps every probability below 256.
+#include <limits.h>
 #include <math.h>
 
 #include <type_traits>
@@ -41,6 +43,15 @@ constexpr int kThreads = 512;
 constexpr int BN = 64;                  // keys per tile
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 8-byte rows supplied by lanes i/4, i/4+4, i/4+8 and i/4+12.
+__device__ inline bf16x4 lds_read_tr16(const __bf16* p) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
 template <bool BF16> struct Elem;
 template <> struct Elem<true> { using T = __bf16; };
 template <> struct Elem<false> { using T = float; };
@@ -49,14 +60,14 @@ template <int D, bool BF16>
 struct PrefillLayout {
     static constexpr int HALF = D / 2;
     static constexpr int KSTR = BF16 ? D + 8 : D + 4;      // K row stride (elements)
-    // bf16: V^T[d][key] rows of BN keys; f32: V[key][d] rows of D values
-    static constexpr int VSTR = BF16 ? BN + 8 : D + 4;
+    // V rows [key][d]; bf16 rows are padded by 64 bytes so that the transposed
+    // reads of 8 key rows spread over all LDS banks
+    static constexpr int VSTR = BF16 ? D + 32 : D + 4;
     static constexpr int K_ELEMS = BN * KSTR;
-    static constexpr int V_ELEMS = BF16 ? D * VSTR : BN * VSTR;
+    static constexpr int V_ELEMS = BN * VSTR;
     static constexpr int PPT = HALF * BN / kThreads;        // rotation pairs per thread
     static constexpr int NQ = BF16 ? D / 16 : D / 8;        // Q fragments per lane
-    static constexpr int KPT = BN * D / (kThreads * 4);     // bf16 V transpose: keys per thread
-    static constexpr int FPT = D / 8;                       // f32 V copy: floats per thread
+    static constexpr int VPT = D / 8;                       // V elements per thread (8 threads per row)
 };
 
 // Registers holding one tile on its way from HBM to LDS.
@@ -65,10 +76,10 @@ struct Stage {
     using Lay = PrefillLayout<D, BF16>;
     using T = typename Elem<BF16>::T;
     typedef T KV __attribute__((ext_vector_type(Lay::PPT)));
-    typedef float FV __attribute__((ext_vector_type(Lay::FPT)));
+    typedef T VV __attribute__((ext_vector_type(Lay::VPT)));
     KV x, y;                      // pair halves: dims f0.. and HALF + f0..
     float4 cs[Lay::PPT / 2];      // correction (cos, sin) of the pairs (remote view)
-    typename std::conditional<BF16, bf16x4[Lay::KPT], FV>::type v;
+    VV v;                         // one row segment of V
 };
 
 template <int D, bool BF16, bool OUT_BF16>
@@ -208,21 +219,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int j = 0; j < PPT / 2; ++j) st.cs[j] = t4[j];
         }
-        if constexpr (BF16) {
-            constexpr int KPT = Lay::KPT;
-            const int dg = tid % (D / 4);
-            const int kgp = tid / (D / 4);
-#pragma unroll
-            for (int e = 0; e < KPT; ++e) {
-                const int kpos2 = k0 + kgp * KPT + e;
-                st.v[e] = kpos2 < L ? *reinterpret_cast<const bf16x4*>(vg + kv_b + (int64_t)kpos2 * kv_row + dg * 4)
-                                    : bf16x4{};
-            }
-        } else {
+        {
             const int kpos2 = k0 + kr;
-            st.v = kpos2 < L ? *reinterpret_cast<const typename St::FV*>(vg + kv_b + (int64_t)kpos2 * kv_row +
-                                                                          (tid & 7) * Lay::FPT)
-                             : typename St::FV{};
+            st.v = kpos2 < L ? *reinterpret_cast<const typename St::VV*>(vg + kv_b + (int64_t)kpos2 * kv_row +
+                                                                          (tid & 7) * Lay::VPT)
+                             : typename St::VV{};
         }
     };
     auto stage_store = [&](int pi, int buf) {
@@ -244,23 +245,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + f0]) = st.x;
             *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + HALF + f0]) = st.y;
         }
-        T* V = sV[buf];
-        if constexpr (BF16) {
-            // transposed: V[d][key], natural key order
-            constexpr int KPT = Lay::KPT;
-            typedef __bf16 VW __attribute__((ext_vector_type(KPT)));
-            const int dg = tid % (D / 4);
-            const int kgp = tid / (D / 4);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                VW w;
-#pragma unroll
-                for (int e = 0; e < KPT; ++e) w[e] = st.v[e][d];
-                *reinterpret_cast<VW*>(&V[(dg * 4 + d) * VSTR + kgp * KPT]) = w;
-            }
-        } else {
-            *reinterpret_cast<typename St::FV*>(&V[kr * VSTR + (tid & 7) * Lay::FPT]) = st.v;
-        }
+        *reinterpret_cast<typename St::VV*>(&sV[buf][kr * VSTR + (tid & 7) * Lay::VPT]) = st.v;
     };
 
     f32x16 acc[NDB];
@@ -317,17 +302,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             s[kb] = a;
         }
         if (masked) {
+            // keep keys in [klo, khi]; the remote view keeps q - k > w0, the
+            // local view 0 <= q - k <= w0 (no lower bound when G == 1)
+            const int klo = (rem || G == 1) ? INT_MIN / 2 : my_q - w0;
+            const int khi = rem ? my_q - w0 - 1 : my_q;
+            const int lane_off = BF16 ? 8 * hh : 4 * hh;
+            const int rlo = klo - k0 - lane_off;
+            const int rhi = khi - k0 - lane_off;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb >= nkb) break;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    int koff;
-                    if constexpr (BF16) koff = 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
-                    else koff = 32 * kb + (i >> 2) * 8 + hh * 4 + (i & 3);
-                    const int dq = my_q - (k0 + koff);
-                    const bool keep = rem ? dq > w0 : (dq >= 0 && (G == 1 || dq <= w0));
-                    if (!keep) s[kb][i] = -INFINITY;
+                    const int c = BF16 ? 32 * kb + 16 * (i >> 3) + (i & 7) : 32 * kb + (i >> 2) * 8 + (i & 3);
+                    s[kb][i] = ((c >= rlo) & (c <= rhi)) ? s[kb][i] : -INFINITY;
                 }
             }
         }
@@ -355,33 +343,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         for (int kb = 0; kb < 2; ++kb) {
             if (kb >= nkb) break;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv = fast_exp2(fmaf(s[kb][i], scale2, -m_use));
-                s[kb][i] = pv;
-                l_run += pv;
-            }
+            for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], scale2, -m_use));
         }
 
         // ---- O^T += V^T P^T ----------------------------------------------------
         if constexpr (BF16) {
+            // A operand (V^T rows = dims, k = keys) from row-major V with the
+            // transposing LDS read: within each 16-lane group, lane c supplies
+            // 4 dims of one key row and lane i receives dim i of 4 key rows.
+            const int Gq = lane >> 4, cq = lane & 15;
+            const int tr_key = 8 * (Gq >> 1) + (cq >> 2);
+            const int tr_dim = 16 * (Gq & 1) + 4 * (cq & 3);
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
                 if (kc >= 2 * nkb) break;
                 bf16x8 Bp;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) Bp[j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
+                // row sums of the probabilities as rounded for the MFMA
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    lsum[kc] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{Bp[2 * j], Bp[2 * j + 1]}, ones, lsum[kc], false);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(&V[(db * 32 + col) * VSTR + 16 * kc + 8 * hh]);
+                    const __bf16* vp = &V[(16 * kc + tr_key) * VSTR + 32 * db + tr_dim];
+                    const bf16x4 lo = lds_read_tr16(vp);
+                    const bf16x4 hi = lds_read_tr16(vp + 4 * VSTR);
+                    const bf16x8 A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bp, acc[db], 0, 0, 0);
                 }
             }
+            l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
         } else {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb >= nkb) break;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
+                    l_run += s[kb][i];
                     const int key = 32 * kb + (i >> 2) * 8 + hh * 4 + (i & 3);
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
