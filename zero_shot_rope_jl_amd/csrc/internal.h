@@ -80,6 +80,7 @@ hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double 
 void table_fill_host(void* table, int64_t n_cover, int head_dim, double rope_base);
 
 hipError_t launch_prefill(const PrefillParams& p, int in_dtype, int out_dtype, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillParams& p, int out_dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int out_dtype, hipStream_t stream);
 
 }  // namespace jl

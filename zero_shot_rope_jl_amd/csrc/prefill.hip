@@ -1,4 +1,5 @@
-// Causal GQA bifocal-attention prefill for gfx950.
+// Causal GQA bifocal-attention prefill for gfx950, generic kernel (serves
+// fp32 inputs; bf16 inputs go to the 64-rows-per-wave kernel).
 //
 // Method (Jet-Long, §3 Eq. 1; §3.1 Eqs. 2-3; §3.2 Eq. 5; §3.3 Eq. 6): a
 // query/key pair with q - k <= w0 scores with the stored RoPE vectors; a pair
@@ -82,6 +83,168 @@ struct Stage {
     VV v;                         // one row segment of V
 };
 
+// Query fragments (B operand of S^T = K Q^T).  bf16: fragment c holds dims
+// 16c + 8hh + [0, 8); f32: fragment t holds dims 8t + 4hh + [0, 4).  Partner
+// dims (+D/2) sit in fragment c + NQ/2.  The remote view rotates each pair by
+// the query's correction offset.
+template <int D, bool BF16, typename QF, typename T>
+__device__ __forceinline__ void load_q_frags(QF* qv, const T* __restrict__ qrow, bool ok, bool remote_view,
+                                             const float2* __restrict__ TF, int64_t nq, int hh) {
+    using Lay = PrefillLayout<D, BF16>;
+    constexpr int NQ = Lay::NQ;
+    constexpr int W = BF16 ? 8 : 4;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) qv[c] = ok ? *reinterpret_cast<const QF*>(qrow + c * 2 * W + W * hh) : QF{};
+    if (remote_view) {
+#pragma unroll
+        for (int c = 0; c < NQ / 2; ++c)
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                float x = (float)qv[c][j];
+                float y = (float)qv[c + NQ / 2][j];
+                rotate_back(x, y, TF[nq * Lay::HALF + c * 2 * W + W * hh + j]);
+                qv[c][j] = (T)x;
+                qv[c + NQ / 2][j] = (T)y;
+            }
+    }
+}
+
+// One 64-key tile for one wave: S^T = K Q^T for the two 32-key blocks, the
+// optional window/causal mask (keys outside [rlo, rhi] relative to the lane's
+// first key), the online-softmax update and O^T += V^T P^T.
+template <int D, bool BF16, typename QF, typename T>
+__device__ __forceinline__ void tile_step(const T* __restrict__ K, const T* __restrict__ V, const QF* qv,
+                                          f32x16* acc, float& m_run, float& l_run, int col, int hh, int lane,
+                                          bool masked, int rlo, int rhi, float scale2) {
+    using Lay = PrefillLayout<D, BF16>;
+    constexpr int NQ = Lay::NQ;
+    constexpr int KSTR = Lay::KSTR;
+    constexpr int VSTR = Lay::VSTR;
+    constexpr int NDB = D / 32;
+
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    if constexpr (BF16) {
+        // A-operand row `col` holds key sigma(col) of each 32-key block; sigma
+        // makes the C rows land so that P^T feeds the PV MFMA in natural order.
+        const int a3 = col >> 3, hp = (col >> 2) & 1, e = col & 3;
+        const int krow = 16 * (a3 >> 1) + 8 * hp + 4 * (a3 & 1) + e;
+        const T* k0p = K + krow * KSTR + 8 * hh;
+        const T* k1p = k0p + 32 * KSTR;
+        // two-deep register pipeline for the K fragments: the reads for
+        // chunk c+1 are in flight while chunk c's MFMAs issue
+        bf16x8 A0 = *reinterpret_cast<const bf16x8*>(k0p);
+        bf16x8 A1 = *reinterpret_cast<const bf16x8*>(k1p);
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            bf16x8 B0, B1;
+            if (c + 1 < NQ) {
+                B0 = *reinterpret_cast<const bf16x8*>(k0p + 16 * (c + 1));
+                B1 = *reinterpret_cast<const bf16x8*>(k1p + 16 * (c + 1));
+            }
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, qv[c], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, qv[c], s1, 0, 0, 0);
+            if (c + 1 < NQ) {
+                A0 = B0;
+                A1 = B1;
+            }
+        }
+    } else {
+        const T* k0p = K + col * KSTR + 4 * hh;
+        const T* k1p = k0p + 32 * KSTR;
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+            const f32x4 A0 = *reinterpret_cast<const f32x4*>(k0p + 8 * t);
+            const f32x4 A1 = *reinterpret_cast<const f32x4*>(k1p + 8 * t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(A0[e], qv[t][e], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(A1[e], qv[t][e], s1, 0, 0, 0);
+            }
+        }
+    }
+    if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int c0 = BF16 ? 16 * (i >> 3) + (i & 7) : (i >> 2) * 8 + (i & 3);
+            s0[i] = ((c0 >= rlo) & (c0 <= rhi)) ? s0[i] : -INFINITY;
+            s1[i] = ((c0 + 32 >= rlo) & (c0 + 32 <= rhi)) ? s1[i] : -INFINITY;
+        }
+    }
+
+    // ---- online softmax (base 2, lazily rescaled) ---------------------------
+    float mx = s0[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
+    mx = wave_max_xor32(mx) * scale2;
+    const bool raise = mx > m_run + kRescaleSlack;
+    if (__any(raise)) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;   // 0 when m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+        m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;   // rows with no key yet
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        s0[i] = fast_exp2(fmaf(s0[i], scale2, -m_use));
+        s1[i] = fast_exp2(fmaf(s1[i], scale2, -m_use));
+    }
+
+    // ---- O^T += V^T P^T ------------------------------------------------------
+    if constexpr (BF16) {
+        // A operand (V^T: rows = dims, k = keys) from row-major V through the
+        // transposing LDS read: within each 16-lane group, lane c supplies 4
+        // dims of one key row and lane i receives dim i of 4 key rows.
+        const int Gq = lane >> 4, cq = lane & 15;
+        const T* vbase = V + (8 * (Gq >> 1) + (cq >> 2)) * VSTR + 16 * (Gq & 1) + 4 * (cq & 3);
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float lsum0 = 0.f, lsum1 = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const f32x16& sp = (kc < 2) ? s0 : s1;
+            const int o = 8 * (kc & 1);
+            bf16x8 Bp;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) Bp[j] = (__bf16)sp[o + j];
+            // row sums of the probabilities as rounded for the MFMA
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+                lsum0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{Bp[2 * j], Bp[2 * j + 1]}, ones, lsum0, false);
+                lsum1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{Bp[2 * j + 2], Bp[2 * j + 3]}, ones, lsum1, false);
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const T* vp = vbase + 16 * kc * VSTR + 32 * db;
+                const bf16x4 lo = lds_read_tr16(vp);
+                const bf16x4 hi = lds_read_tr16(vp + 4 * VSTR);
+                const bf16x8 A = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bp, acc[db], 0, 0, 0);
+            }
+        }
+        l_run += lsum0 + lsum1;
+    } else {
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const f32x16& sp = kb ? s1 : s0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                ls += sp[i];
+                const int key = 32 * kb + (i >> 2) * 8 + hh * 4 + (i & 3);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(V[key * VSTR + db * 32 + col], sp[i], acc[db], 0,
+                                                                   0, 0);
+            }
+        }
+        l_run += ls;
+    }
+}
+
 template <int D, bool BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     using Lay = PrefillLayout<D, BF16>;
@@ -92,7 +255,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     constexpr int PPT = Lay::PPT;
     constexpr int NQ = Lay::NQ;
     constexpr int NDB = D / 32;   // 32-dim blocks of O^T
-    constexpr int W = BF16 ? 8 : 4;   // dims per Q fragment and lane half
     using St = Stage<D, BF16>;
     using QF = typename std::conditional<BF16, bf16x8, f32x4>::type;
 
@@ -102,7 +264,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index through readfirstlane: everything derived from it (rows,
+    // tile classes, masks) is wave-uniform and branches on it are scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5;      // lane half
     const int col = lane & 31;     // query column of the S^T / O^T tiles
 
@@ -138,7 +302,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const T* __restrict__ vg = static_cast<const T*>(p.v);
     const float2* __restrict__ TF = p.TF;
     const int64_t kv_row = (int64_t)Hkv * D;
-    const int64_t kv_b = (int64_t)b * L * kv_row + (int64_t)g * D;
+    const T* __restrict__ kbase = kg + (int64_t)b * L * kv_row + (int64_t)g * D;
+    const T* __restrict__ vbase = vg + (int64_t)b * L * kv_row + (int64_t)g * D;
 
     if (tid == 0) {
         const TableHeader* th = p.table;
@@ -171,81 +336,51 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     }
     const int NP = nR + (nkt - nL0);
 
-    // ---- query fragments (B operand of S^T = K Q^T) -------------------------
-    // bf16: fragment c holds dims 16c + 8hh + [0, 8); f32: fragment t holds
-    // dims 8t + 4hh + [0, 4).  Partner dims (+D/2) sit in fragment c + NQ/2.
+    const bool q_ok = wave_active && my_q < L;
+    const T* qrow = qg + (((int64_t)b * L + (q_ok ? my_q : 0)) * Hq + head) * D;
     QF qv[NQ];
-    auto load_q = [&](bool remote_view) {
-        const bool ok = wave_active && my_q < L;
-        const int64_t qo = (((int64_t)b * L + (ok ? my_q : 0)) * Hq + head) * D;
-#pragma unroll
-        for (int c = 0; c < NQ; ++c)
-            qv[c] = ok ? *reinterpret_cast<const QF*>(qg + qo + c * 2 * W + W * hh) : QF{};
-        if (remote_view) {
-            const int64_t nq = ok ? my_q - my_q / G : 0;
-#pragma unroll
-            for (int c = 0; c < NQ / 2; ++c)
-#pragma unroll
-                for (int j = 0; j < W; ++j) {
-                    float x = (float)qv[c][j];
-                    float y = (float)qv[c + NQ / 2][j];
-                    rotate_back(x, y, TF[nq * HALF + c * 2 * W + W * hh + j]);
-                    qv[c][j] = (T)x;
-                    qv[c + NQ / 2][j] = (T)y;
-                }
-        }
-    };
+    load_q_frags<D, BF16>(qv, qrow, q_ok, nR > 0, TF, q_ok ? (int64_t)(my_q - my_q / G) : 0, hh);
 
     // ---- staging of one tile: HBM -> registers -> LDS -----------------------
     St st;
-    const int kr = tid >> 3;             // K: key row of this thread
+    const int kr = tid >> 3;             // key row of this thread
     const int f0 = (tid & 7) * PPT;      // K: first frequency of this thread
+    const int v0 = (tid & 7) * Lay::VPT; // V: first dim of this thread
+    auto pass_k0 = [&](int pi) { return (pi < nR ? pi : nL0 + (pi - nR)) * BN; };
     auto stage_load = [&](int pi) {
-        const bool rem = pi < nR;
-        const int k0 = (rem ? pi : nL0 + (pi - nR)) * BN;
-        const int kpos = k0 + kr;
+        const int kpos = pass_k0(pi) + kr;
         const bool ok = kpos < L;
-        const int64_t ko = kv_b + (int64_t)(ok ? kpos : 0) * kv_row;
-        if (ok) {
-            st.x = *reinterpret_cast<const typename St::KV*>(kg + ko + f0);
-            st.y = *reinterpret_cast<const typename St::KV*>(kg + ko + HALF + f0);
-        } else {
-            st.x = typename St::KV{};
-            st.y = typename St::KV{};
-        }
-        if (rem) {
-            const int64_t n = ok ? kpos - kpos / G : 0;
-            const float4* t4 = reinterpret_cast<const float4*>(TF + n * HALF + f0);
+        const T* krow = kbase + (int64_t)(ok ? kpos : 0) * kv_row;
+        const T* vrow = vbase + (int64_t)(ok ? kpos : 0) * kv_row;
+        st.x = ok ? *reinterpret_cast<const typename St::KV*>(krow + f0) : typename St::KV{};
+        st.y = ok ? *reinterpret_cast<const typename St::KV*>(krow + HALF + f0) : typename St::KV{};
+        st.v = ok ? *reinterpret_cast<const typename St::VV*>(vrow + v0) : typename St::VV{};
+        if (pi < nR) {
+            const float4* t4 = reinterpret_cast<const float4*>(TF + (int64_t)(ok ? kpos - kpos / G : 0) * HALF + f0);
 #pragma unroll
             for (int j = 0; j < PPT / 2; ++j) st.cs[j] = t4[j];
         }
-        {
-            const int kpos2 = k0 + kr;
-            st.v = kpos2 < L ? *reinterpret_cast<const typename St::VV*>(vg + kv_b + (int64_t)kpos2 * kv_row +
-                                                                          (tid & 7) * Lay::VPT)
-                             : typename St::VV{};
-        }
     };
     auto stage_store = [&](int pi, int buf) {
-        const bool rem = pi < nR;
-        T* K = sK[buf];
-        if (rem) {
+        T* Kd = sK[buf] + kr * KSTR + f0;
+        if (pi < nR) {
             typename St::KV xr, yr;
-            const float2* cs = reinterpret_cast<const float2*>(st.cs);
 #pragma unroll
             for (int j = 0; j < PPT; ++j) {
+                const float4 c4 = st.cs[j >> 1];
+                const float2 cs = (j & 1) ? make_float2(c4.z, c4.w) : make_float2(c4.x, c4.y);
                 float x = (float)st.x[j], y = (float)st.y[j];
-                rotate_back(x, y, cs[j]);
+                rotate_back(x, y, cs);
                 xr[j] = (T)x;
                 yr[j] = (T)y;
             }
-            *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + f0]) = xr;
-            *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + HALF + f0]) = yr;
+            *reinterpret_cast<typename St::KV*>(Kd) = xr;
+            *reinterpret_cast<typename St::KV*>(Kd + HALF) = yr;
         } else {
-            *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + f0]) = st.x;
-            *reinterpret_cast<typename St::KV*>(&K[kr * KSTR + HALF + f0]) = st.y;
+            *reinterpret_cast<typename St::KV*>(Kd) = st.x;
+            *reinterpret_cast<typename St::KV*>(Kd + HALF) = st.y;
         }
-        *reinterpret_cast<typename St::VV*>(&sV[buf][kr * VSTR + (tid & 7) * Lay::VPT]) = st.v;
+        *reinterpret_cast<typename St::VV*>(&sV[buf][kr * VSTR + v0]) = st.v;
     };
 
     f32x16 acc[NDB];
@@ -254,162 +389,44 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    // ---- one pass: S^T, softmax update, O^T ----------------------------------
-    auto compute = [&](int pi, int buf) {
-        if (!wave_active) return;
-        const bool rem = pi < nR;
-        const int k0 = (rem ? pi : nL0 + (pi - nR)) * BN;
-        const int k1 = k0 + BN - 1;
-        bool act, masked;
-        int nkb;
-        if (rem) {
-            act = p_hi - k0 > w0;
-            masked = p0 - k1 <= w0;                        // some local pair here
-            nkb = act ? min(2, (p_hi - w0 - 1 - k0) / 32 + 1) : 0;
-        } else {
-            act = k0 <= p_hi && (G == 1 || p0 - k1 <= w0);
-            masked = k1 > p0 || (G > 1 && p_hi - k0 > w0);  // causal edge or remote pairs
-            nkb = act ? min(2, (p_hi - k0) / 32 + 1) : 0;
-        }
-        if (!act) return;
-        const T* K = sK[buf];
-        const T* V = sV[buf];
-
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (kb >= nkb) break;
-            f32x16 a = f32x16{};
-            if constexpr (BF16) {
-                // A-operand row `col` holds key 32kb + sigma(col); sigma makes the
-                // C rows land so that P^T feeds the PV MFMA in natural key order.
-                const int a3 = col >> 3, hp = (col >> 2) & 1, e = col & 3;
-                const int krow = 32 * kb + 16 * (a3 >> 1) + 8 * hp + 4 * (a3 & 1) + e;
-#pragma unroll
-                for (int c = 0; c < NQ; ++c) {
-                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(&K[krow * KSTR + 16 * c + 8 * hh]);
-                    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[c], a, 0, 0, 0);
-                }
-            } else {
-                const int krow = 32 * kb + col;
-#pragma unroll
-                for (int t = 0; t < NQ; ++t) {
-                    const f32x4 A = *reinterpret_cast<const f32x4*>(&K[krow * KSTR + 8 * t + 4 * hh]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) a = __builtin_amdgcn_mfma_f32_32x32x2f32(A[e], qv[t][e], a, 0, 0, 0);
-                }
-            }
-            s[kb] = a;
-        }
-        if (masked) {
-            // keep keys in [klo, khi]; the remote view keeps q - k > w0, the
-            // local view 0 <= q - k <= w0 (no lower bound when G == 1)
-            const int klo = (rem || G == 1) ? INT_MIN / 2 : my_q - w0;
-            const int khi = rem ? my_q - w0 - 1 : my_q;
-            const int lane_off = BF16 ? 8 * hh : 4 * hh;
-            const int rlo = klo - k0 - lane_off;
-            const int rhi = khi - k0 - lane_off;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb >= nkb) break;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int c = BF16 ? 32 * kb + 16 * (i >> 3) + (i & 7) : 32 * kb + (i >> 2) * 8 + (i & 3);
-                    s[kb][i] = ((c >= rlo) & (c <= rhi)) ? s[kb][i] : -INFINITY;
-                }
-            }
-        }
-
-        // ---- online softmax (base 2, lazily rescaled) ----------------------------
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (kb >= nkb) break;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        }
-        mx = wave_max_xor32(mx) * scale2;
-        const bool raise = mx > m_run + kRescaleSlack;
-        if (__any(raise)) {
-            const float m_new = raise ? mx : m_run;
-            const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;   // 0 when m_run = -inf
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-            m_run = m_new;
-        }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;   // rows with no key yet
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (kb >= nkb) break;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(fmaf(s[kb][i], scale2, -m_use));
-        }
-
-        // ---- O^T += V^T P^T ----------------------------------------------------
-        if constexpr (BF16) {
-            // A operand (V^T rows = dims, k = keys) from row-major V with the
-            // transposing LDS read: within each 16-lane group, lane c supplies
-            // 4 dims of one key row and lane i receives dim i of 4 key rows.
-            const int Gq = lane >> 4, cq = lane & 15;
-            const int tr_key = 8 * (Gq >> 1) + (cq >> 2);
-            const int tr_dim = 16 * (Gq & 1) + 4 * (cq & 3);
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-            float lsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                if (kc >= 2 * nkb) break;
-                bf16x8 Bp;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) Bp[j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
-                // row sums of the probabilities as rounded for the MFMA
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    lsum[kc] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{Bp[2 * j], Bp[2 * j + 1]}, ones, lsum[kc], false);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const __bf16* vp = &V[(16 * kc + tr_key) * VSTR + 32 * db + tr_dim];
-                    const bf16x4 lo = lds_read_tr16(vp);
-                    const bf16x4 hi = lds_read_tr16(vp + 4 * VSTR);
-                    const bf16x8 A = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bp, acc[db], 0, 0, 0);
-                }
-            }
-            l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (kb >= nkb) break;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    l_run += s[kb][i];
-                    const int key = 32 * kb + (i >> 2) * 8 + hh * 4 + (i & 3);
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(V[key * VSTR + db * 32 + col], s[kb][i],
-                                                                       acc[db], 0, 0, 0);
-                }
-            }
-        }
-    };
-
     // ---- software pipeline over the passes --------------------------------------
-    load_q(nR > 0);
     stage_load(0);
     stage_store(0, 0);
     __syncthreads();
     for (int pi = 0; pi < NP; ++pi) {
         const int buf = pi & 1;
         if (pi + 1 < NP) stage_load(pi + 1);
-        if (pi == nR && nR > 0) load_q(false);   // switch to the local view
-        compute(pi, buf);
+        if (pi == nR && nR > 0) load_q_frags<D, BF16>(qv, qrow, q_ok, false, TF, 0, hh);   // local view
+        if (wave_active) {
+            const bool rem = pi < nR;
+            const int k0 = pass_k0(pi);
+            const int k1 = k0 + BN - 1;
+            bool act, masked;
+            if (rem) {
+                act = p_hi - k0 > w0;
+                masked = p0 - k1 <= w0;                          // some local pair here
+            } else {
+                act = k0 <= p_hi && (G == 1 || p0 - k1 <= w0);
+                masked = k1 > p0 || (G > 1 && p_hi - k0 > w0);  // causal edge or remote pairs
+            }
+            if (act) {
+                // masked tiles keep keys in [klo, khi]: the remote view keeps
+                // q - k > w0, the local view 0 <= q - k <= w0 (no lower bound
+                // if G == 1)
+                const int klo = (rem || G == 1) ? INT_MIN / 2 : my_q - w0;
+                const int khi = rem ? my_q - w0 - 1 : my_q;
+                const int off = k0 + (BF16 ? 8 * hh : 4 * hh);
+                tile_step<D, BF16>(sK[buf], sV[buf], qv, acc, m_run, l_run, col, hh, lane, masked, klo - off,
+                                   khi - off, scale2);
+            }
+        }
         if (pi + 1 < NP) stage_store(pi + 1, buf ^ 1);
         __syncthreads();
     }
 
     // ---- epilogue ---------------------------------------------------------------
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (wave_active && my_q < L) {
+    if (q_ok) {
         const float inv = 1.f / l_tot;
         const int64_t o = (((int64_t)b * L + my_q) * Hq + head) * D;
 #pragma unroll
@@ -446,13 +463,10 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, int in_dtype, int out_dtype, hipStream_t stream) {
-    const bool in_bf16 = in_dtype == 1;
-    const bool out_bf16 = out_dtype == 1;
-    if (p.head_dim == 128) {
-        if (in_bf16) return out_bf16 ? launch_one<128, true, true>(p, stream) : launch_one<128, true, false>(p, stream);
-        return launch_one<128, false, false>(p, stream);
-    }
-    if (in_bf16) return out_bf16 ? launch_one<64, true, true>(p, stream) : launch_one<64, true, false>(p, stream);
+    // bf16 inputs take the 64-rows-per-wave kernel; fp32 inputs this one
+    if (in_dtype == 1) return launch_prefill_bf16(p, out_dtype, stream);
+    (void)out_dtype;
+    if (p.head_dim == 128) return launch_one<128, false, false>(p, stream);
     return launch_one<64, false, false>(p, stream);
 }
 
