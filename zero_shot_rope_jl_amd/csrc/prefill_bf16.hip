@@ -3,17 +3,16 @@
 // Method (Jet-Long, §3 Eq. 1; §3.1 Eqs. 2-3; §3.2 Eq. 5; §3.3 Eq. 6): a
 // query/key pair with q - k <= w0 scores with the stored RoPE vectors; a pair
 // with q - k > w0 scores with both vectors rotated by their correction offset
-// f(p) - p, f(p) = floor(p/G).  Both views feed one online softmax per query
-// row, which realises the inclusion-exclusion merge exactly (the overlap term
-// is removed by masking, not subtracted).
+// f(p) - p, f(p) = floor(p/G).  Both views feed one softmax per query row,
+// which realises the inclusion-exclusion merge exactly (the overlap term is
+// removed by masking, not subtracted).
 //
 // Work decomposition (one workgroup = 4 waves = 256 query rows of one KV head)
 //   Rows are ordered head-major over the R = Hq/Hkv query heads of the KV
 //   head and BQ = 256/R positions; wave w owns rows [64w, 64w + 64) as two
 //   32-row query blocks.  Every K or V^T fragment read from LDS feeds the
-//   MFMAs of both blocks, which halves LDS traffic per flop: with 32x32x16
-//   bf16 MFMAs a single block would need the whole LDS read bandwidth of a
-//   compute unit.  One wave per SIMD; the output accumulators live in AGPRs.
+//   MFMAs of both blocks, which halves LDS traffic per flop.  One wave per
+//   SIMD; the output accumulators live in AGPRs.
 //
 //   Key tiles of 64 are walked in two phases: a remote phase over every tile
 //   that holds a remote pair (K rotated by its correction on the way into
@@ -21,21 +20,28 @@
 //   holds a local pair (stored K and Q).  A tile that straddles the window
 //   edge is visited once per phase under a mask.
 //
-//   Pipeline: LDS is double-buffered.  At the start of a tile the next tile's
-//   V is streamed HBM -> LDS with global_load_lds (no registers; 16-byte
-//   chunks XOR-swizzled by row so that the transposed reads below spread over
-//   the LDS banks) and its K and correction rows are loaded into registers;
-//   after the MFMAs K is rotated (remote view) and written to LDS.  One
-//   barrier per tile.
+//   Staging: LDS is double-buffered.  At the start of a tile the next tile's
+//   V and the correction rows it needs are copied HBM -> LDS with buffer
+//   loads into LDS (no registers; V chunks XOR-swizzled by row so that the
+//   transposed reads below spread over the banks), and its K is loaded into
+//   registers; after the MFMAs K is rotated and written to LDS.  One barrier
+//   per tile.
 //
-//   Each wave computes S^T = K Q^T (keys on the MFMA M axis, queries on N):
-//   a query's 64 scores sit in one lane pair, so the row max needs one
-//   cross-half exchange and P^T is already the B operand of O^T += V^T P^T,
-//   whose V^T operand comes from row-major V through ds_read_b64_tr_b16.
-//   The running max is raised (and the accumulator rescaled) only when a
-//   tile's max exceeds it by more than 2^8.
+//   Scores: each wave computes S^T = K Q^T (keys on the MFMA M axis, queries
+//   on N), so a query's scores sit in one lane pair and P^T is already the B
+//   operand of O^T += V^T P^T, whose V^T operand comes from row-major V
+//   through ds_read_b64_tr_b16.  Q is pre-multiplied by sm_scale * log2(e).
+//   Each row's reference max m is fixed (rounded to bf16) at the first tile
+//   that gives it a key and never moved; the score MFMA chain subtracts it
+//   through one extra rank-1 step (a constant K chunk of ones against a Q
+//   chunk holding -m), so P = exp2(S) needs no per-element subtraction and
+//   the accumulators are touched by MFMAs only.  Probabilities above 1 are
+//   harmless (fp32 and bf16 share the exponent range; the final division
+//   restores the scale).
 #include <limits.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -45,8 +51,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int BN = 64;                  // keys per tile
-constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr int BN = 64;                        // keys per tile
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer resource, 32-bit elements
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -55,33 +61,19 @@ __device__ inline bf16x4 lds_read_tr16(const __bf16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// 16-byte HBM -> LDS copy per lane; lane l writes bytes [16l, 16l + 16) after
-// the wave-uniform LDS base.
-__device__ inline void load_lds16(const void* src, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src),
-                                     (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+// Buffer resource over [base, base + bytes): loads beyond `bytes` return 0.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+// 16-byte buffer -> LDS copy per lane; lane l writes bytes [16l, 16l + 16)
+// after the wave-uniform LDS base.
+__device__ inline void buffer_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_base), 16, voff, soff,
+                                             0, 0);
 }
 
 __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// acc *= alpha in place in the accumulation registers.  Written out so that
-// the compiler never keeps a VGPR copy of the accumulators for the (rare)
-// rescale; the trailing nops cover an MFMA that reads the result next.
-__device__ inline void scale_acc(f32x16& acc, float alpha) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float x = acc[i];
-        float t;
-        asm volatile(
-            "v_accvgpr_read_b32 %1, %0\n\t"
-            "v_mul_f32 %1, %1, %2\n\t"
-            "v_accvgpr_write_b32 %0, %1"
-            : "+a"(x), "=&v"(t)
-            : "v"(alpha));
-        acc[i] = x;
-    }
-    asm volatile("s_nop 2");
-}
 
 template <int D>
 struct Lay5 {
@@ -111,8 +103,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     constexpr int PPT = Lay::PPT;
     typedef __bf16 KV __attribute__((ext_vector_type(PPT)));
 
-    __shared__ __attribute__((aligned(16))) __bf16 sK[2][BN * KSTR];
-    __shared__ __attribute__((aligned(16))) __bf16 sV[2][BN * D];
+    // Two LDS buffers per operand, as separate objects and always selected at
+    // compile time: the compiler can then tell that the HBM->LDS copy into
+    // one buffer does not alias the reads of the other, and does not make
+    // those reads wait for the copy.
+    __shared__ __attribute__((aligned(16))) __bf16 sK0[BN * KSTR];
+    __shared__ __attribute__((aligned(16))) __bf16 sK1[BN * KSTR];
+    __shared__ __attribute__((aligned(16))) __bf16 sV0[BN * D];
+    __shared__ __attribute__((aligned(16))) __bf16 sV1[BN * D];
+    // correction rows for the tile being staged, one region of BN/4 rows per
+    // wave (the rows its own K rows need), 16-byte chunks XOR-swizzled by row
+    __shared__ __attribute__((aligned(16))) float2 sT[BN * HALF];
     __shared__ int s_bad;
 
     // Naming an accumulation register keeps the compiler from assuming the
@@ -163,6 +164,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const __bf16* __restrict__ qg = static_cast<const __bf16*>(p.q);
     const float2* __restrict__ TF = p.TF;
     const int64_t kv_row = (int64_t)Hkv * D;
+    const uint32_t row_bytes = (uint32_t)kv_row * 2u;
     const __bf16* __restrict__ kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * L * kv_row + (int64_t)g * D;
     const __bf16* __restrict__ vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * L * kv_row + (int64_t)g * D;
 
@@ -197,27 +199,35 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     }
     const int NP = nR + (nkt - nL0);
 
-    // ---- query fragments: B operand, fragment c = dims 16c + 8hh + [0, 8) ----
-    // Rows past L read row L-1 (finite values, never stored).
+    // ---- query fragments ---------------------------------------------------------
+    // B operand, fragment c = dims 16c + 8hh + [0, 8), multiplied by
+    // sm_scale * log2(e) before the bf16 rounding, so the MFMA yields scores in
+    // log2 units.  Rows past L read row L-1 (finite values, never stored).
     bf16x8 qv[2][NC];
-    auto load_q = [&](bool remote_view) {
+    auto load_q = [&](bool remote_view) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int qpos = min(my_q[j], L - 1);
             const __bf16* qrow = qg + (((int64_t)b * L + qpos) * Hq + head[j]) * D;
+            bf16x8 raw[NC];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) qv[j][c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * hh);
+            for (int c = 0; c < NC; ++c) raw[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * hh);
             if (remote_view) {
                 const int64_t nq = qpos - qpos / G;
 #pragma unroll
                 for (int c = 0; c < NC / 2; ++c)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        float x = (float)qv[j][c][e], y = (float)qv[j][c + NC / 2][e];
+                        float x = (float)raw[c][e], y = (float)raw[c + NC / 2][e];
                         rotate_back(x, y, TF[nq * HALF + 16 * c + 8 * hh + e]);
-                        qv[j][c][e] = (__bf16)x;
-                        qv[j][c + NC / 2][e] = (__bf16)y;
+                        qv[j][c][e] = (__bf16)(x * scale2);
+                        qv[j][c + NC / 2][e] = (__bf16)(y * scale2);
                     }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qv[j][c][e] = (__bf16)((float)raw[c][e] * scale2);
             }
         }
     };
@@ -225,54 +235,112 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // ---- staging of the next tile ------------------------------------------------
     // Every tile is rotated on its way into LDS: remote tiles by their
     // correction rows, local tiles by table row 0, which is exactly (1, 0).
+    // Wave w stages K rows 16w .. 16w+15.  Their correction rows form one
+    // contiguous range of the table (n(k) = k - floor(k/G) rises by 0 or 1 per
+    // key), which the wave copies to its own LDS region with the V tile; K
+    // goes through registers.  A wave reads only rows it copied itself, so
+    // its own wait on the copy suffices.  All loads go through buffer
+    // resources over the tile's rows: lane offsets stay fixed, the tile base
+    // is scalar, and rows past L read as zeros (they are masked).
+    constexpr int RW = BN / kWaves;                // K rows per wave
+    constexpr int TCH = HALF / 2;                  // 16-byte chunks per table row
+    constexpr int SWM = (PPT / 2 < 8 ? PPT / 2 : 8) - 1;   // table chunk swizzle mask
+    constexpr int VU = BN * CH / kThreads;         // V copies per thread
+    constexpr int VRU = kThreads / CH;             // V rows per copy step
+    constexpr int TU = RW * TCH / 64;              // table copies per thread
+    static_assert(Lay::TPR * RW == 64, "a wave stages whole K rows");
+    static_assert(VRU % 4 == 0, "V swizzle is lane-constant");
     const int kr = tid / Lay::TPR;                 // K row of this thread
     const int f0 = (tid % Lay::TPR) * PPT;         // first frequency of this thread
+    // lane-constant byte offsets
+    const uint32_t v_voff = (uint32_t)(tid / CH) * row_bytes + 16u * (uint32_t)vswz<D>(tid / CH, tid % CH);
+    const uint32_t k_voff = (uint32_t)kr * row_bytes + 2u * (uint32_t)f0;
+    auto t_voff = [&](int u) __attribute__((always_inline)) {
+        const int P = u * 64 + lane;
+        const int row = P / TCH;
+        return (uint32_t)(row * HALF * 8 + 16 * ((P % TCH) ^ (row & SWM)));
+    };
     KV stx, sty;
-    float4 stc[PPT / 2];
-    auto tile_k0 = [&](int pi) { return (pi < nR ? pi : nL0 + (pi - nR)) * BN; };
-    auto stage_load = [&](int pi, int buf) {
+    int st_row;                                    // this thread's row in its wave's region
+    char* const sTw = reinterpret_cast<char*>(sT) + wave * RW * HALF * 8;
+    // remote offsets within a wave's rows: n(k) - n(kw) = (k - kw) - floor(a/G)
+    // with a = (kw mod G) + (k - kw) < G + 16; for G > 16 that floor is
+    // (a >= G); for G <= 16, floor((a + 1/2) / G) in float is exact (half-step
+    // margin against a rounding error below 2^-18).
+    const float invG = 1.0f / (float)G;
+    auto small_floor_div = [&](int a) __attribute__((always_inline)) {
+        return G > 16 ? (int)(a >= G) : (int)floorf(fmaf((float)a, invG, 0.5f * invG));
+    };
+    auto tile_k0 = [&](int pi) __attribute__((always_inline)) { return (pi < nR ? pi : nL0 + (pi - nR)) * BN; };
+    auto stage_load = [&](int pi, auto buf) __attribute__((always_inline)) {
+        __bf16* sVd = decltype(buf)::value ? sV1 : sV0;
         const int k0 = tile_k0(pi);
-        // V: 64 rows x CH chunks, BN*CH/256 wave-instructions of 64 chunks each
+        const uint32_t tile_bytes = (uint32_t)min(L - k0, BN) * row_bytes;
+        // V: 64 rows x CH chunks
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)k0 * kv_row, tile_bytes);
 #pragma unroll
-        for (int u = 0; u < BN * CH / kThreads; ++u) {
-            const int P = (u * kWaves + wave) * 64 + lane;   // physical chunk in the tile
-            const int row = P / CH;
-            const int lc = vswz<D>(row, P % CH);           // logical chunk stored there
-            const int key = min(k0 + row, L - 1);           // rows beyond L: finite, masked out
-            load_lds16(vbase + (int64_t)key * kv_row + 8 * lc, &sV[buf][(u * kWaves + wave) * 64 * 8]);
+        for (int u = 0; u < VU; ++u)
+            buffer_lds16(rv, &sVd[(u * kWaves + wave) * 64 * 8], v_voff, (uint32_t)(u * VRU) * row_bytes);
+        // correction rows of this wave's K rows (row 0 and up for a local tile)
+        const bool rem = pi < nR;
+        const int kw = min(k0 + RW * wave, L - 1);
+        const int kwq = kw / G;
+        const int t0 = rem ? kw - kwq : 0;
+        const __amdgpu_buffer_rsrc_t rt = make_rsrc(TF + (int64_t)t0 * HALF, (uint32_t)min(L - t0, RW) * HALF * 8u);
+#pragma unroll
+        for (int u = 0; u < TU; ++u) buffer_lds16(rt, sTw + u * 64 * 16, t_voff(u), 0);
+        // K into registers
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)k0 * kv_row, tile_bytes);
+#pragma unroll
+        for (int c = 0; c < PPT / 8; ++c) {
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 16u * c, 0, 0);
+            const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 2u * HALF + 16u * c, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                stx[8 * c + e] = __builtin_bit_cast(bf16x8, x)[e];
+                sty[8 * c + e] = __builtin_bit_cast(bf16x8, y)[e];
+            }
         }
         const int kpos = min(k0 + kr, L - 1);
-        const __bf16* krow = kbase + (int64_t)kpos * kv_row;
-        stx = *reinterpret_cast<const KV*>(krow + f0);
-        sty = *reinterpret_cast<const KV*>(krow + HALF + f0);
-        const int64_t tn = pi < nR ? kpos - kpos / G : 0;
-        const float4* t4 = reinterpret_cast<const float4*>(TF + tn * HALF + f0);
-#pragma unroll
-        for (int e = 0; e < PPT / 2; ++e) stc[e] = t4[e];
+        st_row = rem ? (kpos - kw) - small_floor_div(kw - kwq * G + (kpos - kw)) : 0;
     };
-    auto stage_store = [&](int buf) {
-        __bf16* Kd = sK[buf] + kr * KSTR + f0;
+    auto stage_store = [&](auto buf) __attribute__((always_inline)) {
+        __bf16* Kd = (decltype(buf)::value ? sK1 : sK0) + kr * KSTR + f0;
+        // chunk (f0/2 + e) of the row sits at position (f0/2 + e) ^ (row & SWM);
+        // f0/2 is a multiple of SWM + 1, so that is f0/2 + (e ^ (row & SWM))
+        const char* tbase = sTw + st_row * (HALF * 8) + 8 * f0;
+        const int sw = st_row & SWM;
         KV xr, yr;
 #pragma unroll
-        for (int e = 0; e < PPT; ++e) {
-            const float4 c4 = stc[e >> 1];
-            const float2 cs = (e & 1) ? make_float2(c4.z, c4.w) : make_float2(c4.x, c4.y);
-            float x = (float)stx[e], y = (float)sty[e];
-            rotate_back(x, y, cs);
-            xr[e] = (__bf16)x;
-            yr[e] = (__bf16)y;
+        for (int e = 0; e < PPT / 2; ++e) {
+            const float4 c4 = *reinterpret_cast<const float4*>(tbase + 16 * (e ^ sw));
+            float x0 = (float)stx[2 * e], y0 = (float)sty[2 * e];
+            float x1 = (float)stx[2 * e + 1], y1 = (float)sty[2 * e + 1];
+            rotate_back(x0, y0, make_float2(c4.x, c4.y));
+            rotate_back(x1, y1, make_float2(c4.z, c4.w));
+            xr[2 * e] = (__bf16)x0;
+            yr[2 * e] = (__bf16)y0;
+            xr[2 * e + 1] = (__bf16)x1;
+            yr[2 * e + 1] = (__bf16)y1;
         }
         *reinterpret_cast<KV*>(Kd) = xr;
         *reinterpret_cast<KV*>(Kd + HALF) = yr;
     };
 
+    // ---- softmax state -------------------------------------------------------------
+    // m_ref: the row's reference max (log2 units, a bf16 value), -inf until the
+    // row meets its first key; qx holds -m_ref as the extra B chunk of the
+    // score MFMA; l_run: row sum of probabilities.
     f32x16 acc[2][NDB];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[j][db] = f32x16{};
-    float m_run[2] = {-INFINITY, -INFINITY};
+    float m_ref[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
+    bf16x8 qx[2] = {bf16x8{}, bf16x8{}};
+    bf16x8 kone = bf16x8{};
+    if (hh == 0) kone[0] = (__bf16)1.0f;
 
     // K A-operand row of this lane in each 32-key block (sigma makes the C
     // rows land so that P^T feeds the PV MFMA in natural key order)
@@ -283,13 +351,118 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const int Gq = lane >> 4, cq = lane & 15;
     const int tr_row = 8 * (Gq >> 1) + (cq >> 2);
     const int tr_dim = 16 * (Gq & 1) + 4 * (cq & 3);
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // One tile: S, masks, online softmax and PV for both query blocks, with
-    // the next tile's staging wrapped around it.  Tiles without a kept pair
-    // for a block run fully masked rather than branch.
-    auto tile = [&](int pi) {
-        const int buf = pi & 1;
-        stage_load(pi + 1 < NP ? pi + 1 : pi, buf ^ 1);   // the last tile refills the idle buffer
+    // S^T - m_ref for one 32-key half, both query blocks; each K fragment
+    // feeds both; the last step adds the rank-1 term ones x (-m_ref).
+    auto qk = [&](const __bf16* K, int kb, f32x16 (&s)[2]) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        const __bf16* kp = K + (32 * kb + krow_l) * KSTR + 8 * hh;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const bf16x8 A = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[0][c], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[1][c], s[1], 0, 0, 0);
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, qx[0], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, qx[1], s[1], 0, 0, 0);
+    };
+    // O^T += V^T P^T for one 32-key half; each V^T fragment feeds both blocks.
+    auto pv = [&](const __bf16* V, int kb, const bf16x8 (&P)[2][2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r0 = 32 * kb + 16 * h + tr_row;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                // logical chunk of dims 32db + tr_dim and its swizzled place
+                const int lc = (32 * db + tr_dim) >> 3;
+                const int wi = tr_dim & 7;
+                const bf16x4 lo = lds_read_tr16(V + r0 * D + 8 * vswz<D>(r0, lc) + wi);
+                const bf16x4 hi = lds_read_tr16(V + (r0 + 4) * D + 8 * vswz<D>(r0 + 4, lc) + wi);
+                const bf16x8 A = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[0][h], acc[0][db], 0, 0, 0);
+                acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[1][h], acc[1][db], 0, 0, 0);
+            }
+        }
+    };
+    // P = exp2(S - m_ref) as rounded for the MFMA, and the row sums of those
+    // rounded values.
+    auto probs = [&](const f32x16 (&s)[2], bf16x8 (&P)[2][2]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) P[j][h][e] = (__bf16)fast_exp2(s[j][8 * h + e]);
+            float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][0], P[j][h][1]}, ones, ls0, false);
+                ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][2], P[j][h][3]}, ones, ls1, false);
+                ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][4], P[j][h][5]}, ones, ls0, false);
+                ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][6], P[j][h][7]}, ones, ls1, false);
+            }
+            l_run[j] += ls0 + ls1;
+        }
+    };
+
+    // Window-edge, causal-diagonal and ragged tiles mask scores per element;
+    // a row meeting its first keys takes this half's max (rounded to bf16) as
+    // its reference, which is subtracted here once and by the MFMA after.
+    auto edge_fix = [&](f32x16 (&s)[2], int kb, const int (&rlo)[2], const int (&rhi)[2]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int c0 = 32 * kb + 16 * (i >> 3) + (i & 7);
+                s[j][i] = ((c0 >= rlo[j]) & (c0 <= rhi[j])) ? s[j][i] : -INFINITY;
+            }
+            float m = s[j][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) m = fmaxf(m, s[j][i]);
+            m = wave_max_xor32(m);
+            const bool first = (m_ref[j] == -INFINITY) & (m != -INFINITY);
+            const float mb = (float)(__bf16)m;
+            const float d = first ? mb : 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[j][i] -= d;
+            m_ref[j] = first ? mb : m_ref[j];
+            qx[j][0] = (hh == 0 && m_ref[j] != -INFINITY) ? (__bf16)(-m_ref[j]) : (__bf16)0.0f;
+        }
+    };
+
+    // One tile as straight-line regions, so that MFMAs and VALU work
+    // interleave: S(h0) | S(h1) with softmax(h0) | PV(h0) with softmax(h1) |
+    // PV(h1) with the rotation of the next tile's K.  The rare edge work sits
+    // in uniform branches between regions and never touches the accumulators.
+    auto tile_body = [&](auto buf, bool edge, const int (&rlo)[2], const int (&rhi)[2]) __attribute__((always_inline)) {
+        using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
+        const __bf16* K = decltype(buf)::value ? sK1 : sK0;
+        const __bf16* V = decltype(buf)::value ? sV1 : sV0;
+        f32x16 s0[2], s1[2];
+        bf16x8 P0[2][2], P1[2][2];
+        qk(K, 0, s0);
+        if (edge) edge_fix(s0, 0, rlo, rhi);
+        qk(K, 1, s1);
+        probs(s0, P0);
+        // keep softmax(h0) in the region of S(h1): without a use here the
+        // compiler sinks it below the branch, next to PV(h0)
+        asm volatile("" ::"v"(P0[0][0]), "v"(P0[0][1]), "v"(P0[1][0]), "v"(P0[1][1]));
+        if (edge) edge_fix(s1, 1, rlo, rhi);
+        pv(V, 0, P0);
+        probs(s1, P1);
+        pv(V, 1, P1);
+        stage_store(Other{});
+    };
+
+    using Buf0 = std::integral_constant<int, 0>;
+    using Buf1 = std::integral_constant<int, 1>;
+    // tile pi computes from buffer pi & 1 (= buf) and stages tile pi + 1 into the other
+    auto tile = [&](int pi, auto buf) __attribute__((always_inline)) {
+        using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
+        if (pi == nR && nR > 0) load_q(false);   // the local phase starts: stored Q
+        stage_load(pi + 1 < NP ? pi + 1 : pi, Other{});   // the last tile refills the idle buffer
         const bool rem = pi < nR;
         const int k0 = tile_k0(pi);
         const int k1 = k0 + BN - 1;
@@ -313,102 +486,28 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             rlo[j] = act ? klo - k0 - 8 * hh : 1;
             rhi[j] = act ? khi - k0 - 8 * hh : 0;
             msk[j] = msk[j] || !act;
-        }
-        const __bf16* K = sK[buf];
-        const __bf16* V = sV[buf];
-        // two 32-key halves per tile keep the score and probability registers
-        // of both query blocks small
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            // ---- S^T = K Q^T: each K fragment feeds both query blocks ---------
-            f32x16 s[2] = {f32x16{}, f32x16{}};
-            const __bf16* kp = K + (32 * kb + krow_l) * KSTR + 8 * hh;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const bf16x8 A = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
-                s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[0][c], s[0], 0, 0, 0);
-                s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[1][c], s[1], 0, 0, 0);
-            }
-            // ---- masks and running max --------------------------------------------
-            float mx[2];
-            bool raise[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (msk[j]) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int c0 = 32 * kb + 16 * (i >> 3) + (i & 7);
-                        s[j][i] = ((c0 >= rlo[j]) & (c0 <= rhi[j])) ? s[j][i] : -INFINITY;
-                    }
-                }
-                float m = s[j][0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) m = fmaxf(m, s[j][i]);
-                mx[j] = wave_max_xor32(m) * scale2;
-                raise[j] = mx[j] > m_run[j] + kRescaleSlack;
-            }
-            if (__any(raise[0] | raise[1])) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float m_new = raise[j] ? mx[j] : m_run[j];
-                    const float alpha = raise[j] ? fast_exp2(m_run[j] - m_new) : 1.f;   // 0 when m_run = -inf
-                    l_run[j] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) scale_acc(acc[j][db], alpha);
-                    m_run[j] = m_new;
-                }
-            }
-            // ---- probabilities (bf16, as the PV MFMA consumes them) ----------------
-            bf16x8 P[2][2];
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float m_use = m_run[j] == -INFINITY ? 0.f : m_run[j];   // rows with no key yet
-                float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        P[j][h][e] = (__bf16)fast_exp2(fmaf(s[j][8 * h + e], scale2, -m_use));
-                    ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][0], P[j][h][1]}, ones, ls0, false);
-                    ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][2], P[j][h][3]}, ones, ls1, false);
-                    ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][4], P[j][h][5]}, ones, ls0, false);
-                    ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][6], P[j][h][7]}, ones, ls1, false);
-                }
-                l_run[j] += ls0 + ls1;
-            }
-            // ---- O^T += V^T P^T: each V^T fragment feeds both query blocks ---------
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int r0 = 32 * kb + 16 * h + tr_row;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    // logical chunk of dims 32db + tr_dim and its swizzled place
-                    const int lc = (32 * db + tr_dim) >> 3;
-                    const int wi = tr_dim & 7;
-                    const bf16x4 lo = lds_read_tr16(V + r0 * D + 8 * vswz<D>(r0, lc) + wi);
-                    const bf16x4 hi = lds_read_tr16(V + (r0 + 4) * D + 8 * vswz<D>(r0 + 4, lc) + wi);
-                    const bf16x8 A = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[0][h], acc[0][db], 0, 0, 0);
-                    acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[1][h], acc[1][db], 0, 0, 0);
-                }
+            if (!msk[j]) {   // every pair kept
+                rlo[j] = INT_MIN / 2;
+                rhi[j] = INT_MAX / 2;
             }
         }
-        stage_store(buf ^ 1);
+        const bool edge = msk[0] || msk[1] || __any((m_ref[0] == -INFINITY) | (m_ref[1] == -INFINITY));
+        tile_body(buf, edge, rlo, rhi);
         wait_vmem();   // the next tile's V has landed in LDS
         __syncthreads();
     };
 
-    stage_load(0, 0);
-    stage_store(0);
+    stage_load(0, Buf0{});
+    stage_store(Buf0{});
     wait_vmem();
     __syncthreads();
-    if (nR > 0) {
-        load_q(true);
-        for (int pi = 0; pi < nR; ++pi) tile(pi);
+    load_q(nR > 0);
+    int pi = 0;
+    for (; pi + 1 < NP; pi += 2) {
+        tile(pi, Buf0{});
+        tile(pi + 1, Buf1{});
     }
-    load_q(false);
-    for (int pi = nR; pi < NP; ++pi) tile(pi);
+    if (pi < NP) tile(pi, Buf0{});
 
     // ---- epilogue ---------------------------------------------------------------
 #pragma unroll
@@ -436,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             }
         }
         if (hh == 0 && p.lse)
-            p.lse[((int64_t)b * Hq + head[j]) * L + my_q[j]] = (m_run[j] + log2f(l_tot)) * 0.69314718055994531f;
+            p.lse[((int64_t)b * Hq + head[j]) * L + my_q[j]] = (m_ref[j] + log2f(l_tot)) * 0.69314718055994531f;
     }
 }
 
