@@ -272,23 +272,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         return G > 16 ? (int)(a >= G) : (int)floorf(fmaf((float)a, invG, 0.5f * invG));
     };
     auto tile_k0 = [&](int pi) __attribute__((always_inline)) { return (pi < nR ? pi : nL0 + (pi - nR)) * BN; };
-    auto stage_load = [&](int pi, auto buf) __attribute__((always_inline)) {
+    // staging is issued in two parts spread over the tile, so that the
+    // vector-memory queue never fills and stalls the wave: K (registers) and
+    // V (LDS) at the start, the correction rows with the second score half
+    auto stage_load_kv = [&](int pi, auto buf) __attribute__((always_inline)) {
         __bf16* sVd = decltype(buf)::value ? sV1 : sV0;
         const int k0 = tile_k0(pi);
         const uint32_t tile_bytes = (uint32_t)min(L - k0, BN) * row_bytes;
-        // V: 64 rows x CH chunks
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)k0 * kv_row, tile_bytes);
-#pragma unroll
-        for (int u = 0; u < VU; ++u)
-            buffer_lds16(rv, &sVd[(u * kWaves + wave) * 64 * 8], v_voff, (uint32_t)(u * VRU) * row_bytes);
-        // correction rows of this wave's K rows (row 0 and up for a local tile)
-        const bool rem = pi < nR;
-        const int kw = min(k0 + RW * wave, L - 1);
-        const int kwq = kw / G;
-        const int t0 = rem ? kw - kwq : 0;
-        const __amdgpu_buffer_rsrc_t rt = make_rsrc(TF + (int64_t)t0 * HALF, (uint32_t)min(L - t0, RW) * HALF * 8u);
-#pragma unroll
-        for (int u = 0; u < TU; ++u) buffer_lds16(rt, sTw + u * 64 * 16, t_voff(u), 0);
         // K into registers
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)k0 * kv_row, tile_bytes);
 #pragma unroll
@@ -301,6 +291,22 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
                 sty[8 * c + e] = __builtin_bit_cast(bf16x8, y)[e];
             }
         }
+        // V: 64 rows x CH chunks
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)k0 * kv_row, tile_bytes);
+#pragma unroll
+        for (int u = 0; u < VU; ++u)
+            buffer_lds16(rv, &sVd[(u * kWaves + wave) * 64 * 8], v_voff, (uint32_t)(u * VRU) * row_bytes);
+    };
+    auto stage_load_t = [&](int pi) __attribute__((always_inline)) {
+        // correction rows of this wave's K rows (row 0 and up for a local tile)
+        const int k0 = tile_k0(pi);
+        const bool rem = pi < nR;
+        const int kw = min(k0 + RW * wave, L - 1);
+        const int kwq = kw / G;
+        const int t0 = rem ? kw - kwq : 0;
+        const __amdgpu_buffer_rsrc_t rt = make_rsrc(TF + (int64_t)t0 * HALF, (uint32_t)min(L - t0, RW) * HALF * 8u);
+#pragma unroll
+        for (int u = 0; u < TU; ++u) buffer_lds16(rt, sTw + u * 64 * 16, t_voff(u), 0);
         const int kpos = min(k0 + kr, L - 1);
         st_row = rem ? (kpos - kw) - small_floor_div(kw - kwq * G + (kpos - kw)) : 0;
     };
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // interleave: S(h0) | S(h1) with softmax(h0) | PV(h0) with softmax(h1) |
     // PV(h1) with the rotation of the next tile's K.  The rare edge work sits
     // in uniform branches between regions and never touches the accumulators.
-    auto tile_body = [&](auto buf, bool edge, const int (&rlo)[2], const int (&rhi)[2]) __attribute__((always_inline)) {
+    auto tile_body = [&](auto buf, int pn, bool edge, const int (&rlo)[2], const int (&rhi)[2]) __attribute__((always_inline)) {
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
         const __bf16* K = decltype(buf)::value ? sK1 : sK0;
         const __bf16* V = decltype(buf)::value ? sV1 : sV0;
@@ -445,6 +451,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         qk(K, 0, s0);
         if (edge) edge_fix(s0, 0, rlo, rhi);
         qk(K, 1, s1);
+        stage_load_t(pn);
         probs(s0, P0);
         // keep softmax(h0) in the region of S(h1): without a use here the
         // compiler sinks it below the branch, next to PV(h0)
@@ -462,7 +469,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     auto tile = [&](int pi, auto buf) __attribute__((always_inline)) {
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
         if (pi == nR && nR > 0) load_q(false);   // the local phase starts: stored Q
-        stage_load(pi + 1 < NP ? pi + 1 : pi, Other{});   // the last tile refills the idle buffer
+        const int pn = pi + 1 < NP ? pi + 1 : pi;   // the last tile refills the idle buffer
+        stage_load_kv(pn, Other{});
         const bool rem = pi < nR;
         const int k0 = tile_k0(pi);
         const int k1 = k0 + BN - 1;
@@ -492,12 +500,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             }
         }
         const bool edge = msk[0] || msk[1] || __any((m_ref[0] == -INFINITY) | (m_ref[1] == -INFINITY));
-        tile_body(buf, edge, rlo, rhi);
+        tile_body(buf, pn, edge, rlo, rhi);
         wait_vmem();   // the next tile's V has landed in LDS
         __syncthreads();
     };
 
-    stage_load(0, Buf0{});
+    stage_load_kv(0, Buf0{});
+    stage_load_t(0);
+    wait_vmem();
     stage_store(Buf0{});
     wait_vmem();
     __syncthreads();
