@@ -272,11 +272,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         return G > 16 ? (int)(a >= G) : (int)floorf(fmaf((float)a, invG, 0.5f * invG));
     };
     auto tile_k0 = [&](int pi) __attribute__((always_inline)) { return (pi < nR ? pi : nL0 + (pi - nR)) * BN; };
-    // staging is issued in two parts spread over the tile, so that the
-    // vector-memory queue never fills and stalls the wave: K (registers) and
-    // V (LDS) at the start, the correction rows with the second score half
-    auto stage_load_kv = [&](int pi, auto buf) __attribute__((always_inline)) {
-        __bf16* sVd = decltype(buf)::value ? sV1 : sV0;
+    // staging is issued in three parts spread over the tile, so that the
+    // vector-memory queue never fills and stalls the wave: K (registers) at
+    // the start, the correction rows with the second score half, V with the
+    // first PV half
+    auto stage_load_k = [&](int pi) __attribute__((always_inline)) {
         const int k0 = tile_k0(pi);
         const uint32_t tile_bytes = (uint32_t)min(L - k0, BN) * row_bytes;
         // K into registers
@@ -291,6 +291,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
                 sty[8 * c + e] = __builtin_bit_cast(bf16x8, y)[e];
             }
         }
+    };
+    auto stage_load_v = [&](int pi, auto buf) __attribute__((always_inline)) {
+        __bf16* sVd = decltype(buf)::value ? sV1 : sV0;
+        const int k0 = tile_k0(pi);
+        const uint32_t tile_bytes = (uint32_t)min(L - k0, BN) * row_bytes;
         // V: 64 rows x CH chunks
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)k0 * kv_row, tile_bytes);
 #pragma unroll
@@ -457,6 +462,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         // compiler sinks it below the branch, next to PV(h0)
         asm volatile("" ::"v"(P0[0][0]), "v"(P0[0][1]), "v"(P0[1][0]), "v"(P0[1][1]));
         if (edge) edge_fix(s1, 1, rlo, rhi);
+        stage_load_v(pn, Other{});
         pv(V, 0, P0);
         probs(s1, P1);
         pv(V, 1, P1);
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
         if (pi == nR && nR > 0) load_q(false);   // the local phase starts: stored Q
         const int pn = pi + 1 < NP ? pi + 1 : pi;   // the last tile refills the idle buffer
-        stage_load_kv(pn, Other{});
+        stage_load_k(pn);
         const bool rem = pi < nR;
         const int k0 = tile_k0(pi);
         const int k1 = k0 + BN - 1;
@@ -505,7 +511,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         __syncthreads();
     };
 
-    stage_load_kv(0, Buf0{});
+    stage_load_k(0);
+    stage_load_v(0, Buf0{});
     stage_load_t(0);
     wait_vmem();
     stage_store(Buf0{});
