@@ -124,7 +124,7 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
     const int64_t n_qtiles = (L + BQ - 1) / BQ;
     if (n_qtiles * Hkv * B > 0x7fffffffLL) return fail(JL_EINVAL, "grid too large");
 
-    jl::PrefillParams p;
+    jl::PrefillParams p{};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -190,7 +190,7 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
     if (Hkv % 8 != 0 && 8 % Hkv != 0)
         return fail(JL_EUNSUPPORTED, "decode needs Hkv dividing 8 or a multiple of 8 (got %lld)", (long long)Hkv);
 
-    jl::DecodeParams p;
+    jl::DecodeParams p{};
     p.q = q;
     p.k = k_cache;
     p.v = v_cache;

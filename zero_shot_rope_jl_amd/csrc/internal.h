@@ -25,6 +25,9 @@ struct PrefillParams {
     float sm_scale_log2;  // sm_scale * log2(e)
     double rope_base;
     int head_dim;
+    // 0: compute every row.  1: recompute only the workgroups whose rows carry
+    // the non-finite-row mark left by the bf16 kernel (NaN in element 0).
+    int fixup;
 };
 
 struct DecodeParams {

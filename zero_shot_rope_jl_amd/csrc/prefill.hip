@@ -261,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     __shared__ __attribute__((aligned(16))) T sK[2][Lay::K_ELEMS];
     __shared__ __attribute__((aligned(16))) T sV[2][Lay::V_ELEMS];
     __shared__ int s_bad;
+    __shared__ int s_marked;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -305,6 +306,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const T* __restrict__ kbase = kg + (int64_t)b * L * kv_row + (int64_t)g * D;
     const T* __restrict__ vbase = vg + (int64_t)b * L * kv_row + (int64_t)g * D;
 
+    if (p.fixup) {
+        // Fixup pass: only a workgroup with a marked row (NaN in element 0)
+        // recomputes; the row sets of both prefill kernels coincide.
+        if (tid == 0) s_marked = 0;
+        __syncthreads();
+        if (tid < 256) {
+            const int hq = g * R + tid / p.BQ;
+            const int pos = q0 + tid % p.BQ;
+            if (pos < L) {
+                const int64_t o = (((int64_t)b * L + pos) * Hq + hq) * D;
+                const float e0 = OUT_BF16 ? (float)static_cast<const __bf16*>(p.out)[o]
+                                          : static_cast<const float*>(p.out)[o];
+                if (e0 != e0) s_marked = 1;
+            }
+        }
+        __syncthreads();
+        if (!s_marked) return;
+    }
     if (tid == 0) {
         const TableHeader* th = p.table;
         s_bad = !(th->magic == kTableMagic && th->head_dim == D && th->rope_base == p.rope_base &&
@@ -463,8 +482,18 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, int in_dtype, int out_dtype, hipStream_t stream) {
-    // bf16 inputs take the 64-rows-per-wave kernel; fp32 inputs this one
-    if (in_dtype == 1) return launch_prefill_bf16(p, out_dtype, stream);
+    if (in_dtype == 1) {
+        // bf16 inputs: the 64-rows-per-wave kernel, then the fixup pass that
+        // recomputes (with the online softmax here) any workgroup whose rows
+        // it marked as non-finite; the pass exits at once when none is marked.
+        const hipError_t e = launch_prefill_bf16(p, out_dtype, stream);
+        if (e != hipSuccess) return e;
+        PrefillParams pf = p;
+        pf.fixup = 1;
+        const bool ob = out_dtype == 1;
+        if (p.head_dim == 128) return ob ? launch_one<128, true, true>(pf, stream) : launch_one<128, true, false>(pf, stream);
+        return ob ? launch_one<64, true, true>(pf, stream) : launch_one<64, true, false>(pf, stream);
+    }
     (void)out_dtype;
     if (p.head_dim == 128) return launch_one<128, false, false>(p, stream);
     return launch_one<64, false, false>(p, stream);

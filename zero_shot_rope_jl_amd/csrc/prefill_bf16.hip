@@ -527,11 +527,21 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     if (pi < NP) tile(pi, Buf0{});
 
     // ---- epilogue ---------------------------------------------------------------
+    // A row whose probabilities overflowed (a later score above its fixed
+    // reference by more than the fp32 exponent range) comes out non-finite;
+    // it is marked with NaN in element 0 for the fixup pass, which recomputes
+    // its workgroup with a running max.
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const float l_tot = l_run[j] + __shfl_xor(l_run[j], 32);
-        if (!qok[j]) continue;
         const float inv = 1.f / l_tot;
+        bool finite = l_tot > 0.f && l_tot < INFINITY;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) finite = finite && fabsf(acc[j][db][i] * inv) < INFINITY;
+        const bool row_ok = finite && __shfl_xor((int)finite, 32);
+        if (!qok[j]) continue;
         const int64_t o = (((int64_t)b * L + my_q[j]) * Hq + head[j]) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -542,11 +552,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
                     bf16x4 w;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[j][db][4 * a4 + e] * inv);
+                    if (d0 == 0 && !row_ok) w[0] = (__bf16)NAN;
                     *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.out) + o + d0) = w;
                 } else {
                     f32x4 w;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = acc[j][db][4 * a4 + e] * inv;
+                    if (d0 == 0 && !row_ok) w[0] = NAN;
                     *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o + d0) = w;
                 }
             }
