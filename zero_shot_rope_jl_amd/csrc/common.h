@@ -49,4 +49,25 @@ __device__ inline float wave_max_xor32(float x) {
     return fmaxf(x, __shfl_xor(x, 32));
 }
 
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte rows addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
+__device__ inline bf16x4 lds_read_tr16(const __bf16* p) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer resource, 32-bit elements
+
+// Buffer resource over [base, base + bytes): loads beyond `bytes` return 0.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+// 16-byte buffer -> LDS copy per lane; lane l writes bytes [16l, 16l + 16)
+// after the wave-uniform LDS base.
+__device__ inline void buffer_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_base), 16, voff, soff,
+                                             0, 0);
+}
+
 }  // namespace jl

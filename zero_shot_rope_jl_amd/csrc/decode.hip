@@ -128,6 +128,17 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const int64_t row = p.Hkv * D;
     const int64_t cache_b = (int64_t)b * p.Lmax * row + (int64_t)g * D;
 
+    // the first step's K and V go out before anything else (the set-up below
+    // waits on the table and q); they stay within the cache whatever the
+    // table check decides
+    const int wstart = (split * NW + sub) * p.wave_chunk;
+    const int wend0 = min(L, wstart + p.wave_chunk);
+    DecodeTile<D> cur;
+    if (wstart < wend0) {
+        load_k<D>(cur, kc, cache_b, row, wstart, wend0, colh, gq);
+        load_v<D>(cur, vc, cache_b, row, wstart, wend0, lane);
+    }
+
     if (tid == 0) {
         const TableHeader* th = p.table;
         s_bad = !(th->magic == kTableMagic && th->head_dim == D && th->rope_base == p.rope_base &&
@@ -172,8 +183,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int wstart = (split * NW + sub) * p.wave_chunk;
-    const int wend = bad ? wstart : min(L, wstart + p.wave_chunk);
+    const int wend = bad ? wstart : wend0;
     __bf16* myV = sVt[wave];
     float2* myBase = sBase[wave];
 
@@ -183,13 +193,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     float2 base = make_float2(1.f, 0.f);
     if (lane < HALF && wstart < wend && G > 1) base = TF[(int64_t)(wstart - wstart / G) * HALF + lane];
 
-    // One register tile: each half is reloaded for the next step as soon as
-    // this step has consumed it, so loads stay in flight during the compute.
-    DecodeTile<D> cur;
-    if (wstart < wend) {
-        load_k<D>(cur, kc, cache_b, row, wstart, wend, colh, gq);
-        load_v<D>(cur, vc, cache_b, row, wstart, wend, lane);
-    }
+    // One register tile (loaded above): each half is reloaded for the next
+    // step as soon as this step has consumed it, so loads stay in flight
+    // during the compute.
     for (int kbase = wstart; kbase < wend; kbase += kWaveKeys) {
         const int knext = kbase + kWaveKeys;
         // ---- V rows -> V^T in this wave's LDS slice --------------------------
@@ -345,9 +351,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
 }
 
 // Log-sum-exp merge of one head's split partials (up to 256 splits):
-// workgroup = (head, batch, 32-dim block) of 1024 threads.  Split weights go
-// to LDS once; each thread then sums one dimension over every 32nd split,
-// all of its (at most 8) loads issued together.
+// workgroup = (head, batch, 32-dim block) of 1024 threads.  Each thread loads
+// one dimension of every 32nd split together with one split's (max, sum),
+// all in one round trip; split weights go to LDS once.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeParams p) {
     __shared__ float sW[kDecodeMaxSplits];
@@ -360,6 +366,16 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeParams p) {
     const int wave = tid >> 6;
     const int ns = p.n_split;
     const float* base = p.ws + ((int64_t)b * p.Hq + head) * ns * (D + 2);
+    const int d = blockIdx.z * 32 + (tid & 31);
+    const int part = tid >> 5;   // 32 interleaved split groups
+    // every load of the kernel goes out at once: this thread's partial sums
+    // and, for thread t < ns, split t's max and row sum
+    float pa[kDecodeMaxSplits / 32];
+#pragma unroll
+    for (int u = 0; u < kDecodeMaxSplits / 32; ++u) {
+        const int s = part + 32 * u;
+        pa[u] = s < ns ? base[s * (D + 2) + d] : 0.f;
+    }
     const float m = tid < ns ? base[tid * (D + 2) + D] : -INFINITY;
     const float lsplit = tid < ns ? base[tid * (D + 2) + D + 1] : 0.f;
     float M = m;
@@ -385,13 +401,11 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeParams p) {
         sM = M;
         sL = t;
     }
-    const int d = blockIdx.z * 32 + (tid & 31);
-    const int part = tid >> 5;   // 32 interleaved split groups
     float a = 0.f;
 #pragma unroll
     for (int u = 0; u < kDecodeMaxSplits / 32; ++u) {
         const int s = part + 32 * u;
-        if (s < ns) a += sW[s] * base[s * (D + 2) + d];
+        if (s < ns) a += sW[s] * pa[u];
     }
     __syncthreads();
     sRed[tid] = a;

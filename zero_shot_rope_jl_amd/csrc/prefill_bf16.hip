@@ -52,26 +52,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int BN = 64;                        // keys per tile
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer resource, 32-bit elements
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ inline bf16x4 lds_read_tr16(const __bf16* p) {
-    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-}
-
-// Buffer resource over [base, base + bytes): loads beyond `bytes` return 0.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
-}
-
-// 16-byte buffer -> LDS copy per lane; lane l writes bytes [16l, 16l + 16)
-// after the wave-uniform LDS base.
-__device__ inline void buffer_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_base), 16, voff, soff,
-                                             0, 0);
-}
 
 __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
