@@ -49,7 +49,11 @@ namespace jl {
 
 namespace {
 
-constexpr int kWaves = 4;
+// 32-row query blocks per wave: 1 gives 8 waves per workgroup, two per SIMD,
+// whose MFMA and VALU work the hardware interleaves; 2 gives 4 waves, one per
+// SIMD, each K or V^T fragment read from LDS feeding two MFMAs.
+constexpr int NJ = 1;
+constexpr int kWaves = 8 / NJ;
 constexpr int kThreads = kWaves * 64;
 constexpr int BN = 64;                        // keys per tile
 
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // Naming an accumulation register keeps the compiler from assuming the
     // kernel needs none; it then gives the MFMAs their accumulation-register
     // form and the output accumulators stay out of the VGPR budget.
-    asm volatile("" ::: "a255");
+    asm volatile("" ::: "a0");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -130,12 +134,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const int q_hi = min(q0 + BQ, L) - 1;
     const float scale2 = p.sm_scale_log2;
 
-    // the wave's two 32-row query blocks
-    int head[2], pj0[2], pjhi[2], my_q[2];
-    bool qok[2];
+    // the wave's 32-row query blocks
+    int head[NJ], pj0[NJ], pjhi[NJ], my_q[NJ];
+    bool qok[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int rho = 64 * wave + 32 * j;
+    for (int j = 0; j < NJ; ++j) {
+        const int rho = 32 * NJ * wave + 32 * j;
         head[j] = g * R + rho / BQ;
         pj0[j] = q0 + rho % BQ;
         pjhi[j] = min(pj0[j] + 31, L - 1);
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     if (s_bad) {
         // The table does not belong to this (D, rope_base, L): poison the output.
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             if (!qok[j]) continue;
             const int64_t o = (((int64_t)b * L + my_q[j]) * Hq + head[j]) * D;
             for (int d = hh; d < D; d += 2) {
@@ -185,10 +189,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // B operand, fragment c = dims 16c + 8hh + [0, 8), multiplied by
     // sm_scale * log2(e) before the bf16 rounding, so the MFMA yields scores in
     // log2 units.  Rows past L read row L-1 (finite values, never stored).
-    bf16x8 qv[2][NC];
+    bf16x8 qv[NJ][NC];
     auto load_q = [&](bool remote_view) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const int qpos = min(my_q[j], L - 1);
             const __bf16* qrow = qg + (((int64_t)b * L + qpos) * Hq + head[j]) * D;
             bf16x8 raw[NC];
@@ -263,14 +267,25 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         const uint32_t tile_bytes = (uint32_t)min(L - k0, BN) * row_bytes;
         // K into registers
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)k0 * kv_row, tile_bytes);
+        if constexpr (PPT >= 8) {
 #pragma unroll
-        for (int c = 0; c < PPT / 8; ++c) {
-            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 16u * c, 0, 0);
-            const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 2u * HALF + 16u * c, 0, 0);
+            for (int c = 0; c < PPT / 8; ++c) {
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 16u * c, 0, 0);
+                const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 2u * HALF + 16u * c, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                stx[8 * c + e] = __builtin_bit_cast(bf16x8, x)[e];
-                sty[8 * c + e] = __builtin_bit_cast(bf16x8, y)[e];
+                for (int e = 0; e < 8; ++e) {
+                    stx[8 * c + e] = __builtin_bit_cast(bf16x8, x)[e];
+                    sty[8 * c + e] = __builtin_bit_cast(bf16x8, y)[e];
+                }
+            }
+        } else {
+            static_assert(PPT == 4, "K staging covers 4, 8 or 16 pairs per thread");
+            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rk, k_voff, 0, 0);
+            const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(rk, k_voff + 2u * HALF, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                stx[e] = __builtin_bit_cast(bf16x4, x)[e];
+                sty[e] = __builtin_bit_cast(bf16x4, y)[e];
             }
         }
     };
@@ -324,14 +339,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // m_ref: the row's reference max (log2 units, a bf16 value), -inf until the
     // row meets its first key; qx holds -m_ref as the extra B chunk of the
     // score MFMA; l_run: row sum of probabilities.
-    f32x16 acc[2][NDB];
+    f32x16 acc[NJ][NDB];
+    float m_ref[NJ], l_run[NJ];
+    bf16x8 qx[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[j][db] = f32x16{};
-    float m_ref[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
-    bf16x8 qx[2] = {bf16x8{}, bf16x8{}};
+        m_ref[j] = -INFINITY;
+        l_run[j] = 0.f;
+        qx[j] = bf16x8{};
+    }
     bf16x8 kone = bf16x8{};
     if (hh == 0) kone[0] = (__bf16)1.0f;
 
@@ -346,23 +364,24 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const int tr_dim = 16 * (Gq & 1) + 4 * (cq & 3);
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // S^T - m_ref for one 32-key half, both query blocks; each K fragment
-    // feeds both; the last step adds the rank-1 term ones x (-m_ref).
-    auto qk = [&](const __bf16* K, int kb, f32x16 (&s)[2]) {
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+    // S^T - m_ref for one 32-key half, every query block of the wave (each K
+    // fragment feeds all of them); the last step adds the rank-1 term
+    // ones x (-m_ref).
+    auto qk = [&](const __bf16* K, int kb, f32x16 (&s)[NJ]) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) s[j] = f32x16{};
         const __bf16* kp = K + (32 * kb + krow_l) * KSTR + 8 * hh;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const bf16x8 A = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[0][c], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[1][c], s[1], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[j][c], s[j], 0, 0, 0);
         }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, qx[0], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, qx[1], s[1], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, qx[j], s[j], 0, 0, 0);
     };
-    // O^T += V^T P^T for one 32-key half; each V^T fragment feeds both blocks.
-    auto pv = [&](const __bf16* V, int kb, const bf16x8 (&P)[2][2]) {
+    // O^T += V^T P^T for one 32-key half; each V^T fragment feeds every block.
+    auto pv = [&](const __bf16* V, int kb, const bf16x8 (&P)[NJ][2]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int r0 = 32 * kb + 16 * h + tr_row;
@@ -374,16 +393,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
                 const bf16x4 lo = lds_read_tr16(V + r0 * D + 8 * vswz<D>(r0, lc) + wi);
                 const bf16x4 hi = lds_read_tr16(V + (r0 + 4) * D + 8 * vswz<D>(r0 + 4, lc) + wi);
                 const bf16x8 A = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[0][h], acc[0][db], 0, 0, 0);
-                acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[1][h], acc[1][db], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[j][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[j][h], acc[j][db], 0, 0, 0);
             }
         }
     };
     // P = exp2(S - m_ref) as rounded for the MFMA, and the row sums of those
     // rounded values.
-    auto probs = [&](const f32x16 (&s)[2], bf16x8 (&P)[2][2]) {
+    auto probs = [&](const f32x16 (&s)[NJ], bf16x8 (&P)[NJ][2]) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -403,9 +423,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // Window-edge, causal-diagonal and ragged tiles mask scores per element;
     // a row meeting its first keys takes this half's max (rounded to bf16) as
     // its reference, which is subtracted here once and by the MFMA after.
-    auto edge_fix = [&](f32x16 (&s)[2], int kb, const int (&rlo)[2], const int (&rhi)[2]) {
+    auto edge_fix = [&](f32x16 (&s)[NJ], int kb, const int (&rlo)[NJ], const int (&rhi)[NJ]) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int c0 = 32 * kb + 16 * (i >> 3) + (i & 7);
@@ -429,12 +449,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // interleave: S(h0) | S(h1) with softmax(h0) | PV(h0) with softmax(h1) |
     // PV(h1) with the rotation of the next tile's K.  The rare edge work sits
     // in uniform branches between regions and never touches the accumulators.
-    auto tile_body = [&](auto buf, int pn, bool edge, const int (&rlo)[2], const int (&rhi)[2]) __attribute__((always_inline)) {
+    auto tile_body = [&](auto buf, int pn, bool edge, const int (&rlo)[NJ], const int (&rhi)[NJ]) __attribute__((always_inline)) {
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
         const __bf16* K = decltype(buf)::value ? sK1 : sK0;
         const __bf16* V = decltype(buf)::value ? sV1 : sV0;
-        f32x16 s0[2], s1[2];
-        bf16x8 P0[2][2], P1[2][2];
+        f32x16 s0[NJ], s1[NJ];
+        bf16x8 P0[NJ][2], P1[NJ][2];
         qk(K, 0, s0);
         if (edge) edge_fix(s0, 0, rlo, rhi);
         qk(K, 1, s1);
@@ -442,7 +462,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         probs(s0, P0);
         // keep softmax(h0) in the region of S(h1): without a use here the
         // compiler sinks it below the branch, next to PV(h0)
-        asm volatile("" ::"v"(P0[0][0]), "v"(P0[0][1]), "v"(P0[1][0]), "v"(P0[1][1]));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) asm volatile("" ::"v"(P0[j][0]), "v"(P0[j][1]));
         if (edge) edge_fix(s1, 1, rlo, rhi);
         stage_load_v(pn, Other{});
         pv(V, 0, P0);
@@ -464,10 +485,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         const int k1 = k0 + BN - 1;
         // per query block: masked?, kept key window [rlo, rhi] relative to
         // the lane's first key k0 + 8hh
-        bool msk[2];
-        int rlo[2], rhi[2];
+        bool msk[NJ];
+        int rlo[NJ], rhi[NJ];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             bool act;
             if (rem) {
                 act = pjhi[j] - k0 > w0;
@@ -487,7 +508,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
                 rhi[j] = INT_MAX / 2;
             }
         }
-        const bool edge = msk[0] || msk[1] || __any((m_ref[0] == -INFINITY) | (m_ref[1] == -INFINITY));
+        bool any_msk = false, any_unset = false;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            any_msk = any_msk || msk[j];
+            any_unset = any_unset || m_ref[j] == -INFINITY;
+        }
+        const bool edge = any_msk || __any(any_unset);
         tile_body(buf, pn, edge, rlo, rhi);
         wait_vmem();   // the next tile's V has landed in LDS
         __syncthreads();
@@ -514,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // it is marked with NaN in element 0 for the fixup pass, which recomputes
     // its workgroup with a running max.
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const float l_tot = l_run[j] + __shfl_xor(l_run[j], 32);
         const float inv = 1.f / l_tot;
         bool finite = l_tot > 0.f && l_tot < INFINITY;
