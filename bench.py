@@ -88,10 +88,11 @@ def bench_prefill(torch, jl, si, args, w, x):
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device="cuda")
     table = jl.alloc_table(w.L, w.D, w.rope_base)
+    ws = jl.alloc_prefill_workspace(k, w.w_pretrained)   # keys in their remote view, rewritten every step
     torch.cuda.synchronize()
 
     def step():
-        jl.jl_bifocal_prefill(q, k, v, out, lse, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table)
+        jl.jl_bifocal_prefill(q, k, v, out, lse, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table, ws)
 
     for _ in range(args.warmup):
         step()

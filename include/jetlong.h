@@ -9,8 +9,9 @@
  *     remote (q - k >  w0):  RoPE(x_q, f(q)) . RoPE(x_k, f(k))
  * with f(x) = floor(x / G) (§3.1, Eq. 3) and G = max(1, ceil(L / w_pretrained))
  * (§3.1, Eq. 2).  The cache holds RoPE(x_k, k) and is never rewritten (§3.2,
- * Eq. 4); the remote view is formed on the fly by rotating stored vectors by
- * f(p) - p (§3.2, Eq. 5).  The two views are merged exactly inside one online
+ * Eq. 4); the remote view is formed inside each call by rotating stored
+ * vectors by f(p) - p (§3.2, Eq. 5): queries and decode keys as they are
+ * read, prefill keys once per call into a caller-provided workspace.  The two views are merged exactly inside one online
  * softmax, which is the inclusion-exclusion merge of §3.3 (Eq. 6) with the
  * overlap term cancelled by masking instead of subtraction.
  *
@@ -92,6 +93,19 @@ JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double
                 size_t* table_bytes_needed, void* hip_stream);
 
 /*
+ * jl_bifocal_prefill_workspace -- device bytes of scratch jl_bifocal_prefill
+ * needs: for bf16 inputs with G = max(1, ceil(L / w_pretrained)) > 1 the
+ * keys in their remote view (§3.2 Eq. 5), B * L * Hkv * D bf16, laid out
+ * like k; 0 otherwise (fp32 inputs, or every pair local).  Pure host call.
+ *
+ * Errors: bytes == NULL, B, L, Hkv < 1 or L > 2^30, w_pretrained < 1 ->
+ * JL_EINVAL; D not in {64, 128} or in_dtype not JL_F32 / JL_BF16 ->
+ * JL_EUNSUPPORTED.
+ */
+JL_API int jl_bifocal_prefill_workspace(int in_dtype, int64_t B, int64_t L, int64_t Hkv, int64_t D,
+                                        int64_t w_pretrained, size_t* bytes);
+
+/*
  * jl_bifocal_prefill -- causal bifocal attention over a whole sequence
  * (§3 Eq. 1 with §3.1 Eqs. 2-3, §3.2 Eq. 5, §3.3 Eq. 6).
  *
@@ -106,17 +120,23 @@ JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double
  * {1, 2, 4, 8}.  `table` must have been filled by jl_schedule for this D and
  * rope_base with coverage >= L; if its header does not match (D, rope_base,
  * coverage) the kernels write NaN to `out` (the host cannot read it).
+ * `workspace` holds workspace_bytes >= jl_bifocal_prefill_workspace(...)
+ * bytes of device scratch, owned by the caller; it may be NULL when that
+ * size is 0.  Its contents on entry do not matter and are overwritten, so
+ * two calls in flight at once need two workspaces.
  *
  * Errors: JL_EINVAL for B, L, Hq, Hkv < 1, Hq % Hkv != 0, w0 < 0,
  * w_pretrained < 1, sm_scale not finite or <= 0, NULL or misaligned pointers;
  * JL_EUNSUPPORTED for other D, dtype pairs or GQA ratios; JL_ESPACE if
- * table_bytes is below jl_schedule's requirement for L.
+ * table_bytes is below jl_schedule's requirement for L or workspace_bytes
+ * below jl_bifocal_prefill_workspace's.
  */
 JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
                        int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Hq,
                        int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained,
                        double rope_base, float sm_scale, const void* table,
-                       size_t table_bytes, void* hip_stream);
+                       size_t table_bytes, void* workspace, size_t workspace_bytes,
+                       void* hip_stream);
 
 /*
  * jl_bifocal_decode_workspace -- bytes of fp32 scratch that jl_bifocal_decode

@@ -23,11 +23,12 @@ def header_symbols():
 
 def test_exports_every_declared_symbol():
     syms = header_symbols()
-    assert syms == sorted(["jl_last_error", "jl_version", "jl_schedule", "jl_bifocal_prefill",
-                           "jl_bifocal_decode_workspace", "jl_bifocal_decode", "jl_table_fill_host"])
+    assert syms == sorted(["jl_last_error", "jl_version", "jl_schedule", "jl_bifocal_prefill_workspace",
+                           "jl_bifocal_prefill", "jl_bifocal_decode_workspace", "jl_bifocal_decode",
+                           "jl_table_fill_host"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 1
+    assert jl.jl_version() == 2
 
 
 def test_schedule_golden_and_table_size():
@@ -60,11 +61,11 @@ def test_schedule_validation(kw, code):
 
 def _prefill(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, L=256, Hq=4,
-             Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE, tb=1 << 30)
+             Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE, tb=1 << 30, ws=FAKE, wsb=1 << 30)
     a.update(over)
     return jl.lib.jl_bifocal_prefill(a["q"], a["k"], a["v"], a["out"], a["lse"], a["i"], a["o"], a["B"],
                                      a["L"], a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"], a["base"],
-                                     a["sc"], a["table"], a["tb"], None)
+                                     a["sc"], a["table"], a["tb"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -75,10 +76,30 @@ def _prefill(**over):
     (dict(L=(1 << 30) + 1), jl.JL_EINVAL), (dict(D=96), jl.JL_EUNSUPPORTED),
     (dict(i=jl.JL_F32, o=jl.JL_BF16), jl.JL_EUNSUPPORTED), (dict(Hq=32, Hkv=2), jl.JL_EUNSUPPORTED),
     (dict(Hq=6, Hkv=2), jl.JL_EUNSUPPORTED), (dict(tb=100), jl.JL_ESPACE), (dict(base=0.5), jl.JL_EINVAL),
+    (dict(ws=None), jl.JL_ESPACE), (dict(wsb=256 * 2 * 128 * 2 - 1), jl.JL_ESPACE), (dict(ws=FAKE + 8), jl.JL_EINVAL),
 ])
 def test_prefill_validation(over, code):
     assert _prefill(**over) == code
     assert jl.jl_last_error()
+
+
+def test_prefill_workspace_size():
+    # bf16 with G = ceil(L / w_pretrained) > 1: the keys in their remote view, B*L*Hkv*D bf16
+    assert jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 1, 131072, 8, 128, 32768) == 131072 * 8 * 128 * 2
+    assert jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 2, 300, 2, 64, 256) == 2 * 300 * 2 * 64 * 2
+    # G == 1 (every pair local) or fp32 inputs: none
+    assert jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 1, 4096, 8, 128, 4096) == 0
+    assert jl.jl_bifocal_prefill_workspace(jl.JL_F32, 1, 131072, 8, 128, 32768) == 0
+    with pytest.raises(jl.JetLongError):
+        jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 1, 10, 1, 96, 4)
+    with pytest.raises(jl.JetLongError):
+        jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 0, 10, 1, 64, 4)
+
+
+def test_prefill_without_workspace_when_none_is_needed_passes_validation_order():
+    # G == 1: a NULL workspace is accepted; the call still fails later, on the
+    # unsupported head_dim, before any HIP call
+    assert _prefill(L=64, wp=64, ws=None, wsb=0, D=96) == jl.JL_EUNSUPPORTED
 
 
 def _decode(**over):

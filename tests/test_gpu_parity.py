@@ -123,6 +123,38 @@ def test_device_table_equals_host_table():
         assert np.all(np.abs(a - b) <= np.spacing(np.abs(b)).astype(np.float64) + 1e-10)
 
 
+def test_prefill_workspace_holds_remote_keys_and_inputs_are_untouched():
+    """§3.2 Eq. 5 applied to the stored keys: the workspace receives every key
+    in its remote view (equal to the oracle's rotation of the stored bf16 keys
+    up to the bf16 rounding of the result); q, k and v are never written; stale
+    workspace contents do not change the output."""
+    require_gpu()
+    w = small_workload(1000, 8, 2, 128, 300, 64, seed=11)   # G = 4
+    x = si.make_prefill_inputs(w, want_f64=False)
+    q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    before = [t.clone() for t in (q, k, v)]
+    table = jl.alloc_table(w.L, w.D, w.rope_base)
+    ws = jl.alloc_prefill_workspace(k, w.w_pretrained)
+    assert ws is not None and ws.numel() == k.numel() * 2
+    out1 = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    jl.jl_bifocal_prefill(q, k, v, out1, None, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table, ws)
+    torch.cuda.synchronize()
+    for a, b in zip(before, (q, k, v)):
+        assert torch.equal(a, b)
+    kb = k.float().cpu().numpy().astype(np.float64)
+    ref = oracle.remote_view(kb, np.arange(w.L), oracle.group_size(w.L, w.w_pretrained), w.rope_base)
+    got = ws.view(torch.bfloat16).view(k.shape).float().cpu().numpy().astype(np.float64)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(kb).max()
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+    ws.fill_(0xFF)   # every bf16 of the workspace becomes a NaN
+    out2 = torch.empty_like(out1)
+    jl.jl_bifocal_prefill(q, k, v, out2, None, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    # every pair local (G == 1): no workspace
+    assert jl.alloc_prefill_workspace(k, w.L) is None
+
+
 def test_mismatched_table_poisons_output():
     require_gpu()
     w = small_workload(256, 4, 2, 128, 64, 16, seed=5)

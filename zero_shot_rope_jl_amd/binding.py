@@ -41,8 +41,10 @@ def _load():
     L.jl_table_fill_host.restype = ctypes.c_int
     L.jl_table_fill_host.argtypes = [i64, i64, ctypes.c_double, vp, sz]
     L.jl_bifocal_prefill.restype = ctypes.c_int
+    L.jl_bifocal_prefill_workspace.restype = ctypes.c_int
+    L.jl_bifocal_prefill_workspace.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.POINTER(sz)]
     L.jl_bifocal_prefill.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
-                                     i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp]
+                                     i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
     L.jl_bifocal_decode_workspace.restype = ctypes.c_int
     L.jl_bifocal_decode_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(sz)]
     L.jl_bifocal_decode.restype = ctypes.c_int
@@ -143,10 +145,29 @@ def alloc_table(L: int, head_dim: int, rope_base: float, device="cuda", stream=N
     return t
 
 
+def jl_bifocal_prefill_workspace(in_dtype: int, B: int, L: int, Hkv: int, D: int, w_pretrained: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D, w_pretrained, ctypes.byref(n)))
+    return n.value
+
+
+def alloc_prefill_workspace(k, w_pretrained: int, device="cuda"):
+    """Scratch for jl_bifocal_prefill over keys shaped like `k` [B, L, Hkv, D] (None if none is needed)."""
+    torch = _torch()
+    B, L, Hkv, D = k.shape
+    n = jl_bifocal_prefill_workspace(_dtype_code(k), B, L, Hkv, D, w_pretrained)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def jl_bifocal_prefill(q, k, v, out, lse, w0: int, w_pretrained: int, rope_base: float,
-                       sm_scale: float, table, stream=None):
-    """q [B,L,Hq,D], k/v [B,L,Hkv,D], out [B,L,Hq,D], lse [B,Hq,L] fp32 or None."""
-    _need_device(q, k, v, out, lse, table)
+                       sm_scale: float, table, workspace=None, stream=None):
+    """q [B,L,Hq,D], k/v [B,L,Hkv,D], out [B,L,Hq,D], lse [B,Hq,L] fp32 or None.
+
+    `workspace`: device scratch of jl_bifocal_prefill_workspace bytes (see
+    alloc_prefill_workspace); when None and some is needed, one is allocated
+    through torch for this call.
+    """
+    _need_device(q, k, v, out, lse, table, workspace)
     B, L, Hq, D = q.shape
     Hkv = k.shape[2]
     if tuple(k.shape) != (B, L, Hkv, D) or tuple(v.shape) != (B, L, Hkv, D):
@@ -157,10 +178,13 @@ def jl_bifocal_prefill(q, k, v, out, lse, w0: int, w_pretrained: int, rope_base:
         raise ValueError("lse must be float32 [B, Hq, L]")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
+    if workspace is None:
+        workspace = alloc_prefill_workspace(k, w_pretrained, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.jl_bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
                                   _dtype_code(out), B, L, Hq, Hkv, D, w0, w_pretrained, rope_base,
                                   sm_scale, _ptr(table), table.numel() * table.element_size(),
-                                  _stream(stream)))
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
 
 

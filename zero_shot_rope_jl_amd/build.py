@@ -5,7 +5,8 @@
 Every source under csrc/ is compiled to an object in _build/ (in parallel)
 and linked into zero_shot_rope_jl_amd/libjetlong.so.  The compile line turns
 off packed-FP32 code generation for the device and hides every symbol except
-the C ABI declared in include/jetlong.h.
+the C ABI declared in include/jetlong.h.  Sources listed in PER_FILE_FLAGS get
+extra device-compiler options.
 """
 from __future__ import annotations
 
@@ -21,6 +22,13 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libjetlong.so")
 ARCH = os.environ.get("JL_OFFLOAD_ARCH", "gfx950")
+# The bf16 prefill keeps its score tiles, output accumulators and operands
+# together within the 256 registers a wave has at two waves per SIMD; in the
+# MFMAs' VGPR form (result and accumulator in ordinary VGPRs) the scores feed
+# the exponentials directly, where the accumulation-register form would copy
+# every score tile out of AGPRs and shuffle the accumulators between loop
+# iterations.
+PER_FILE_FLAGS = {"prefill_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -64,7 +72,8 @@ def build(verbose: bool = False) -> str:
         for s in srcs:
             obj = os.path.join(BUILD, s[:-4] + ".o")
             objs.append(obj)
-            jobs.append(ex.submit(_run, [cc, *flags, "-c", os.path.join(CSRC, s), "-o", obj], verbose))
+            extra = PER_FILE_FLAGS.get(s, [])
+            jobs.append(ex.submit(_run, [cc, *flags, *extra, "-c", os.path.join(CSRC, s), "-o", obj], verbose))
         for j in jobs:
             j.result()
     tmp = LIB + ".tmp"

@@ -67,7 +67,7 @@ extern "C" {
 
 JL_API const char* jl_last_error(void) { return g_err.c_str(); }
 
-JL_API int jl_version(void) { return 1; }
+JL_API int jl_version(void) { return 2; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -102,14 +102,28 @@ JL_API int jl_table_fill_host(int64_t L, int64_t head_dim, double rope_base, voi
     return JL_OK;
 }
 
+JL_API int jl_bifocal_prefill_workspace(int in_dtype, int64_t B, int64_t L, int64_t Hkv, int64_t D,
+                                        int64_t w_pretrained, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(JL_EINVAL, "bytes is NULL");
+    if (B < 1 || Hkv < 1 || L < 1 || L > kMaxLen)
+        return fail(JL_EINVAL, "B, Hkv, L must be >= 1 and L <= 2^30");
+    if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1 (got %lld)", (long long)w_pretrained);
+    if (D != 64 && D != 128) return fail(JL_EUNSUPPORTED, "head_dim %lld not supported", (long long)D);
+    if (in_dtype != JL_F32 && in_dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "unknown in_dtype %d", in_dtype);
+    const bool rotated_keys = in_dtype == JL_BF16 && group_size(L, w_pretrained) > 1;
+    *bytes = rotated_keys ? (size_t)B * (size_t)L * (size_t)Hkv * (size_t)D * 2u : 0u;
+    return JL_OK;
+}
+
 JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int in_dtype,
                               int out_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
                               int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
-                              size_t table_bytes, void* hip_stream) {
+                              size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
     g_err.clear();
     if (!q || !k || !v || !out || !table) return fail(JL_EINVAL, "q, k, v, out and table must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(table) ||
-        !aligned16(lse))
+        !aligned16(lse) || !aligned16(workspace))
         return fail(JL_EINVAL, "device pointers must be 16-byte aligned");
     if (int rc = check_attention_common(B, L, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, in_dtype,
                                         out_dtype))
@@ -120,6 +134,11 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
     const size_t need = jl::table_bytes_for(L, (int)D);
     if (table_bytes < need)
         return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
+    size_t ws_need = 0;
+    jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D, w_pretrained, &ws_need);
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
+        return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                    ws_need);
     const int BQ = 256 / (int)R;
     const int64_t n_qtiles = (L + BQ - 1) / BQ;
     if (n_qtiles * Hkv * B > 0x7fffffffLL) return fail(JL_EINVAL, "grid too large");
@@ -144,6 +163,7 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
     p.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
     p.rope_base = rope_base;
     p.head_dim = (int)D;
+    p.krot = workspace;
     (void)hipGetLastError();
     hipError_t e = jl::launch_prefill(p, in_dtype, out_dtype, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(JL_EHIP, "prefill launch failed: %s", hipGetErrorString(e));

@@ -28,6 +28,9 @@ struct PrefillParams {
     // 0: compute every row.  1: recompute only the workgroups whose rows carry
     // the non-finite-row mark left by the bf16 kernel (NaN in element 0).
     int fixup;
+    // bf16 kernel only: B*L*Hkv*D bf16 workspace that receives the keys in
+    // their corrected view when G > 1 (laid out like k)
+    void* krot;
 };
 
 struct DecodeParams {

@@ -7,25 +7,28 @@
 // which realises the inclusion-exclusion merge exactly (the overlap term is
 // removed by masking, not subtracted).
 //
-// Work decomposition (one workgroup = 4 waves = 256 query rows of one KV head)
+// Work decomposition (one workgroup = 8 waves = 256 query rows of one KV head)
 //   Rows are ordered head-major over the R = Hq/Hkv query heads of the KV
-//   head and BQ = 256/R positions; wave w owns rows [64w, 64w + 64) as two
-//   32-row query blocks.  Every K or V^T fragment read from LDS feeds the
-//   MFMAs of both blocks, which halves LDS traffic per flop.  One wave per
-//   SIMD; the output accumulators live in AGPRs.
+//   head and BQ = 256/R positions; wave w owns the 32-row query block
+//   [32w, 32w + 32).  Two waves per SIMD: while one issues MFMAs the other's
+//   softmax VALU work runs beside them.  Every MFMA keeps its result and
+//   accumulator in VGPRs (the library compiles this file in that form), so
+//   scores feed the exponentials with no register-file copies.
 //
 //   Key tiles of 64 are walked in two phases: a remote phase over every tile
-//   that holds a remote pair (K rotated by its correction on the way into
-//   LDS, Q in its corrected view), then a local phase over every tile that
-//   holds a local pair (stored K and Q).  A tile that straddles the window
-//   edge is visited once per phase under a mask.
+//   that holds a remote pair (keys and Q in their corrected view), then a
+//   local phase over every tile that holds a local pair (stored K and Q).  A
+//   tile that straddles the window edge is visited once per phase under a
+//   mask.  The remote view of the keys is formed once per call by
+//   rotate_keys_kernel into the caller's workspace: every workgroup of a KV
+//   head reads the same keys, so rotating them per visited tile would repeat
+//   the same VALU work once per query tile.  The cache itself is never
+//   written.
 //
-//   Staging: LDS is double-buffered.  At the start of a tile the next tile's
-//   V and the correction rows it needs are copied HBM -> LDS with buffer
-//   loads into LDS (no registers; V chunks XOR-swizzled by row so that the
-//   transposed reads below spread over the banks), and its K is loaded into
-//   registers; after the MFMAs K is rotated and written to LDS.  One barrier
-//   per tile.
+//   Staging: LDS is double-buffered.  During a tile the next tile's K and V
+//   are copied HBM -> LDS with buffer loads into LDS (no registers, no VALU;
+//   K rows padded to KSTR, V chunks XOR-swizzled by row so that the
+//   transposed reads below spread over the banks).  One barrier per tile.
 //
 //   Scores: each wave computes S^T = K Q^T (keys on the MFMA M axis, queries
 //   on N), so a query's scores sit in one lane pair and P^T is already the B
@@ -49,9 +52,11 @@ namespace jl {
 
 namespace {
 
-// 32-row query blocks per wave: 1 gives 8 waves per workgroup, two per SIMD,
-// whose MFMA and VALU work the hardware interleaves; 2 gives 4 waves, one per
-// SIMD, each K or V^T fragment read from LDS feeding two MFMAs.
+// 32-row query blocks per wave.  1 gives 8 waves per workgroup, two per
+// SIMD, whose MFMA and VALU work the hardware interleaves.  (2 would give 4
+// waves, one per SIMD, each K or V^T fragment read from LDS feeding two
+// MFMAs, but its accumulators and scores no longer fit the 256 VGPRs of the
+// MFMAs' VGPR form.)
 constexpr int NJ = 1;
 constexpr int kWaves = 8 / NJ;
 constexpr int kThreads = kWaves * 64;
@@ -67,9 +72,7 @@ struct Lay5 {
     static constexpr int NC = D / 16;           // 16-dim K chunks (MFMA k)
     static constexpr int NDB = D / 32;          // 32-dim O^T blocks
     static constexpr int KSTR = D + 8;          // K row stride (elements), padded
-    static constexpr int CH = D / 8;            // 16-byte chunks per V row
-    static constexpr int PPT = HALF * BN / kThreads;   // K pairs per thread
-    static constexpr int TPR = kThreads / BN;          // threads per K row
+    static constexpr int CH = D / 8;            // 16-byte chunks per K or V row
 };
 
 // physical 16-byte chunk of logical chunk `c` in V row `row`
@@ -86,8 +89,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     constexpr int NDB = Lay::NDB;
     constexpr int KSTR = Lay::KSTR;
     constexpr int CH = Lay::CH;
-    constexpr int PPT = Lay::PPT;
-    typedef __bf16 KV __attribute__((ext_vector_type(PPT)));
 
     // Two LDS buffers per operand, as separate objects and always selected at
     // compile time: the compiler can then tell that the HBM->LDS copy into
@@ -97,15 +98,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     __shared__ __attribute__((aligned(16))) __bf16 sK1[BN * KSTR];
     __shared__ __attribute__((aligned(16))) __bf16 sV0[BN * D];
     __shared__ __attribute__((aligned(16))) __bf16 sV1[BN * D];
-    // correction rows for the tile being staged, one region of BN/4 rows per
-    // wave (the rows its own K rows need), 16-byte chunks XOR-swizzled by row
-    __shared__ __attribute__((aligned(16))) float2 sT[BN * HALF];
     __shared__ int s_bad;
-
-    // Naming an accumulation register keeps the compiler from assuming the
-    // kernel needs none; it then gives the MFMAs their accumulation-register
-    // form and the output accumulators stay out of the VGPR budget.
-    asm volatile("" ::: "a0");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -153,6 +146,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const uint32_t row_bytes = (uint32_t)kv_row * 2u;
     const __bf16* __restrict__ kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * L * kv_row + (int64_t)g * D;
     const __bf16* __restrict__ vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * L * kv_row + (int64_t)g * D;
+    // keys in their corrected view (only read by remote tiles, which exist only when G > 1)
+    const __bf16* __restrict__ krbase =
+        (G > 1 ? static_cast<const __bf16*>(p.krot) : static_cast<const __bf16*>(p.k)) + (int64_t)b * L * kv_row +
+        (int64_t)g * D;
 
     if (tid == 0) {
         const TableHeader* th = p.table;
@@ -219,75 +216,43 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     };
 
     // ---- staging of the next tile ------------------------------------------------
-    // Every tile is rotated on its way into LDS: remote tiles by their
-    // correction rows, local tiles by table row 0, which is exactly (1, 0).
-    // Wave w stages K rows 16w .. 16w+15.  Their correction rows form one
-    // contiguous range of the table (n(k) = k - floor(k/G) rises by 0 or 1 per
-    // key), which the wave copies to its own LDS region with the V tile; K
-    // goes through registers.  A wave reads only rows it copied itself, so
-    // its own wait on the copy suffices.  All loads go through buffer
-    // resources over the tile's rows: lane offsets stay fixed, the tile base
-    // is scalar, and rows past L read as zeros (they are masked).
-    constexpr int RW = BN / kWaves;                // K rows per wave
-    constexpr int TCH = HALF / 2;                  // 16-byte chunks per table row
-    constexpr int SWM = (PPT / 2 < 8 ? PPT / 2 : 8) - 1;   // table chunk swizzle mask
+    // K and V tiles are copied HBM -> LDS with buffer loads into LDS (no
+    // registers, no VALU).  Remote tiles read the keys in their corrected view
+    // (rotated once per call by rotate_keys_kernel), local tiles the stored
+    // keys.  A copy instruction fills 64 consecutive 16-byte LDS slots, one per
+    // lane, so each lane's HBM offset places its slot: V rows are dense with
+    // their 16-byte chunks XOR-swizzled by row (for the transposed reads),
+    // K rows keep a 16-byte pad (row stride KSTR) whose slot reads past the
+    // tile and lands as zeros.  All offsets are lane constants over a tile
+    // base held in a buffer resource; rows past L read as zeros (masked).
     constexpr int VU = BN * CH / kThreads;         // V copies per thread
     constexpr int VRU = kThreads / CH;             // V rows per copy step
-    constexpr int TU = RW * TCH / 64;              // table copies per thread
-    static_assert(Lay::TPR * RW == 64, "a wave stages whole K rows");
+    constexpr int KS = BN * (CH + 1);              // 16-byte slots of a K tile, pads included
+    constexpr int KU = KS / kThreads;              // K copy rounds every wave takes
+    constexpr int KREM = (KS - KU * kThreads) / 64;   // waves that take one more
     static_assert(VRU % 4 == 0, "V swizzle is lane-constant");
-    const int kr = tid / Lay::TPR;                 // K row of this thread
-    const int f0 = (tid % Lay::TPR) * PPT;         // first frequency of this thread
-    // lane-constant byte offsets
+    static_assert((KS - KU * kThreads) % 64 == 0 && KREM < kWaves, "K slots fill whole copies");
     const uint32_t v_voff = (uint32_t)(tid / CH) * row_bytes + 16u * (uint32_t)vswz<D>(tid / CH, tid % CH);
-    const uint32_t k_voff = (uint32_t)kr * row_bytes + 2u * (uint32_t)f0;
-    auto t_voff = [&](int u) __attribute__((always_inline)) {
-        const int P = u * 64 + lane;
-        const int row = P / TCH;
-        return (uint32_t)(row * HALF * 8 + 16 * ((P % TCH) ^ (row & SWM)));
+    auto k_slot_voff = [&](int slot) __attribute__((always_inline)) {
+        const int row = slot / (CH + 1), ch = slot % (CH + 1);
+        return ch == CH ? 0x80000000u : (uint32_t)row * row_bytes + 16u * (uint32_t)ch;
     };
-    KV stx, sty;
-    int st_row;                                    // this thread's row in its wave's region
-    char* const sTw = reinterpret_cast<char*>(sT) + wave * RW * HALF * 8;
-    // remote offsets within a wave's rows: n(k) - n(kw) = (k - kw) - floor(a/G)
-    // with a = (kw mod G) + (k - kw) < G + 16; for G > 16 that floor is
-    // (a >= G); for G <= 16, floor((a + 1/2) / G) in float is exact (half-step
-    // margin against a rounding error below 2^-18).
-    const float invG = 1.0f / (float)G;
-    auto small_floor_div = [&](int a) __attribute__((always_inline)) {
-        return G > 16 ? (int)(a >= G) : (int)floorf(fmaf((float)a, invG, 0.5f * invG));
-    };
+    uint32_t k_voff[KU + 1];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) k_voff[u] = k_slot_voff((u * kWaves + wave) * 64 + lane);
+    k_voff[KU] = wave < KREM ? k_slot_voff((KU * kWaves + wave) * 64 + lane) : 0u;
     auto tile_k0 = [&](int pi) __attribute__((always_inline)) { return (pi < nR ? pi : nL0 + (pi - nR)) * BN; };
-    // staging is issued in three parts spread over the tile, so that the
-    // vector-memory queue never fills and stalls the wave: K (registers) at
-    // the start, the correction rows with the second score half, V with the
-    // first PV half
-    auto stage_load_k = [&](int pi) __attribute__((always_inline)) {
+    // staging is issued in two parts spread over the tile, so that the
+    // vector-memory queue never fills and stalls the wave: K at the start, V
+    // with the first PV half
+    auto stage_load_k = [&](int pi, auto buf) __attribute__((always_inline)) {
+        char* sKd = reinterpret_cast<char*>(decltype(buf)::value ? sK1 : sK0);
         const int k0 = tile_k0(pi);
         const uint32_t tile_bytes = (uint32_t)min(L - k0, BN) * row_bytes;
-        // K into registers
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)k0 * kv_row, tile_bytes);
-        if constexpr (PPT >= 8) {
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc((pi < nR ? krbase : kbase) + (int64_t)k0 * kv_row, tile_bytes);
 #pragma unroll
-            for (int c = 0; c < PPT / 8; ++c) {
-                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 16u * c, 0, 0);
-                const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + 2u * HALF + 16u * c, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    stx[8 * c + e] = __builtin_bit_cast(bf16x8, x)[e];
-                    sty[8 * c + e] = __builtin_bit_cast(bf16x8, y)[e];
-                }
-            }
-        } else {
-            static_assert(PPT == 4, "K staging covers 4, 8 or 16 pairs per thread");
-            const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rk, k_voff, 0, 0);
-            const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(rk, k_voff + 2u * HALF, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                stx[e] = __builtin_bit_cast(bf16x4, x)[e];
-                sty[e] = __builtin_bit_cast(bf16x4, y)[e];
-            }
-        }
+        for (int u = 0; u < KU; ++u) buffer_lds16(rk, sKd + (u * kWaves + wave) * 1024, k_voff[u], 0);
+        if (KREM > 0 && wave < KREM) buffer_lds16(rk, sKd + (KU * kWaves + wave) * 1024, k_voff[KU], 0);
     };
     auto stage_load_v = [&](int pi, auto buf) __attribute__((always_inline)) {
         __bf16* sVd = decltype(buf)::value ? sV1 : sV0;
@@ -298,41 +263,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
         for (int u = 0; u < VU; ++u)
             buffer_lds16(rv, &sVd[(u * kWaves + wave) * 64 * 8], v_voff, (uint32_t)(u * VRU) * row_bytes);
-    };
-    auto stage_load_t = [&](int pi) __attribute__((always_inline)) {
-        // correction rows of this wave's K rows (row 0 and up for a local tile)
-        const int k0 = tile_k0(pi);
-        const bool rem = pi < nR;
-        const int kw = min(k0 + RW * wave, L - 1);
-        const int kwq = kw / G;
-        const int t0 = rem ? kw - kwq : 0;
-        const __amdgpu_buffer_rsrc_t rt = make_rsrc(TF + (int64_t)t0 * HALF, (uint32_t)min(L - t0, RW) * HALF * 8u);
-#pragma unroll
-        for (int u = 0; u < TU; ++u) buffer_lds16(rt, sTw + u * 64 * 16, t_voff(u), 0);
-        const int kpos = min(k0 + kr, L - 1);
-        st_row = rem ? (kpos - kw) - small_floor_div(kw - kwq * G + (kpos - kw)) : 0;
-    };
-    auto stage_store = [&](auto buf) __attribute__((always_inline)) {
-        __bf16* Kd = (decltype(buf)::value ? sK1 : sK0) + kr * KSTR + f0;
-        // chunk (f0/2 + e) of the row sits at position (f0/2 + e) ^ (row & SWM);
-        // f0/2 is a multiple of SWM + 1, so that is f0/2 + (e ^ (row & SWM))
-        const char* tbase = sTw + st_row * (HALF * 8) + 8 * f0;
-        const int sw = st_row & SWM;
-        KV xr, yr;
-#pragma unroll
-        for (int e = 0; e < PPT / 2; ++e) {
-            const float4 c4 = *reinterpret_cast<const float4*>(tbase + 16 * (e ^ sw));
-            float x0 = (float)stx[2 * e], y0 = (float)sty[2 * e];
-            float x1 = (float)stx[2 * e + 1], y1 = (float)sty[2 * e + 1];
-            rotate_back(x0, y0, make_float2(c4.x, c4.y));
-            rotate_back(x1, y1, make_float2(c4.z, c4.w));
-            xr[2 * e] = (__bf16)x0;
-            yr[2 * e] = (__bf16)y0;
-            xr[2 * e + 1] = (__bf16)x1;
-            yr[2 * e + 1] = (__bf16)y1;
-        }
-        *reinterpret_cast<KV*>(Kd) = xr;
-        *reinterpret_cast<KV*>(Kd + HALF) = yr;
     };
 
     // ---- softmax state -------------------------------------------------------------
@@ -447,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 
     // One tile as straight-line regions, so that MFMAs and VALU work
     // interleave: S(h0) | S(h1) with softmax(h0) | PV(h0) with softmax(h1) |
-    // PV(h1) with the rotation of the next tile's K.  The rare edge work sits
+    // PV(h1).  The rare edge work sits
     // in uniform branches between regions and never touches the accumulators.
     auto tile_body = [&](auto buf, int pn, bool edge, const int (&rlo)[NJ], const int (&rhi)[NJ]) __attribute__((always_inline)) {
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
@@ -458,7 +388,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         qk(K, 0, s0);
         if (edge) edge_fix(s0, 0, rlo, rhi);
         qk(K, 1, s1);
-        stage_load_t(pn);
         probs(s0, P0);
         // keep softmax(h0) in the region of S(h1): without a use here the
         // compiler sinks it below the branch, next to PV(h0)
@@ -466,10 +395,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         for (int j = 0; j < NJ; ++j) asm volatile("" ::"v"(P0[j][0]), "v"(P0[j][1]));
         if (edge) edge_fix(s1, 1, rlo, rhi);
         stage_load_v(pn, Other{});
+        // the copies have no users in the kernel's data flow; left alone the
+        // scheduler sinks them to the tile's end, where the closing wait
+        // would then see their whole latency
+        __builtin_amdgcn_sched_barrier(0);
         pv(V, 0, P0);
         probs(s1, P1);
         pv(V, 1, P1);
-        stage_store(Other{});
     };
 
     using Buf0 = std::integral_constant<int, 0>;
@@ -479,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
         if (pi == nR && nR > 0) load_q(false);   // the local phase starts: stored Q
         const int pn = pi + 1 < NP ? pi + 1 : pi;   // the last tile refills the idle buffer
-        stage_load_k(pn);
+        stage_load_k(pn, Other{});
         const bool rem = pi < nR;
         const int k0 = tile_k0(pi);
         const int k1 = k0 + BN - 1;
@@ -520,11 +452,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         __syncthreads();
     };
 
-    stage_load_k(0);
+    stage_load_k(0, Buf0{});
     stage_load_v(0, Buf0{});
-    stage_load_t(0);
-    wait_vmem();
-    stage_store(Buf0{});
     wait_vmem();
     __syncthreads();
     load_q(nR > 0);
@@ -577,8 +506,53 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     }
 }
 
+// The keys in their corrected view (§3.2 Eq. 5 applied to K): row k of every
+// (batch, KV head) rotated by its correction offset, table row n(k) = k -
+// floor(k/G), rounded to bf16.  One thread per 8 rotation pairs of a row;
+// HBM-bound (one read and one write of K, table rows shared by the KV heads
+// of a position through L2).
+template <int D>
+__global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kr,
+                                                          const float2* __restrict__ TF, int64_t n_items, int64_t L,
+                                                          int Hkv, int64_t G) {
+    constexpr int HALF = D / 2;
+    constexpr int CPR = HALF / 8;   // 8-pair items per row
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n_items) return;
+    const int64_t row = t / CPR;    // (b, position, head), head fastest
+    const int c = (int)(t % CPR);
+    const int64_t pos = (row / Hkv) % L;
+    const int64_t n = pos - pos / G;
+    const __bf16* src = k + row * D + 8 * c;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(src);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(src + HALF);
+    const float4* cs = reinterpret_cast<const float4*>(TF + n * HALF + 8 * c);
+    bf16x8 xo, yo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float4 c4 = cs[e];
+        float x0 = (float)x[2 * e], y0 = (float)y[2 * e];
+        float x1 = (float)x[2 * e + 1], y1 = (float)y[2 * e + 1];
+        rotate_back(x0, y0, make_float2(c4.x, c4.y));
+        rotate_back(x1, y1, make_float2(c4.z, c4.w));
+        xo[2 * e] = (__bf16)x0;
+        yo[2 * e] = (__bf16)y0;
+        xo[2 * e + 1] = (__bf16)x1;
+        yo[2 * e + 1] = (__bf16)y1;
+    }
+    __bf16* dst = kr + row * D + 8 * c;
+    *reinterpret_cast<bf16x8*>(dst) = xo;
+    *reinterpret_cast<bf16x8*>(dst + HALF) = yo;
+}
+
 template <int D, bool OUT_BF16>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
+    if (p.G > 1) {
+        const int64_t n_items = p.B * p.L * p.Hkv * (D / 16);
+        hipLaunchKernelGGL((rotate_keys_kernel<D>), dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.krot), p.TF, n_items, p.L,
+                           (int)p.Hkv, p.G);
+    }
     const int64_t blocks = (int64_t)p.n_qtiles * p.Hkv * p.B;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
