@@ -353,13 +353,34 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // Window-edge, causal-diagonal and ragged tiles mask scores per element;
     // a row meeting its first keys takes this half's max (rounded to bf16) as
     // its reference, which is subtracted here once and by the MFMA after.
-    auto edge_fix = [&](f32x16 (&s)[NJ], int kb, const int (&rlo)[NJ], const int (&rhi)[NJ]) {
+    // Per query block of a tile: does it hold a kept pair (act), and is some
+    // pair of the block outside the kept window (msk)?  Wave-uniform, and
+    // written with selects so that it compiles without branches.
+    auto block_state = [&](int j, bool rem, int k0, bool& act, bool& msk) __attribute__((always_inline)) {
+        const int k1 = k0 + BN - 1;
+        const bool act_r = pjhi[j] - k0 > w0;
+        const bool msk_r = pj0[j] - k1 <= w0;
+        const bool act_l = (k0 <= pjhi[j]) & ((G == 1) | (pj0[j] - k1 <= w0));
+        const bool msk_l = (k1 > pj0[j]) | ((G > 1) & (pjhi[j] - k0 > w0));
+        act = (rem ? act_r : act_l) & (pj0[j] < L);
+        msk = (rem ? msk_r : msk_l) | !act;
+    };
+    auto edge_fix = [&](f32x16 (&s)[NJ], int kb, bool rem, int k0) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
+            // kept key window [rlo, rhi] relative to the lane's first key k0 + 8hh
+            bool act, msk;
+            block_state(j, rem, k0, act, msk);
+            const int klo = (rem || G == 1) ? INT_MIN / 2 : my_q[j] - w0;
+            const int khi = rem ? my_q[j] - w0 - 1 : my_q[j];
+            int rlo = act ? klo - k0 - 8 * hh : 1;
+            int rhi = act ? khi - k0 - 8 * hh : 0;
+            rlo = msk ? rlo : INT_MIN / 2;   // every pair kept
+            rhi = msk ? rhi : INT_MAX / 2;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int c0 = 32 * kb + 16 * (i >> 3) + (i & 7);
-                s[j][i] = ((c0 >= rlo[j]) & (c0 <= rhi[j])) ? s[j][i] : -INFINITY;
+                s[j][i] = ((c0 >= rlo) & (c0 <= rhi)) ? s[j][i] : -INFINITY;
             }
             float m = s[j][0];
 #pragma unroll
@@ -377,23 +398,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 
     // One tile as straight-line regions, so that MFMAs and VALU work
     // interleave: S(h0) | S(h1) with softmax(h0) | PV(h0) with softmax(h1) |
-    // PV(h1).  The rare edge work sits
-    // in uniform branches between regions and never touches the accumulators.
-    auto tile_body = [&](auto buf, int pn, bool edge, const int (&rlo)[NJ], const int (&rhi)[NJ]) __attribute__((always_inline)) {
+    // PV(h1).  S(h0) is issued by the caller right after the barrier.  The
+    // rare edge work sits in uniform branches between regions and never
+    // touches the accumulators.
+    auto tile_body = [&](auto buf, int pn, bool edge, bool rem, int k0, f32x16 (&s0)[NJ]) __attribute__((always_inline)) {
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
         const __bf16* K = decltype(buf)::value ? sK1 : sK0;
         const __bf16* V = decltype(buf)::value ? sV1 : sV0;
-        f32x16 s0[NJ], s1[NJ];
+        f32x16 s1[NJ];
         bf16x8 P0[NJ][2], P1[NJ][2];
-        qk(K, 0, s0);
-        if (edge) edge_fix(s0, 0, rlo, rhi);
+        if (edge) edge_fix(s0, 0, rem, k0);
         qk(K, 1, s1);
         probs(s0, P0);
         // keep softmax(h0) in the region of S(h1): without a use here the
         // compiler sinks it below the branch, next to PV(h0)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) asm volatile("" ::"v"(P0[j][0]), "v"(P0[j][1]));
-        if (edge) edge_fix(s1, 1, rlo, rhi);
+        if (edge) edge_fix(s1, 1, rem, k0);
         stage_load_v(pn, Other{});
         // the copies have no users in the kernel's data flow; left alone the
         // scheduler sinks them to the tile's end, where the closing wait
@@ -410,44 +431,24 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     auto tile = [&](int pi, auto buf) __attribute__((always_inline)) {
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
         if (pi == nR && nR > 0) load_q(false);   // the local phase starts: stored Q
+        // the first score MFMAs go out right after the barrier, ahead of the
+        // tile's scalar set-up
+        f32x16 s0[NJ];
+        qk(decltype(buf)::value ? sK1 : sK0, 0, s0);
         const int pn = pi + 1 < NP ? pi + 1 : pi;   // the last tile refills the idle buffer
         stage_load_k(pn, Other{});
         const bool rem = pi < nR;
         const int k0 = tile_k0(pi);
-        const int k1 = k0 + BN - 1;
-        // per query block: masked?, kept key window [rlo, rhi] relative to
-        // the lane's first key k0 + 8hh
-        bool msk[NJ];
-        int rlo[NJ], rhi[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            bool act;
-            if (rem) {
-                act = pjhi[j] - k0 > w0;
-                msk[j] = pj0[j] - k1 <= w0;
-            } else {
-                act = k0 <= pjhi[j] && (G == 1 || pj0[j] - k1 <= w0);
-                msk[j] = k1 > pj0[j] || (G > 1 && pjhi[j] - k0 > w0);
-            }
-            act = act && pj0[j] < L;
-            const int klo = (rem || G == 1) ? INT_MIN / 2 : my_q[j] - w0;
-            const int khi = rem ? my_q[j] - w0 - 1 : my_q[j];
-            rlo[j] = act ? klo - k0 - 8 * hh : 1;
-            rhi[j] = act ? khi - k0 - 8 * hh : 0;
-            msk[j] = msk[j] || !act;
-            if (!msk[j]) {   // every pair kept
-                rlo[j] = INT_MIN / 2;
-                rhi[j] = INT_MAX / 2;
-            }
-        }
         bool any_msk = false, any_unset = false;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            any_msk = any_msk || msk[j];
-            any_unset = any_unset || m_ref[j] == -INFINITY;
+            bool act, msk;
+            block_state(j, rem, k0, act, msk);
+            any_msk = any_msk | msk;
+            any_unset = any_unset | (m_ref[j] == -INFINITY);
         }
         const bool edge = any_msk || __any(any_unset);
-        tile_body(buf, pn, edge, rlo, rhi);
+        tile_body(buf, pn, edge, rem, k0, s0);
         wait_vmem();   // the next tile's V has landed in LDS
         __syncthreads();
     };
