@@ -15,7 +15,7 @@
 //   accumulator in VGPRs (the library compiles this file in that form), so
 //   scores feed the exponentials with no register-file copies.
 //
-//   Key tiles of 64 are walked in two phases: a remote phase over every tile
+//   Key tiles of BN = 128 are walked in two phases: a remote phase over every tile
 //   that holds a remote pair (keys and Q in their corrected view), then a
 //   local phase over every tile that holds a local pair (stored K and Q).  A
 //   tile that straddles the window edge is visited once per phase under a
@@ -60,7 +60,10 @@ namespace {
 constexpr int NJ = 1;
 constexpr int kWaves = 8 / NJ;
 constexpr int kThreads = kWaves * 64;
-constexpr int BN = 64;                        // keys per tile
+// keys per tile: 128 halves the per-tile scalar set-up, copy issue and
+// barrier per key against 64, and double-buffered K and V still fit in LDS
+// (135 KB of 160 KB at D = 128)
+constexpr int BN = 128;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -397,32 +400,41 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     };
 
     // One tile as straight-line regions, so that MFMAs and VALU work
-    // interleave: S(h0) | S(h1) with softmax(h0) | PV(h0) with softmax(h1) |
-    // PV(h1).  S(h0) is issued by the caller right after the barrier.  The
-    // rare edge work sits in uniform branches between regions and never
-    // touches the accumulators.
+    // interleave: S(b+1) with softmax(b), then PV(b), for each 32-key block
+    // b.  S(0) is issued by the caller right after the barrier.  The rare
+    // edge work sits in uniform branches between regions and never touches
+    // the accumulators.
+    constexpr int NKB = BN / 32;   // 32-key score blocks per tile
     auto tile_body = [&](auto buf, int pn, bool edge, bool rem, int k0, f32x16 (&s0)[NJ]) __attribute__((always_inline)) {
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
         const __bf16* K = decltype(buf)::value ? sK1 : sK0;
         const __bf16* V = decltype(buf)::value ? sV1 : sV0;
-        f32x16 s1[NJ];
-        bf16x8 P0[NJ][2], P1[NJ][2];
-        if (edge) edge_fix(s0, 0, rem, k0);
-        qk(K, 1, s1);
-        probs(s0, P0);
-        // keep softmax(h0) in the region of S(h1): without a use here the
-        // compiler sinks it below the branch, next to PV(h0)
+        f32x16 sa[NJ], sb[NJ];
+        bf16x8 Pa[NJ][2];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) asm volatile("" ::"v"(P0[j][0]), "v"(P0[j][1]));
-        if (edge) edge_fix(s1, 1, rem, k0);
-        stage_load_v(pn, Other{});
-        // the copies have no users in the kernel's data flow; left alone the
-        // scheduler sinks them to the tile's end, where the closing wait
-        // would then see their whole latency
-        __builtin_amdgcn_sched_barrier(0);
-        pv(V, 0, P0);
-        probs(s1, P1);
-        pv(V, 1, P1);
+        for (int j = 0; j < NJ; ++j) sa[j] = s0[j];
+        if (edge) edge_fix(sa, 0, rem, k0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            // the scores of block kb are in sa; block kb + 1 goes into sb
+            if (kb + 1 < NKB) qk(K, kb + 1, sb);
+            probs(sa, Pa);
+            // keep softmax(kb) in the region of S(kb + 1): without a use here
+            // the compiler sinks it below the branch, next to PV(kb)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) asm volatile("" ::"v"(Pa[j][0]), "v"(Pa[j][1]));
+            if (kb + 1 < NKB && edge) edge_fix(sb, kb + 1, rem, k0);
+            if (kb == 0) {
+                stage_load_v(pn, Other{});
+                // the copies have no users in the kernel's data flow; left
+                // alone the scheduler sinks them to the tile's end, where the
+                // closing wait would then see their whole latency
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            pv(V, kb, Pa);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) sa[j] = sb[j];
+        }
     };
 
     using Buf0 = std::integral_constant<int, 0>;
