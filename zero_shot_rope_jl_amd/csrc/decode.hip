@@ -11,7 +11,7 @@
 // waves of a workgroup read whole key rows (all heads are contiguous in the
 // cache) and the grid holds about one workgroup per compute unit.  A wave
 // streams its keys 32 per iteration with the next iteration's K and V in
-// flight.  K goes straight from HBM into MFMA
+// flight (non-temporal loads).  K goes straight from HBM into MFMA
 // A-operand registers (rows = keys); V goes through wave-private LDS,
 // transposed, to be the A operand of O^T += V^T P^T.  The R query heads of
 // the KV head are the MFMA N columns (16x16x32 bf16), so each K/V byte is read
@@ -54,21 +54,29 @@ struct DecodeTile {
     bf16x8 v[KPL];                       // V rows for the transpose
 };
 
+// Cache reads are non-temporal: every byte is read once per step, and the
+// streaming hint gave ~13% more read bandwidth for this access shape than
+// ordinary loads.
+template <int D>
+__device__ inline void load_k_blk(DecodeTile<D>& t, const __bf16* __restrict__ kc, int64_t cache_b, int64_t row,
+                                  int kbase, int kend, int colh, int gq, int blk) {
+    constexpr int NC = DecodeTile<D>::NC;
+    // A-operand row colh of block blk holds key 8*(colh/4) + 4*blk + colh%4:
+    // C rows then give P^T slots in natural key order
+    const int key = kbase + 8 * (colh >> 2) + 4 * blk + (colh & 3);
+    const bool ok = key < kend;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        t.k[blk][c] = ok ? __builtin_nontemporal_load(
+                               reinterpret_cast<const bf16x8*>(kc + cache_b + (int64_t)key * row + 32 * c + 8 * gq))
+                         : bf16x8{};
+}
+
 template <int D>
 __device__ inline void load_k(DecodeTile<D>& t, const __bf16* __restrict__ kc, int64_t cache_b, int64_t row,
                               int kbase, int kend, int colh, int gq) {
-    constexpr int NC = DecodeTile<D>::NC;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        // A-operand row colh of block blk holds key 8*(colh/4) + 4*blk + colh%4:
-        // C rows then give P^T slots in natural key order
-        const int key = kbase + 8 * (colh >> 2) + 4 * blk + (colh & 3);
-        const bool ok = key < kend;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-            t.k[blk][c] = ok ? *reinterpret_cast<const bf16x8*>(kc + cache_b + (int64_t)key * row + 32 * c + 8 * gq)
-                             : bf16x8{};
-    }
+    for (int blk = 0; blk < 2; ++blk) load_k_blk<D>(t, kc, cache_b, row, kbase, kend, colh, gq, blk);
 }
 
 template <int D>
@@ -80,8 +88,9 @@ __device__ inline void load_v(DecodeTile<D>& t, const __bf16* __restrict__ vc, i
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
         const int key = kbase + kg * KPL + e;
-        t.v[e] = key < kend ? *reinterpret_cast<const bf16x8*>(vc + cache_b + (int64_t)key * row + dg * 8)
-                            : bf16x8{};
+        t.v[e] = key < kend
+                     ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(vc + cache_b + (int64_t)key * row + dg * 8))
+                     : bf16x8{};
     }
 }
 
@@ -193,9 +202,30 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     float2 base = make_float2(1.f, 0.f);
     if (lane < HALF && wstart < wend && G > 1) base = TF[(int64_t)(wstart - wstart / G) * HALF + lane];
 
-    // One register tile (loaded above): each half is reloaded for the next
-    // step as soon as this step has consumed it, so loads stay in flight
-    // during the compute.
+    // the corrected query for the current step: R(nb) applied to R(-n_q) q
+    bf16x8 qit[NC];
+    int nb = 0;
+    auto rotate_query = [&](int kb) {
+        nb = kb - kb / G;
+        wave_lds_sync();   // earlier reads of myBase are done
+        if (lane < HALF) myBase[lane] = base;
+        wave_lds_sync();
+#pragma unroll
+        for (int c = 0; c < NC / 2; ++c)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float2 cs = myBase[32 * c + 8 * gq + j];
+                const float x = (float)qrem[c][j], y = (float)qrem[c + NC / 2][j];
+                qit[c][j] = (__bf16)(x * cs.x - y * cs.y);
+                qit[c + NC / 2][j] = (__bf16)(x * cs.y + y * cs.x);
+            }
+    };
+    if (G > 1 && wstart < wend && wstart < kloc) rotate_query(wstart);
+
+    // One register tile (loaded above): each part is reloaded for the next
+    // step as soon as this step has consumed it (V after its transpose, each
+    // 16-key half of K after its scores), so loads stay in flight during the
+    // compute.
     for (int kbase = wstart; kbase < wend; kbase += kWaveKeys) {
         const int knext = kbase + kWaveKeys;
         // ---- V rows -> V^T in this wave's LDS slice --------------------------
@@ -216,23 +246,6 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
 
         const bool w_loc = (G == 1) || (kbase + kWaveKeys - 1 >= kloc);
         const bool w_rem = (G > 1) && (kbase < kloc);
-        bf16x8 qit[NC];
-        int nb = 0;
-        if (w_rem) {
-            // per-iteration base rotation, one frequency per lane
-            nb = kbase - kbase / G;
-            if (lane < HALF) myBase[lane] = base;
-            wave_lds_sync();
-#pragma unroll
-            for (int c = 0; c < NC / 2; ++c)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float2 cs = myBase[32 * c + 8 * gq + j];
-                    const float x = (float)qrem[c][j], y = (float)qrem[c + NC / 2][j];
-                    qit[c][j] = (__bf16)(x * cs.x - y * cs.y);
-                    qit[c + NC / 2][j] = (__bf16)(x * cs.y + y * cs.x);
-                }
-        }
 
         float s[2][4];
 #pragma unroll
@@ -267,9 +280,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
                 else v = w_loc ? sl[i] : sr[i];
                 s[blk][i] = kk < wend ? v * scale2 : -INFINITY;
             }
+            // this half's K registers are free: start the next step's loads
+            if (knext < wend) load_k_blk<D>(cur, kc, cache_b, row, knext, wend, colh, gq, blk);
         }
-        // K registers are free: start the next step's K loads
-        if (knext < wend) load_k<D>(cur, kc, cache_b, row, knext, wend, colh, gq);
 
         // ---- online softmax per head column: 8 values here, 4 quads per head --
         float mx = -INFINITY;
@@ -308,6 +321,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
             const float2 j2 = sJ[step * JSTR + lane];
             base = make_float2(base.x * j2.x - base.y * j2.y, base.y * j2.x + base.x * j2.y);
         }
+        // the next step's corrected query, computed here so that it is off the
+        // path from K's arrival to the next K loads
+        if (G > 1 && knext < wend && knext < kloc) rotate_query(knext);
     }
 
     // ---- merge the NW waves of each head, write this split's partials -------
