@@ -99,23 +99,26 @@ def bench_prefill(torch, jl, si, args, w, x):
     torch.cuda.synchronize()
     log(f"[bench] prefill warmup done, timing {args.steps} steps")
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_call = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    stats = {"mean": round(ms, 4), "median": round(float(np.median(per_call)), 4), "min": round(per_call[0], 4)}
     assert torch.isfinite(out[:, :: 4096].float()).all(), "non-finite prefill output"
     flops = prefill_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] prefill {ms:.3f} ms/step, {tflops:.1f} TFLOP/s (wall {wall:.2f}s)")
+    log(f"[bench] prefill {ms:.3f} ms/step (median {stats['median']:.3f}, min {stats['min']:.3f}), "
+        f"{tflops:.1f} TFLOP/s (wall {wall:.2f}s)")
     del q, k, v, out, lse
     torch.cuda.empty_cache()
-    return ms, tflops, flops
+    return ms, tflops, flops, stats
 
 
 def bench_decode(torch, jl, si, args):
@@ -155,13 +158,22 @@ def bench_decode(torch, jl, si, args):
     ev1.record(stream)
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / (args.decode_passes * dw.steps)
+    # per-step median from one more pass with an event between steps (not part of the timed region)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(dw.steps + 1)]
+    evs[0].record(stream)
+    for s in range(dw.steps):
+        L = dw.prompt_len + s + 1
+        jl.jl_bifocal_decode(qs[s], kc, vc, out, None, L, dw.w0, dw.w_pretrained, dw.rope_base, dw.sm_scale, table, ws)
+        evs[s + 1].record(stream)
+    torch.cuda.synchronize()
+    us_median = float(np.median([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(dw.steps)]))
     mean_L = dw.prompt_len + (dw.steps + 1) / 2.0
     bytes_step = 2.0 * dw.B * mean_L * dw.Hkv * dw.D * 2
     gbs = bytes_step / (us * 1e-6) / 1e9
-    log(f"[bench] decode {us:.2f} us/step, {gbs:.0f} GB/s")
+    log(f"[bench] decode {us:.2f} us/step (per-step median {us_median:.2f}), {gbs:.0f} GB/s")
     del kc, vc
     torch.cuda.empty_cache()
-    return dw, us, gbs, bytes_step
+    return dw, us, gbs, bytes_step, us_median
 
 
 def cpu_baseline(si, w, x, n_rows):
@@ -212,7 +224,7 @@ def main():
     w = si.WORKLOADS["ext128k"]
     log(f"[bench] generating {w.name} inputs")
     x = si.make_prefill_inputs(w, want_f64=False)
-    ms, tflops, flops = bench_prefill(torch, jl, si, args, w, x)
+    ms, tflops, flops, pstats = bench_prefill(torch, jl, si, args, w, x)
     traffic = measured_traffic()
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -226,11 +238,13 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": pick(traffic, "jl::prefill_bf16_kernel<128, true>"),
                      "flops_per_launch": flops},
+        "prefill_ms_per_call": pstats,
     }
     if not args.skip_decode:
-        dw, us, gbs, bytes_step = bench_decode(torch, jl, si, args)
+        dw, us, gbs, bytes_step, us_median = bench_decode(torch, jl, si, args)
         result["decode"] = {
-            "us_per_step": round(us, 3), "unit": "µs/step", "steps_timed": args.decode_passes * dw.steps,
+            "us_per_step": round(us, 3), "us_per_step_median": round(us_median, 3), "unit": "µs/step",
+            "steps_timed": args.decode_passes * dw.steps,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": pick(traffic, "jl::decode_"),

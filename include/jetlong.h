@@ -139,6 +139,36 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
                        void* hip_stream);
 
 /*
+ * jl_bifocal_prefill_chunk -- a chunk of Lq new tokens appended to a cache
+ * (chunked prefill, or several decode tokens at once): the rows at positions
+ * L-Lq .. L-1 of jl_bifocal_prefill over L tokens (§3 Eq. 1, §3.2 Eqs. 4-5,
+ * §3.3 Eq. 6).  G = max(1, ceil(L / w_pretrained)) comes from L, the count
+ * of every key the chunk sees, so a chunk that crosses a multiple of
+ * w_pretrained is computed under the new G (the cache is not rewritten).
+ *
+ *   q       [B, Lq,   Hq,  D]  in_dtype   stored RoPE(x, p), p = L-Lq .. L-1
+ *   k_cache [B, Lmax, Hkv, D]  in_dtype   rows 0..L-1 valid (the chunk's own
+ *   v_cache [B, Lmax, Hkv, D]  in_dtype   rows already written by the caller)
+ *   out     [B, Lq,   Hq,  D]  out_dtype
+ *   lse     [B, Hq,   Lq]      fp32, or NULL
+ *
+ * dtypes, D, GQA ratios, table and workspace as for jl_bifocal_prefill
+ * (workspace: jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D,
+ * w_pretrained) bytes).  Every key row 0..L-1 is rotated into the workspace
+ * on each call, so a chunk costs one pass over the cache's keys besides its
+ * attention.
+ *
+ * Errors: as for jl_bifocal_prefill, plus JL_EINVAL unless
+ * 1 <= Lq <= L <= Lmax <= 2^30.
+ */
+JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* out,
+                             float* lse, int in_dtype, int out_dtype, int64_t B, int64_t Lq,
+                             int64_t L, int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D,
+                             int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale,
+                             const void* table, size_t table_bytes, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
+
+/*
  * jl_bifocal_decode_workspace -- bytes of fp32 scratch that jl_bifocal_decode
  * needs for a step that attends L keys (split-KV partials).  Pure host call.
  */

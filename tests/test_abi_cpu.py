@@ -24,11 +24,11 @@ def header_symbols():
 def test_exports_every_declared_symbol():
     syms = header_symbols()
     assert syms == sorted(["jl_last_error", "jl_version", "jl_schedule", "jl_bifocal_prefill_workspace",
-                           "jl_bifocal_prefill", "jl_bifocal_decode_workspace", "jl_bifocal_decode",
-                           "jl_table_fill_host"])
+                           "jl_bifocal_prefill", "jl_bifocal_prefill_chunk", "jl_bifocal_decode_workspace",
+                           "jl_bifocal_decode", "jl_table_fill_host"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 2
+    assert jl.jl_version() == 3
 
 
 def test_schedule_golden_and_table_size():
@@ -100,6 +100,29 @@ def test_prefill_without_workspace_when_none_is_needed_passes_validation_order()
     # G == 1: a NULL workspace is accepted; the call still fails later, on the
     # unsupported head_dim, before any HIP call
     assert _prefill(L=64, wp=64, ws=None, wsb=0, D=96) == jl.JL_EUNSUPPORTED
+
+
+def _chunk(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, Lq=64, L=600,
+             Lmax=700, Hq=8, Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE, tb=1 << 30, ws=FAKE,
+             wsb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_prefill_chunk(a["q"], a["k"], a["v"], a["out"], a["lse"], a["i"], a["o"], a["B"],
+                                           a["Lq"], a["L"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["w0"],
+                                           a["wp"], a["base"], a["sc"], a["table"], a["tb"], a["ws"], a["wsb"],
+                                           None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Lq=0), jl.JL_EINVAL), (dict(Lq=601), jl.JL_EINVAL), (dict(Lmax=599), jl.JL_EINVAL),
+    (dict(L=0), jl.JL_EINVAL), (dict(q=None), jl.JL_EINVAL), (dict(out=FAKE + 2), jl.JL_EINVAL),
+    (dict(D=96), jl.JL_EUNSUPPORTED), (dict(Hq=32, Hkv=2), jl.JL_EUNSUPPORTED), (dict(tb=100), jl.JL_ESPACE),
+    (dict(ws=None), jl.JL_ESPACE), (dict(wsb=600 * 2 * 128 * 2 - 1), jl.JL_ESPACE),
+    (dict(i=jl.JL_F32, o=jl.JL_BF16), jl.JL_EUNSUPPORTED), (dict(Lmax=(1 << 30) + 1), jl.JL_EINVAL),
+])
+def test_prefill_chunk_validation(over, code):
+    assert _chunk(**over) == code
+    assert jl.jl_last_error()
 
 
 def _decode(**over):

@@ -45,6 +45,10 @@ def _load():
     L.jl_bifocal_prefill_workspace.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.POINTER(sz)]
     L.jl_bifocal_prefill.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                      i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
+    L.jl_bifocal_prefill_chunk.restype = ctypes.c_int
+    L.jl_bifocal_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                           i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp,
+                                           sz, vp]
     L.jl_bifocal_decode_workspace.restype = ctypes.c_int
     L.jl_bifocal_decode_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(sz)]
     L.jl_bifocal_decode.restype = ctypes.c_int
@@ -185,6 +189,34 @@ def jl_bifocal_prefill(q, k, v, out, lse, w0: int, w_pretrained: int, rope_base:
                                   _dtype_code(out), B, L, Hq, Hkv, D, w0, w_pretrained, rope_base,
                                   sm_scale, _ptr(table), table.numel() * table.element_size(),
                                   _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def jl_bifocal_prefill_chunk(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrained: int,
+                             rope_base: float, sm_scale: float, table, workspace=None, stream=None):
+    """q [B,Lq,Hq,D] at positions L-Lq..L-1, caches [B,Lmax,Hkv,D] with rows < L valid,
+    out [B,Lq,Hq,D], lse [B,Hq,Lq] fp32 or None.  `workspace` as for jl_bifocal_prefill
+    (sized for L keys); when None and some is needed, one is allocated through torch."""
+    _need_device(q, k_cache, v_cache, out, lse, table, workspace)
+    B, Lq, Hq, D = q.shape
+    Bk, Lmax, Hkv, Dk = k_cache.shape
+    if Bk != B or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [B, Lmax, Hkv, D] matching q")
+    if tuple(out.shape) != (B, Lq, Hq, D):
+        raise ValueError("out must be [B, Lq, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq, Lq) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq, Lq]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share a dtype")
+    if workspace is None:
+        n = jl_bifocal_prefill_workspace(_dtype_code(q), B, L, Hkv, D, w_pretrained)
+        workspace = _torch().empty(n, dtype=_torch().uint8, device=q.device) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.jl_bifocal_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                        _dtype_code(q), _dtype_code(out), B, Lq, L, Lmax, Hq, Hkv, D, w0,
+                                        w_pretrained, rope_base, sm_scale, _ptr(table),
+                                        table.numel() * table.element_size(), _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
     return out, lse
 
 

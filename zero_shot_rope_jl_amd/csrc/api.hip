@@ -67,7 +67,7 @@ extern "C" {
 
 JL_API const char* jl_last_error(void) { return g_err.c_str(); }
 
-JL_API int jl_version(void) { return 2; }
+JL_API int jl_version(void) { return 3; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -116,18 +116,27 @@ JL_API int jl_bifocal_prefill_workspace(int in_dtype, int64_t B, int64_t L, int6
     return JL_OK;
 }
 
-JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int in_dtype,
-                              int out_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
-                              int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
-                              size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Both prefill entry points: Lq queries at positions L - Lq .. L - 1 over keys
+// 0..L-1 held in k/v with Lkv rows per batch entry.
+int prefill_impl(const char* who, const void* q, const void* k, const void* v, void* out, float* lse, int in_dtype,
+                 int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Lkv, int64_t Hq, int64_t Hkv, int64_t D,
+                 int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
+                 size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
     g_err.clear();
-    if (!q || !k || !v || !out || !table) return fail(JL_EINVAL, "q, k, v, out and table must be non-NULL");
+    if (!q || !k || !v || !out || !table) return fail(JL_EINVAL, "%s: q, k, v, out and table must be non-NULL", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(table) ||
         !aligned16(lse) || !aligned16(workspace))
-        return fail(JL_EINVAL, "device pointers must be 16-byte aligned");
+        return fail(JL_EINVAL, "%s: device pointers must be 16-byte aligned", who);
     if (int rc = check_attention_common(B, L, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, in_dtype,
                                         out_dtype))
         return rc;
+    if (Lq < 1 || Lq > L || Lkv < L || Lkv > kMaxLen)
+        return fail(JL_EINVAL, "%s: need 1 <= Lq <= L <= Lmax <= 2^30 (Lq=%lld, L=%lld, Lmax=%lld)", who,
+                    (long long)Lq, (long long)L, (long long)Lkv);
     const int64_t R = Hq / Hkv;
     if (R != 1 && R != 2 && R != 4 && R != 8)
         return fail(JL_EUNSUPPORTED, "GQA ratio Hq/Hkv = %lld not supported (1, 2, 4, 8)", (long long)R);
@@ -140,7 +149,7 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
         return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : (size_t)0,
                     ws_need);
     const int BQ = 256 / (int)R;
-    const int64_t n_qtiles = (L + BQ - 1) / BQ;
+    const int64_t n_qtiles = (Lq + BQ - 1) / BQ;
     if (n_qtiles * Hkv * B > 0x7fffffffLL) return fail(JL_EINVAL, "grid too large");
 
     jl::PrefillParams p{};
@@ -153,6 +162,9 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
     p.TF = reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes);
     p.B = B;
     p.L = L;
+    p.Lq = Lq;
+    p.q_off = L - Lq;
+    p.Lkv = Lkv;
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.R = (int)R;
@@ -166,8 +178,30 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
     p.krot = workspace;
     (void)hipGetLastError();
     hipError_t e = jl::launch_prefill(p, in_dtype, out_dtype, static_cast<hipStream_t>(hip_stream));
-    if (e != hipSuccess) return fail(JL_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
     return JL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int in_dtype,
+                              int out_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                              int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
+                              size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return prefill_impl("prefill", q, k, v, out, lse, in_dtype, out_dtype, B, L, L, L, Hq, Hkv, D, w0,
+                        w_pretrained, rope_base, sm_scale, table, table_bytes, workspace, workspace_bytes, hip_stream);
+}
+
+JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                    int in_dtype, int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Lmax,
+                                    int64_t Hq, int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained,
+                                    double rope_base, float sm_scale, const void* table, size_t table_bytes,
+                                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return prefill_impl("prefill_chunk", q, k_cache, v_cache, out, lse, in_dtype, out_dtype, B, Lq, L, Lmax, Hq,
+                        Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
+                        workspace_bytes, hip_stream);
 }
 
 JL_API int jl_bifocal_decode_workspace(int64_t B, int64_t Hq, int64_t D, int64_t L, size_t* bytes) {

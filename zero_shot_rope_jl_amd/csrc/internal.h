@@ -16,7 +16,10 @@ struct PrefillParams {
     float* lse;
     const TableHeader* table;
     const float2* TF;   // (cos, sin)(n theta_i) rows, n < coverage
-    int64_t B, L, Hq, Hkv;
+    int64_t B, L, Hq, Hkv;   // L: keys (positions 0..L-1); G comes from L
+    int64_t Lq;              // query rows, at positions q_off .. q_off + Lq - 1 = L - 1
+    int64_t q_off;
+    int64_t Lkv;             // rows per batch entry of k and v (>= L)
     int R;              // Hq / Hkv
     int BQ;             // query positions per workgroup (256 / R)
     int n_qtiles;

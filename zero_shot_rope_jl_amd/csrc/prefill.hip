@@ -281,7 +281,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     bid /= (int)p.B;
     const int qt = p.n_qtiles - 1 - bid;
 
+    // positions: keys 0..L-1; queries q_off..L-1, stored as rows 0..Lq-1
     const int L = (int)p.L;
+    const int Lq = (int)p.Lq;
+    const int q_off = (int)p.q_off;
+    const int64_t Lkv = p.Lkv;   // rows per batch entry of k and v
     const int Hq = (int)p.Hq;
     const int Hkv = (int)p.Hkv;
     const int G = (int)p.G;
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const int r = wave % R;
     const int pb = wave / R;
     const int head = g * R + r;
-    const int q0 = qt * p.BQ;
+    const int q0 = q_off + qt * p.BQ;
     const int q_hi = min(q0 + p.BQ, L) - 1;
     const int p0 = q0 + pb * 32;
     const int p_hi = min(p0 + 31, L - 1);
@@ -303,8 +307,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const T* __restrict__ vg = static_cast<const T*>(p.v);
     const float2* __restrict__ TF = p.TF;
     const int64_t kv_row = (int64_t)Hkv * D;
-    const T* __restrict__ kbase = kg + (int64_t)b * L * kv_row + (int64_t)g * D;
-    const T* __restrict__ vbase = vg + (int64_t)b * L * kv_row + (int64_t)g * D;
+    const T* __restrict__ kbase = kg + (int64_t)b * Lkv * kv_row + (int64_t)g * D;
+    const T* __restrict__ vbase = vg + (int64_t)b * Lkv * kv_row + (int64_t)g * D;
 
     if (p.fixup) {
         // Fixup pass: only a workgroup with a marked row (NaN in element 0)
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             const int hq = g * R + tid / p.BQ;
             const int pos = q0 + tid % p.BQ;
             if (pos < L) {
-                const int64_t o = (((int64_t)b * L + pos) * Hq + hq) * D;
+                const int64_t o = (((int64_t)b * Lq + (pos - q_off)) * Hq + hq) * D;
                 const float e0 = OUT_BF16 ? (float)static_cast<const __bf16*>(p.out)[o]
                                           : static_cast<const float*>(p.out)[o];
                 if (e0 != e0) s_marked = 1;
@@ -333,12 +337,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     if (s_bad) {
         // The table does not belong to this (D, rope_base, L): poison the output.
         if (wave_active && my_q < L) {
-            const int64_t o = (((int64_t)b * L + my_q) * Hq + head) * D;
+            const int64_t o = (((int64_t)b * Lq + (my_q - q_off)) * Hq + head) * D;
             for (int d = hh; d < D; d += 2) {
                 if constexpr (OUT_BF16) static_cast<__bf16*>(p.out)[o + d] = (__bf16)NAN;
                 else static_cast<float*>(p.out)[o + d] = NAN;
             }
-            if (hh == 0 && p.lse) p.lse[((int64_t)b * Hq + head) * L + my_q] = NAN;
+            if (hh == 0 && p.lse) p.lse[((int64_t)b * Hq + head) * Lq + (my_q - q_off)] = NAN;
         }
         return;
     }
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const int NP = nR + (nkt - nL0);
 
     const bool q_ok = wave_active && my_q < L;
-    const T* qrow = qg + (((int64_t)b * L + (q_ok ? my_q : 0)) * Hq + head) * D;
+    const T* qrow = qg + (((int64_t)b * Lq + (q_ok ? my_q - q_off : 0)) * Hq + head) * D;
     QF qv[NQ];
     load_q_frags<D, BF16>(qv, qrow, q_ok, nR > 0, TF, q_ok ? (int64_t)(my_q - my_q / G) : 0, hh);
 
@@ -447,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (q_ok) {
         const float inv = 1.f / l_tot;
-        const int64_t o = (((int64_t)b * L + my_q) * Hq + head) * D;
+        const int64_t o = (((int64_t)b * Lq + (my_q - q_off)) * Hq + head) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             }
         }
         if (hh == 0 && p.lse)
-            p.lse[((int64_t)b * Hq + head) * L + my_q] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+            p.lse[((int64_t)b * Hq + head) * Lq + (my_q - q_off)] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
     }
 }
 

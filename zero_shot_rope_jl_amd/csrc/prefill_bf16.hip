@@ -119,14 +119,18 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     bid /= (int)p.B;
     const int qt = p.n_qtiles - 1 - bid;
 
+    // positions: keys 0..L-1; queries q_off..L-1, stored as rows 0..Lq-1
     const int L = (int)p.L;
+    const int Lq = (int)p.Lq;
+    const int q_off = (int)p.q_off;
+    const int64_t Lkv = p.Lkv;   // rows per batch entry of k and v
     const int Hq = (int)p.Hq;
     const int Hkv = (int)p.Hkv;
     const int G = (int)p.G;
     const int w0 = (int)p.w0;
     const int R = p.R;
     const int BQ = p.BQ;
-    const int q0 = qt * BQ;
+    const int q0 = q_off + qt * BQ;
     const int q_hi = min(q0 + BQ, L) - 1;
     const float scale2 = p.sm_scale_log2;
 
@@ -147,12 +151,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const float2* __restrict__ TF = p.TF;
     const int64_t kv_row = (int64_t)Hkv * D;
     const uint32_t row_bytes = (uint32_t)kv_row * 2u;
-    const __bf16* __restrict__ kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * L * kv_row + (int64_t)g * D;
-    const __bf16* __restrict__ vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * L * kv_row + (int64_t)g * D;
-    // keys in their corrected view (only read by remote tiles, which exist only when G > 1)
+    const __bf16* __restrict__ kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * Lkv * kv_row + (int64_t)g * D;
+    const __bf16* __restrict__ vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * Lkv * kv_row + (int64_t)g * D;
+    // keys in their corrected view (only read by remote tiles, which exist only
+    // when G > 1), laid out like k with L rows per batch entry
     const __bf16* __restrict__ krbase =
-        (G > 1 ? static_cast<const __bf16*>(p.krot) : static_cast<const __bf16*>(p.k)) + (int64_t)b * L * kv_row +
-        (int64_t)g * D;
+        G > 1 ? static_cast<const __bf16*>(p.krot) + (int64_t)b * L * kv_row + (int64_t)g * D : kbase;
 
     if (tid == 0) {
         const TableHeader* th = p.table;
@@ -165,12 +169,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             if (!qok[j]) continue;
-            const int64_t o = (((int64_t)b * L + my_q[j]) * Hq + head[j]) * D;
+            const int64_t o = (((int64_t)b * Lq + (my_q[j] - q_off)) * Hq + head[j]) * D;
             for (int d = hh; d < D; d += 2) {
                 if constexpr (OUT_BF16) static_cast<__bf16*>(p.out)[o + d] = (__bf16)NAN;
                 else static_cast<float*>(p.out)[o + d] = NAN;
             }
-            if (hh == 0 && p.lse) p.lse[((int64_t)b * Hq + head[j]) * L + my_q[j]] = NAN;
+            if (hh == 0 && p.lse) p.lse[((int64_t)b * Hq + head[j]) * Lq + (my_q[j] - q_off)] = NAN;
         }
         return;
     }
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int qpos = min(my_q[j], L - 1);
-            const __bf16* qrow = qg + (((int64_t)b * L + qpos) * Hq + head[j]) * D;
+            const __bf16* qrow = qg + (((int64_t)b * Lq + (qpos - q_off)) * Hq + head[j]) * D;
             bf16x8 raw[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c) raw[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * hh);
@@ -493,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             for (int i = 0; i < 16; ++i) finite = finite && fabsf(acc[j][db][i] * inv) < INFINITY;
         const bool row_ok = finite && __shfl_xor((int)finite, 32);
         if (!qok[j]) continue;
-        const int64_t o = (((int64_t)b * L + my_q[j]) * Hq + head[j]) * D;
+        const int64_t o = (((int64_t)b * Lq + (my_q[j] - q_off)) * Hq + head[j]) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             }
         }
         if (hh == 0 && p.lse)
-            p.lse[((int64_t)b * Hq + head[j]) * L + my_q[j]] = (m_ref[j] + log2f(l_tot)) * 0.69314718055994531f;
+            p.lse[((int64_t)b * Hq + head[j]) * Lq + (my_q[j] - q_off)] = (m_ref[j] + log2f(l_tot)) * 0.69314718055994531f;
     }
 }
 
@@ -527,16 +531,18 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 template <int D>
 __global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kr,
                                                           const float2* __restrict__ TF, int64_t n_items, int64_t L,
-                                                          int Hkv, int64_t G) {
+                                                          int64_t Lkv, int Hkv, int64_t G) {
     constexpr int HALF = D / 2;
     constexpr int CPR = HALF / 8;   // 8-pair items per row
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= n_items) return;
-    const int64_t row = t / CPR;    // (b, position, head), head fastest
+    const int64_t row = t / CPR;    // (b, position, head) of the output, head fastest
     const int c = (int)(t % CPR);
-    const int64_t pos = (row / Hkv) % L;
+    const int64_t bp = row / Hkv;
+    const int64_t pos = bp % L;
     const int64_t n = pos - pos / G;
-    const __bf16* src = k + row * D + 8 * c;
+    // k holds Lkv rows per batch entry, the output L
+    const __bf16* src = k + (((bp / L) * Lkv + pos) * Hkv + row % Hkv) * D + 8 * c;
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(src);
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(src + HALF);
     const float4* cs = reinterpret_cast<const float4*>(TF + n * HALF + 8 * c);
@@ -564,7 +570,7 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
         const int64_t n_items = p.B * p.L * p.Hkv * (D / 16);
         hipLaunchKernelGGL((rotate_keys_kernel<D>), dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0, stream,
                            static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.krot), p.TF, n_items, p.L,
-                           (int)p.Hkv, p.G);
+                           p.Lkv, (int)p.Hkv, p.G);
     }
     const int64_t blocks = (int64_t)p.n_qtiles * p.Hkv * p.B;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
