@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query rows in the CPU-oracle sample")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--control-steps", type=int, default=5,
+                    help="timed calls of the matched control (same inputs, every pair local); 0 skips it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 512 MiB device-to-device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -119,6 +121,34 @@ def bench_prefill(torch, jl, si, args, w, x):
     del q, k, v, out, lse
     torch.cuda.empty_cache()
     return ms, tflops, flops, stats
+
+
+def bench_control(torch, jl, args, w, x):
+    """The matched control: the same kernel on the same inputs with
+    w_pretrained = L, so G = 1 and every pair is local (plain causal
+    attention: no remote view, no rotation pre-pass, no window edge)."""
+    q, k, v = (to_dev(torch, x[n], w.dtype) for n in "qkv")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device="cuda")
+    table = jl.alloc_table(w.L, w.D, w.rope_base)
+
+    def step():
+        jl.jl_bifocal_prefill(q, k, v, out, lse, w.w0, w.L, w.rope_base, w.sm_scale, table)
+
+    step()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.control_steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.control_steps
+    log(f"[bench] matched control (G=1) {ms:.3f} ms/call")
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return ms
 
 
 def bench_decode(torch, jl, si, args):
@@ -240,6 +270,12 @@ def main():
                      "flops_per_launch": flops},
         "prefill_ms_per_call": pstats,
     }
+    if args.control_steps > 0:
+        cms = bench_control(torch, jl, args, w, x)
+        result["matched_control"] = {
+            "what": "same kernel and inputs with w_pretrained = L (G = 1, every pair local)",
+            "ms_per_call": round(cms, 4), "tflops": round(flops / (cms * 1e-3) / 1e12, 2),
+            "bifocal_over_control": round(cms / ms, 4)}
     if not args.skip_decode:
         dw, us, gbs, bytes_step, us_median = bench_decode(torch, jl, si, args)
         result["decode"] = {

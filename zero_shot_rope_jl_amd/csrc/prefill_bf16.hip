@@ -35,10 +35,9 @@
 //   operand of O^T += V^T P^T, whose V^T operand comes from row-major V
 //   through ds_read_b64_tr_b16.  Q is pre-multiplied by sm_scale * log2(e).
 //   Each row's reference max m is fixed (rounded to bf16) at the first tile
-//   that gives it a key and never moved; the score MFMA chain subtracts it
-//   through one extra rank-1 step (a constant K chunk of ones against a Q
-//   chunk holding -m), so P = exp2(S) needs no per-element subtraction and
-//   the accumulators are touched by MFMAs only.  Probabilities above 1 are
+//   that gives it a key and never moved; each score MFMA chain starts from
+//   -m as its accumulator input, so P = exp2(S) needs no per-element
+//   subtraction and the accumulators are touched by MFMAs only.  Probabilities above 1 are
 //   harmless (fp32 and bf16 share the exponent range; the final division
 //   restores the scale).
 #include <limits.h>
@@ -274,21 +273,20 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 
     // ---- softmax state -------------------------------------------------------------
     // m_ref: the row's reference max (log2 units, a bf16 value), -inf until the
-    // row meets its first key; qx holds -m_ref as the extra B chunk of the
-    // score MFMA; l_run: row sum of probabilities.
+    // row meets its first key; negm: -m_ref (0 while unset) in every element,
+    // the accumulator input of each score chain's first MFMA, which so
+    // subtracts the reference at no cost; l_run: row sum of probabilities.
     f32x16 acc[NJ][NDB];
     float m_ref[NJ], l_run[NJ];
-    bf16x8 qx[NJ];
+    f32x16 negm[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[j][db] = f32x16{};
         m_ref[j] = -INFINITY;
         l_run[j] = 0.f;
-        qx[j] = bf16x8{};
+        negm[j] = f32x16{};
     }
-    bf16x8 kone = bf16x8{};
-    if (hh == 0) kone[0] = (__bf16)1.0f;
 
     // K A-operand row of this lane in each 32-key block (sigma makes the C
     // rows land so that P^T feeds the PV MFMA in natural key order)
@@ -301,21 +299,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const int tr_dim = 16 * (Gq & 1) + 4 * (cq & 3);
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // S^T - m_ref for one 32-key half, every query block of the wave (each K
-    // fragment feeds all of them); the last step adds the rank-1 term
-    // ones x (-m_ref).
+    // S^T - m_ref for one 32-key block, every query block of the wave (each K
+    // fragment feeds all of them); the chain starts from -m_ref.
     auto qk = [&](const __bf16* K, int kb, f32x16 (&s)[NJ]) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) s[j] = f32x16{};
         const __bf16* kp = K + (32 * kb + krow_l) * KSTR + 8 * hh;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const bf16x8 A = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[j][c], s[j], 0, 0, 0);
+            for (int j = 0; j < NJ; ++j)
+                s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[j][c], c == 0 ? negm[j] : s[j], 0, 0, 0);
         }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, qx[j], s[j], 0, 0, 0);
     };
     // O^T += V^T P^T for one 32-key half; each V^T fragment feeds every block.
     auto pv = [&](const __bf16* V, int kb, const bf16x8 (&P)[NJ][2]) {
@@ -399,7 +393,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[j][i] -= d;
             m_ref[j] = first ? mb : m_ref[j];
-            qx[j][0] = (hh == 0 && m_ref[j] != -INFINITY) ? (__bf16)(-m_ref[j]) : (__bf16)0.0f;
+            const float nm = m_ref[j] != -INFINITY ? -m_ref[j] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) negm[j][i] = nm;
         }
     };
 
