@@ -56,8 +56,9 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads: a tiny fp32 case, the identity regime at L = w_pre,
-# two extension prefills (G = 2 and G = 4) and a 128K decode.
+# The workloads: a tiny fp32 case, the identity regime at L = w_pre,
+# extension prefills at 64K (G = 2), 128K (G = 4) and 1M (G = 4), and a
+# 128K decode.
 WORKLOADS = {
     "tiny": Workload("tiny", "f32", 1, 512, 4, 2, 64, 64, 256, 1.0e4, 1001),
     "identity32k": Workload("identity32k", "bf16", 1, 32768, 16, 8, 128, 4096,
@@ -66,6 +67,10 @@ WORKLOADS = {
                        1.0e6, 1003, channel_scale=True),
     "ext128k": Workload("ext128k", "bf16", 1, 131072, 32, 8, 128, 4096, 32768,
                         1.0e6, 1004),
+    # a 256K-native model extended 4x to 1M tokens (G = 4), one KV head and
+    # its 4 query heads: one GPU's share of an 8-KV-head model split by head
+    "ext1m": Workload("ext1m", "bf16", 1, 1048576, 4, 1, 128, 4096, 262144,
+                      1.0e6, 1006),
 }
 
 
