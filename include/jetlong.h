@@ -198,6 +198,35 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
                       size_t workspace_bytes, void* hip_stream);
 
 /*
+ * jl_bifocal_decode_paged -- jl_bifocal_decode over a paged cache (a block
+ * table maps each sequence's positions to fixed-size pages, as serving
+ * engines keep their caches).
+ *
+ *   k_pages, v_pages [n_pages, page_size, Hkv, D]  bf16
+ *   block_table      [B, max_pages] int32 (device): key position p of
+ *                    sequence b is row p % page_size of page
+ *                    block_table[b * max_pages + p / page_size]
+ *
+ * page_size must be a positive multiple of 32 and max_pages * page_size >=
+ * L; the pages that cover positions 0..L-1 must be written, the new token's
+ * row included.  Everything else as for jl_bifocal_decode (one L for every
+ * sequence of the batch).  A page index outside [0, n_pages) is not followed:
+ * the kernel reads page 0 in its place and writes NaN for that sequence's
+ * heads.
+ *
+ * Errors: as for jl_bifocal_decode, plus JL_EINVAL for a NULL or misaligned
+ * block_table, a page_size that is not a positive multiple of 32, n_pages < 1
+ * or max_pages * page_size < L.
+ */
+JL_API int jl_bifocal_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int32_t* block_table, void* out, float* lse, int in_dtype,
+                            int out_dtype, int64_t B, int64_t L, int64_t n_pages, int64_t page_size,
+                            int64_t max_pages, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                            int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
+                            size_t table_bytes, void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+
+/*
  * jl_table_fill_host -- fill a HOST buffer with the same table jl_schedule
  * writes on the device (same layout, same float64 formulas compiled for the
  * host).  Lets the table builder be checked without a GPU.  Errors as for

@@ -25,10 +25,10 @@ def test_exports_every_declared_symbol():
     syms = header_symbols()
     assert syms == sorted(["jl_last_error", "jl_version", "jl_schedule", "jl_bifocal_prefill_workspace",
                            "jl_bifocal_prefill", "jl_bifocal_prefill_chunk", "jl_bifocal_decode_workspace",
-                           "jl_bifocal_decode", "jl_table_fill_host"])
+                           "jl_bifocal_decode", "jl_bifocal_decode_paged", "jl_table_fill_host"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 3
+    assert jl.jl_version() == 4
 
 
 def test_schedule_golden_and_table_size():
@@ -144,6 +144,28 @@ def _decode(**over):
 ])
 def test_decode_validation(over, code):
     assert _decode(**over) == code
+    assert jl.jl_last_error()
+
+
+def _paged(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=2, L=600,
+             n_pages=40, ps=64, mp=10, Hq=8, Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE,
+             tb=1 << 30, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_decode_paged(a["q"], a["k"], a["v"], a["bt"], a["out"], a["lse"], a["i"], a["o"],
+                                          a["B"], a["L"], a["n_pages"], a["ps"], a["mp"], a["Hq"], a["Hkv"],
+                                          a["D"], a["w0"], a["wp"], a["base"], a["sc"], a["table"], a["tb"],
+                                          a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(bt=None), jl.JL_EINVAL), (dict(bt=FAKE + 2), jl.JL_EINVAL), (dict(ps=48), jl.JL_EINVAL),
+    (dict(ps=0), jl.JL_EINVAL), (dict(mp=9), jl.JL_EINVAL), (dict(n_pages=0), jl.JL_EINVAL),
+    (dict(i=jl.JL_F32, o=jl.JL_F32), jl.JL_EUNSUPPORTED), (dict(wsb=16), jl.JL_ESPACE),
+    (dict(k=None), jl.JL_EINVAL), (dict(D=96), jl.JL_EUNSUPPORTED),
+])
+def test_decode_paged_validation(over, code):
+    assert _paged(**over) == code
     assert jl.jl_last_error()
 
 

@@ -54,6 +54,10 @@ def _load():
     L.jl_bifocal_decode.restype = ctypes.c_int
     L.jl_bifocal_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                     i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
+    L.jl_bifocal_decode_paged.restype = ctypes.c_int
+    L.jl_bifocal_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                          i64, i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz,
+                                          vp, sz, vp]
     return L
 
 
@@ -249,4 +253,28 @@ def jl_bifocal_decode(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrain
                                  w_pretrained, rope_base, sm_scale, _ptr(table),
                                  table.numel() * table.element_size(), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def jl_bifocal_decode_paged(q, k_pages, v_pages, block_table, out, lse, L: int, w0: int, w_pretrained: int,
+                            rope_base: float, sm_scale: float, table, workspace, stream=None):
+    """q [B,1,Hq,D] bf16; pages [n_pages, page_size, Hkv, D] bf16; block_table [B, max_pages] int32;
+    out [B,1,Hq,D]; lse [B,Hq] or None."""
+    torch = _torch()
+    _need_device(q, k_pages, v_pages, block_table, out, lse, table, workspace)
+    B, one, Hq, D = q.shape
+    n_pages, page_size, Hkv, Dk = k_pages.shape
+    if one != 1 or Dk != D or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("q must be [B,1,Hq,D] and the pages [n_pages, page_size, Hkv, D]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if tuple(out.shape) != (B, 1, Hq, D):
+        raise ValueError("out must be [B, 1, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq]")
+    _check(lib.jl_bifocal_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(out),
+                                       _ptr(lse), _dtype_code(q), _dtype_code(out), B, L, n_pages, page_size,
+                                       block_table.shape[1], Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale,
+                                       _ptr(table), table.numel() * table.element_size(), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse

@@ -67,7 +67,7 @@ extern "C" {
 
 JL_API const char* jl_last_error(void) { return g_err.c_str(); }
 
-JL_API int jl_version(void) { return 3; }
+JL_API int jl_version(void) { return 4; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -213,22 +213,39 @@ JL_API int jl_bifocal_decode_workspace(int64_t B, int64_t Hq, int64_t D, int64_t
     return JL_OK;
 }
 
-JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
-                             int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq,
-                             int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained, double rope_base,
-                             float sm_scale, const void* table, size_t table_bytes, void* workspace,
-                             size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points.  Contiguous cache: block_table == NULL, k/v
+// [B, Lmax, Hkv, D].  Paged cache: k/v [n_pages, page_size, Hkv, D] and
+// block_table [B, max_pages].
+int decode_impl(const char* who, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                int64_t page_size, int64_t max_pages, int64_t n_pages, void* out, float* lse, int in_dtype,
+                int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                int64_t w_pretrained, double rope_base, float sm_scale, const void* table, size_t table_bytes,
+                void* workspace, size_t workspace_bytes, void* hip_stream) {
     g_err.clear();
     if (!q || !k_cache || !v_cache || !out || !table || !workspace)
-        return fail(JL_EINVAL, "q, k_cache, v_cache, out, table and workspace must be non-NULL");
+        return fail(JL_EINVAL, "%s: q, the caches, out, table and workspace must be non-NULL", who);
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(table) ||
         !aligned16(workspace) || !aligned16(lse))
-        return fail(JL_EINVAL, "device pointers must be 16-byte aligned");
+        return fail(JL_EINVAL, "%s: device pointers must be 16-byte aligned", who);
     if (int rc = check_attention_common(B, L, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, in_dtype,
                                         out_dtype))
         return rc;
-    if (Lmax < L || Lmax > kMaxLen)
+    if (block_table) {
+        if (reinterpret_cast<uintptr_t>(block_table) & 3u)
+            return fail(JL_EINVAL, "%s: block_table must be 4-byte aligned", who);
+        if (page_size < 32 || page_size % 32 != 0 || page_size > kMaxLen)
+            return fail(JL_EINVAL, "%s: page_size must be a positive multiple of 32 (got %lld)", who,
+                        (long long)page_size);
+        if (n_pages < 1 || max_pages < 1 || max_pages * page_size < L)
+            return fail(JL_EINVAL, "%s: need n_pages >= 1 and max_pages * page_size >= L (%lld, %lld, L=%lld)",
+                        who, (long long)n_pages, (long long)max_pages, (long long)L);
+    } else if (Lmax < L || Lmax > kMaxLen) {
         return fail(JL_EINVAL, "need L <= Lmax <= 2^30 (L=%lld, Lmax=%lld)", (long long)L, (long long)Lmax);
+    }
     if (in_dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "decode reads a bf16 cache only");
     const int64_t R = Hq / Hkv;
     if (R != 1 && R != 2 && R != 4 && R != 8 && R != 16)
@@ -255,7 +272,11 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
     p.TF = reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes);
     p.B = B;
     p.L = L;
-    p.Lmax = Lmax;
+    p.Lmax = block_table ? 0 : Lmax;
+    p.block_table = block_table;
+    p.page_size = page_size;
+    p.max_pages = max_pages;
+    p.n_pages = n_pages;
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.R = (int)R;
@@ -268,8 +289,37 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
     p.head_dim = (int)D;
     (void)hipGetLastError();
     hipError_t e = jl::launch_decode(p, out_dtype, static_cast<hipStream_t>(hip_stream));
-    if (e != hipSuccess) return fail(JL_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
     return JL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                             int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq,
+                             int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained, double rope_base,
+                             float sm_scale, const void* table, size_t table_bytes, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+    return decode_impl("decode", q, k_cache, v_cache, nullptr, 0, 0, 0, out, lse, in_dtype, out_dtype, B, L, Lmax,
+                       Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
+                       workspace_bytes, hip_stream);
+}
+
+JL_API int jl_bifocal_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                                   const int32_t* block_table, void* out, float* lse, int in_dtype, int out_dtype,
+                                   int64_t B, int64_t L, int64_t n_pages, int64_t page_size, int64_t max_pages,
+                                   int64_t Hq, int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained,
+                                   double rope_base, float sm_scale, const void* table, size_t table_bytes,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!block_table) {
+        g_err.clear();
+        return fail(JL_EINVAL, "decode_paged: block_table must be non-NULL");
+    }
+    return decode_impl("decode_paged", q, k_pages, v_pages, block_table, page_size, max_pages, n_pages, out, lse,
+                       in_dtype, out_dtype, B, L, 0, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table,
+                       table_bytes, workspace, workspace_bytes, hip_stream);
 }
 
 }  // extern "C"

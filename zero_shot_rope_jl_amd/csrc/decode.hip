@@ -57,44 +57,46 @@ struct DecodeTile {
 // Cache reads are non-temporal: every byte is read once per step, and the
 // streaming hint gave ~13% more read bandwidth for this access shape than
 // ordinary loads.
+// `rbase` is the cache row of key kbase; the 32 keys of a step occupy the
+// consecutive rows from there (a page holds a multiple of 32 keys).
 template <int D>
 __device__ inline void load_k_blk(DecodeTile<D>& t, const __bf16* __restrict__ kc, int64_t cache_b, int64_t row,
-                                  int kbase, int kend, int colh, int gq, int blk) {
+                                  int kbase, int64_t rbase, int kend, int colh, int gq, int blk) {
     constexpr int NC = DecodeTile<D>::NC;
     // A-operand row colh of block blk holds key 8*(colh/4) + 4*blk + colh%4:
     // C rows then give P^T slots in natural key order
-    const int key = kbase + 8 * (colh >> 2) + 4 * blk + (colh & 3);
-    const bool ok = key < kend;
+    const int dk = 8 * (colh >> 2) + 4 * blk + (colh & 3);
+    const bool ok = kbase + dk < kend;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
         t.k[blk][c] = ok ? __builtin_nontemporal_load(
-                               reinterpret_cast<const bf16x8*>(kc + cache_b + (int64_t)key * row + 32 * c + 8 * gq))
+                               reinterpret_cast<const bf16x8*>(kc + cache_b + (rbase + dk) * row + 32 * c + 8 * gq))
                          : bf16x8{};
 }
 
 template <int D>
 __device__ inline void load_k(DecodeTile<D>& t, const __bf16* __restrict__ kc, int64_t cache_b, int64_t row,
-                              int kbase, int kend, int colh, int gq) {
+                              int kbase, int64_t rbase, int kend, int colh, int gq) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) load_k_blk<D>(t, kc, cache_b, row, kbase, kend, colh, gq, blk);
+    for (int blk = 0; blk < 2; ++blk) load_k_blk<D>(t, kc, cache_b, row, kbase, rbase, kend, colh, gq, blk);
 }
 
 template <int D>
 __device__ inline void load_v(DecodeTile<D>& t, const __bf16* __restrict__ vc, int64_t cache_b, int64_t row,
-                              int kbase, int kend, int lane) {
+                              int kbase, int64_t rbase, int kend, int lane) {
     constexpr int KPL = DecodeTile<D>::KPL;
     const int dg = lane % (D / 8);
     const int kg = lane / (D / 8);
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
-        const int key = kbase + kg * KPL + e;
-        t.v[e] = key < kend
-                     ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(vc + cache_b + (int64_t)key * row + dg * 8))
+        const int dk = kg * KPL + e;
+        t.v[e] = kbase + dk < kend
+                     ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(vc + cache_b + (rbase + dk) * row + dg * 8))
                      : bf16x8{};
     }
 }
 
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, bool PAGED>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeParams p) {
     constexpr int HALF = D / 2;
     constexpr int NC = D / 32;
@@ -135,7 +137,26 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const __bf16* __restrict__ vc = static_cast<const __bf16*>(p.v);
     const float2* __restrict__ TF = p.TF;
     const int64_t row = p.Hkv * D;
-    const int64_t cache_b = (int64_t)b * p.Lmax * row + (int64_t)g * D;
+    const int64_t cache_b = PAGED ? (int64_t)g * D : (int64_t)b * p.Lmax * row + (int64_t)g * D;
+
+    // Cache row of key kb (a multiple of 32).  Paged: the page comes from
+    // the block table; an index outside [0, n_pages) reads page 0 instead
+    // and marks the result, so no load leaves the pages.
+    bool bad_page = false;
+    auto row_of = [&](int kb) -> int64_t {
+        if constexpr (!PAGED) {
+            return kb;
+        } else {
+            const int64_t ps = p.page_size;
+            const int64_t slot = kb / ps;
+            int64_t pg = p.block_table[(int64_t)b * p.max_pages + slot];
+            if (pg < 0 || pg >= p.n_pages) {
+                bad_page = true;
+                pg = 0;
+            }
+            return pg * ps + (kb - slot * ps);
+        }
+    };
 
     // the first step's K and V go out before anything else (the set-up below
     // waits on the table and q); they stay within the cache whatever the
@@ -143,9 +164,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const int wstart = (split * NW + sub) * p.wave_chunk;
     const int wend0 = min(L, wstart + p.wave_chunk);
     DecodeTile<D> cur;
+    int64_t r_next = 0;   // cache row of the next step's first key
     if (wstart < wend0) {
-        load_k<D>(cur, kc, cache_b, row, wstart, wend0, colh, gq);
-        load_v<D>(cur, vc, cache_b, row, wstart, wend0, lane);
+        const int64_t r0 = row_of(wstart);
+        load_k<D>(cur, kc, cache_b, row, wstart, r0, wend0, colh, gq);
+        load_v<D>(cur, vc, cache_b, row, wstart, r0, wend0, lane);
+        if (wstart + kWaveKeys < wend0) r_next = row_of(wstart + kWaveKeys);
     }
 
     if (tid == 0) {
@@ -228,6 +252,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     // compute.
     for (int kbase = wstart; kbase < wend; kbase += kWaveKeys) {
         const int knext = kbase + kWaveKeys;
+        // the step after next: its page is looked up a step ahead
+        const int64_t r_after = knext + kWaveKeys < wend ? row_of(knext + kWaveKeys) : 0;
         // ---- V rows -> V^T in this wave's LDS slice --------------------------
         {
             const int dg = lane % (D / 8);
@@ -242,7 +268,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
             }
         }
         // V registers are free: start the next step's V loads
-        if (knext < wend) load_v<D>(cur, vc, cache_b, row, knext, wend, lane);
+        if (knext < wend) load_v<D>(cur, vc, cache_b, row, knext, r_next, wend, lane);
 
         const bool w_loc = (G == 1) || (kbase + kWaveKeys - 1 >= kloc);
         const bool w_rem = (G > 1) && (kbase < kloc);
@@ -281,7 +307,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
                 s[blk][i] = kk < wend ? v * scale2 : -INFINITY;
             }
             // this half's K registers are free: start the next step's loads
-            if (knext < wend) load_k_blk<D>(cur, kc, cache_b, row, knext, wend, colh, gq, blk);
+            if (knext < wend) load_k_blk<D>(cur, kc, cache_b, row, knext, r_next, wend, colh, gq, blk);
         }
 
         // ---- online softmax per head column: 8 values here, 4 quads per head --
@@ -324,7 +350,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         // the next step's corrected query, computed here so that it is off the
         // path from K's arrival to the next K loads
         if (G > 1 && knext < wend && knext < kloc) rotate_query(knext);
+        r_next = r_after;
     }
+    if (bad_page) l_run = NAN;   // poisons this head's output through the merge
 
     // ---- merge the NW waves of each head, write this split's partials -------
     float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -440,8 +468,9 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeParams p) {
 
 template <int D, bool OUT_BF16>
 hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16>), dim3(p.n_split, p.Hkv / p.heads_per_wg, p.B),
-                       dim3(kDecThreads), 0, stream, p);
+    const dim3 grid(p.n_split, p.Hkv / p.heads_per_wg, p.B);
+    if (p.block_table) hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, true>), grid, dim3(kDecThreads), 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false>), grid, dim3(kDecThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(p.Hq, p.B, D / 32), dim3(1024), 0, stream, p);

@@ -46,6 +46,11 @@ struct DecodeParams {
     const TableHeader* table;
     const float2* TF;   // (cos, sin)(n theta_i) rows, n < coverage
     int64_t B, L, Lmax, Hq, Hkv;
+    // paged cache (block_table non-NULL): k/v are [n_pages, page_size, Hkv, D]
+    // and key p of sequence b is row p % page_size of page
+    // block_table[b * max_pages + p / page_size]; page_size is a multiple of 32
+    const int32_t* block_table;
+    int64_t page_size, max_pages, n_pages;
     int R;
     int n_split;        // workgroups per (batch, KV-head group)
     int wave_chunk;     // consecutive keys per wave (multiple of 32)
