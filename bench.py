@@ -66,8 +66,9 @@ def measured_traffic():
         return {}
 
 
-def pick(traffic, prefix):
-    hits = [v for k, v in traffic.items() if k.startswith(prefix)]
+def pick(traffic, *prefixes):
+    """Summed bytes per dispatch of the kernels whose names start with any of the prefixes."""
+    hits = [v for k, v in traffic.items() if k.startswith(prefixes)]
     return sum(hits) if hits else None
 
 
@@ -197,13 +198,41 @@ def bench_decode(torch, jl, si, args):
         evs[s + 1].record(stream)
     torch.cuda.synchronize()
     us_median = float(np.median([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(dw.steps)]))
+
+    # the same steps over the cache held in shuffled 256-key pages
+    ps = 256
+    max_pages = (dw.Lmax + ps - 1) // ps
+    perm = np.random.Generator(np.random.PCG64([dw.seed, 17])).permutation(dw.B * max_pages)
+    kp = torch.zeros((dw.B * max_pages, ps, dw.Hkv, dw.D), dtype=kc.dtype, device="cuda")
+    vp = torch.zeros_like(kp)
+    for b in range(dw.B):
+        for s in range(max_pages):
+            rows = slice(s * ps, min((s + 1) * ps, dw.Lmax))
+            kp[int(perm[b * max_pages + s]), : rows.stop - rows.start] = kc[b, rows]
+            vp[int(perm[b * max_pages + s]), : rows.stop - rows.start] = vc[b, rows]
+    bt = torch.from_numpy(perm.reshape(dw.B, max_pages).astype(np.int32)).cuda()
+
+    def paged_pass():
+        for s in range(dw.steps):
+            L = dw.prompt_len + s + 1
+            jl.jl_bifocal_decode_paged(qs[s], kp, vp, bt, out, None, L, dw.w0, dw.w_pretrained, dw.rope_base,
+                                       dw.sm_scale, table, ws)
+
+    paged_pass()
+    ev0.record(stream)
+    paged_pass()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_paged = ev0.elapsed_time(ev1) * 1e3 / dw.steps
+    del kp, vp
     mean_L = dw.prompt_len + (dw.steps + 1) / 2.0
     bytes_step = 2.0 * dw.B * mean_L * dw.Hkv * dw.D * 2
     gbs = bytes_step / (us * 1e-6) / 1e9
-    log(f"[bench] decode {us:.2f} us/step (per-step median {us_median:.2f}), {gbs:.0f} GB/s")
+    log(f"[bench] decode {us:.2f} us/step (per-step median {us_median:.2f}, paged cache {us_paged:.2f}), "
+        f"{gbs:.0f} GB/s")
     del kc, vc
     torch.cuda.empty_cache()
-    return dw, us, gbs, bytes_step, us_median
+    return dw, us, gbs, bytes_step, us_median, us_paged
 
 
 def cpu_baseline(si, w, x, n_rows):
@@ -277,13 +306,15 @@ def main():
             "ms_per_call": round(cms, 4), "tflops": round(flops / (cms * 1e-3) / 1e12, 2),
             "bifocal_over_control": round(cms / ms, 4)}
     if not args.skip_decode:
-        dw, us, gbs, bytes_step, us_median = bench_decode(torch, jl, si, args)
+        dw, us, gbs, bytes_step, us_median, us_paged = bench_decode(torch, jl, si, args)
         result["decode"] = {
-            "us_per_step": round(us, 3), "us_per_step_median": round(us_median, 3), "unit": "µs/step",
+            "us_per_step": round(us, 3), "us_per_step_median": round(us_median, 3),
+            "us_per_step_paged_256": round(us_paged, 3), "unit": "µs/step",
             "steps_timed": args.decode_passes * dw.steps,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": pick(traffic, "jl::decode_"),
+                         "traffic": pick(traffic, "jl::decode_split_kernel<128, true, false>",
+                                         "jl::decode_combine_kernel"),
                          "bytes_per_step": bytes_step},
         }
     if not args.no_cpu_baseline:
