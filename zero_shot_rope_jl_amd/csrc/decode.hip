@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: key ranges and pages in SGPRs
     const int colh = lane & 15;   // MFMA column = query head within the group
     const int gq = lane >> 4;     // lane quad
 
@@ -139,24 +139,34 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const int64_t row = p.Hkv * D;
     const int64_t cache_b = PAGED ? (int64_t)g * D : (int64_t)b * p.Lmax * row + (int64_t)g * D;
 
-    // Cache row of key kb (a multiple of 32).  Paged: the page comes from
-    // the block table; an index outside [0, n_pages) reads page 0 instead
-    // and marks the result, so no load leaves the pages.
+    // Cache row of key kb (a multiple of 32), in two parts so that the
+    // block-table read can be issued well before its value is needed:
+    // page_of reads the entry, row_in turns it into a row.  An entry outside
+    // [0, n_pages) reads page 0 instead and marks the result, so no load
+    // leaves the pages.  Contiguous caches: the row is kb.
+    // The table is read through the constant address space (it is not
+    // written during the kernel) so that its reads are scalar loads, whose
+    // wait does not drain the cache loads in flight.
     bool bad_page = false;
-    auto row_of = [&](int kb) -> int64_t {
+    const int ps = PAGED ? (int)p.page_size : 1;
+    const __attribute__((address_space(4))) int32_t* btab =
+        (const __attribute__((address_space(4))) int32_t*)(p.block_table + (int64_t)b * p.max_pages);
+    auto page_of = [&](int kb) -> int {
+        if constexpr (!PAGED) return 0;
+        else return btab[kb / ps];
+    };
+    auto row_in = [&](int pg, int kb) -> int64_t {
         if constexpr (!PAGED) {
             return kb;
         } else {
-            const int64_t ps = p.page_size;
-            const int64_t slot = kb / ps;
-            int64_t pg = p.block_table[(int64_t)b * p.max_pages + slot];
             if (pg < 0 || pg >= p.n_pages) {
                 bad_page = true;
                 pg = 0;
             }
-            return pg * ps + (kb - slot * ps);
+            return (int64_t)pg * ps + kb % ps;
         }
     };
+    auto row_of = [&](int kb) -> int64_t { return row_in(page_of(kb), kb); };
 
     // the first step's K and V go out before anything else (the set-up below
     // waits on the table and q); they stay within the cache whatever the
@@ -165,11 +175,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const int wend0 = min(L, wstart + p.wave_chunk);
     DecodeTile<D> cur;
     int64_t r_next = 0;   // cache row of the next step's first key
+    int pg_ahead = 0;     // block-table entry of the step after next
     if (wstart < wend0) {
         const int64_t r0 = row_of(wstart);
         load_k<D>(cur, kc, cache_b, row, wstart, r0, wend0, colh, gq);
         load_v<D>(cur, vc, cache_b, row, wstart, r0, wend0, lane);
         if (wstart + kWaveKeys < wend0) r_next = row_of(wstart + kWaveKeys);
+        if (wstart + 2 * kWaveKeys < wend0) pg_ahead = page_of(wstart + 2 * kWaveKeys);
     }
 
     if (tid == 0) {
@@ -252,8 +264,6 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     // compute.
     for (int kbase = wstart; kbase < wend; kbase += kWaveKeys) {
         const int knext = kbase + kWaveKeys;
-        // the step after next: its page is looked up a step ahead
-        const int64_t r_after = knext + kWaveKeys < wend ? row_of(knext + kWaveKeys) : 0;
         // ---- V rows -> V^T in this wave's LDS slice --------------------------
         {
             const int dg = lane % (D / 8);
@@ -350,7 +360,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         // the next step's corrected query, computed here so that it is off the
         // path from K's arrival to the next K loads
         if (G > 1 && knext < wend && knext < kloc) rotate_query(knext);
-        r_next = r_after;
+        // rows of the step after next (its table entry was read a step ago);
+        // then the table entry of the step after that
+        r_next = knext + kWaveKeys < wend ? row_in(pg_ahead, knext + kWaveKeys) : 0;
+        if (PAGED && knext + 2 * kWaveKeys < wend) pg_ahead = page_of(knext + 2 * kWaveKeys);
     }
     if (bad_page) l_run = NAN;   // poisons this head's output through the merge
 
