@@ -225,14 +225,32 @@ def bench_decode(torch, jl, si, args):
     torch.cuda.synchronize()
     us_paged = ev0.elapsed_time(ev1) * 1e3 / dw.steps
     del kp, vp
+
+    # the 256 contiguous-cache steps captured once as a HIP graph and replayed;
+    # the replay's last output must equal the eager pass's bit for bit
+    one_pass()
+    eager_out = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    graph.replay()
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_graph = ev0.elapsed_time(ev1) * 1e3 / dw.steps
+    graph_ok = bool(torch.equal(out, eager_out))
+    del graph
     mean_L = dw.prompt_len + (dw.steps + 1) / 2.0
     bytes_step = 2.0 * dw.B * mean_L * dw.Hkv * dw.D * 2
     gbs = bytes_step / (us * 1e-6) / 1e9
-    log(f"[bench] decode {us:.2f} us/step (per-step median {us_median:.2f}, paged cache {us_paged:.2f}), "
-        f"{gbs:.0f} GB/s")
+    log(f"[bench] decode {us:.2f} us/step (per-step median {us_median:.2f}, paged cache {us_paged:.2f}, "
+        f"graph {us_graph:.2f}{'' if graph_ok else ' MISMATCH'}), {gbs:.0f} GB/s")
     del kc, vc
     torch.cuda.empty_cache()
-    return dw, us, gbs, bytes_step, us_median, us_paged
+    return dw, us, gbs, bytes_step, us_median, {"us_per_step_paged_256": round(us_paged, 3),
+                                               "us_per_step_graph": round(us_graph, 3),
+                                               "graph_matches_eager": graph_ok}
 
 
 def cpu_baseline(si, w, x, n_rows):
@@ -306,10 +324,9 @@ def main():
             "ms_per_call": round(cms, 4), "tflops": round(flops / (cms * 1e-3) / 1e12, 2),
             "bifocal_over_control": round(cms / ms, 4)}
     if not args.skip_decode:
-        dw, us, gbs, bytes_step, us_median, us_paged = bench_decode(torch, jl, si, args)
+        dw, us, gbs, bytes_step, us_median, extra = bench_decode(torch, jl, si, args)
         result["decode"] = {
-            "us_per_step": round(us, 3), "us_per_step_median": round(us_median, 3),
-            "us_per_step_paged_256": round(us_paged, 3), "unit": "µs/step",
+            "us_per_step": round(us, 3), "us_per_step_median": round(us_median, 3), **extra, "unit": "µs/step",
             "steps_timed": args.decode_passes * dw.steps,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
