@@ -96,6 +96,56 @@ def traffic_summary(fetch_csv: str, write_csv: str, cmd_fetch: str, cmd_write: s
     }
 
 
+def pmc_markdown(paths, kernel_prefix: str, title: str, cmds, simds: int = 1024, xcds: int = 8) -> str:
+    """Per-dispatch averages of every counter collected for the kernels whose
+    short name starts with kernel_prefix, over one or more --pmc runs, plus
+    derived shares when their counters were collected.  GRBM_GUI_ACTIVE
+    comes summed over the chip's XCDs, so one XCD's active cycles are
+    GRBM_GUI_ACTIVE / xcds; MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over that
+    times the SIMD count.  The SQ_WAVE_CYCLES-style counters are per wave in
+    units of 4 cycles, summed over waves."""
+    vals = collections.defaultdict(list)
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if short_name(r["Kernel_Name"]).startswith(kernel_prefix):
+                vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel_prefix} in {paths}")
+    out = [f"# {title}", "", f"Kernel `{kernel_prefix}`; counters averaged per dispatch.", "",
+           "Commands (repository root on one MI355X, one run per counter set):", ""]
+    out += ["```", *cmds, "```", "", "| counter | dispatches | value per dispatch |", "|---|---|---|"]
+    avg = {}
+    for k in sorted(vals):
+        avg[k] = sum(vals[k]) / len(vals[k])
+        out.append(f"| `{k}` | {len(vals[k])} | {avg[k]:.6g} |")
+    gui = avg.get("GRBM_GUI_ACTIVE")
+    gui = gui / xcds if gui else None
+    derived = []
+    if gui:
+        derived.append(f"* active cycles of one XCD: GRBM_GUI_ACTIVE / {xcds} = {gui:.4g}")
+    if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        derived.append(f"* MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x {simds} SIMDs) = "
+                       f"{100.0 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * simds):.1f}%")
+    if gui and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+        derived.append(f"* MFMA and VALU in the same cycle: SQ_VALU_MFMA_COEXEC_CYCLES / (active cycles x {simds}) = "
+                       f"{100.0 * avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / (gui * simds):.1f}%")
+    if gui and "SQ_BUSY_CU_CYCLES" in avg:
+        derived.append(f"* CUs busy on average: SQ_BUSY_CU_CYCLES / active cycles = {avg['SQ_BUSY_CU_CYCLES'] / gui:.1f}")
+    if "SQ_WAVE_CYCLES" in avg and avg["SQ_WAVE_CYCLES"]:
+        for k in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY",
+                  "SQ_WAIT_INST_LDS"):
+            if k in avg:
+                derived.append(f"* {k} / SQ_WAVE_CYCLES = {100.0 * avg[k] / avg['SQ_WAVE_CYCLES']:.1f}% of wave time")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+        derived.append(f"* bf16 MFMA FLOP per dispatch (MOPS x 512) = {avg['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g}")
+    if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_LDS_IDX_ACTIVE" in avg and avg["SQ_LDS_IDX_ACTIVE"]:
+        derived.append(f"* LDS bank-conflict cycles / LDS active cycles = "
+                       f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.4g}")
+    if derived:
+        out += ["", "Derived:", "", *derived]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(prog="python -m zero_shot_rope_jl_amd.profiling")
     sub = ap.add_subparsers(dest="what", required=True)
@@ -108,7 +158,15 @@ def main(argv=None) -> int:
     t.add_argument("--write", required=True)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
+    m = sub.add_parser("pmc")
+    m.add_argument("csv", nargs="+")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--title", required=True)
+    m.add_argument("--cmd", action="append", default=[])
     a = ap.parse_args(argv)
+    if a.what == "pmc":
+        sys.stdout.write(pmc_markdown(a.csv, a.kernel, a.title, a.cmd))
+        return 0
     if a.what == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.title, a.cmd))
     else:
