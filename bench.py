@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query rows in the CPU-oracle sample")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--unfused-steps", type=int, default=3,
+                    help="calls of the unfused three-pass prefill timed (0 skips it)")
     ap.add_argument("--control-steps", type=int, default=5,
                     help="timed calls of the matched control (same inputs, every pair local); 0 skips it")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -148,6 +150,35 @@ def bench_control(torch, jl, args, w, x):
     ms = ev0.elapsed_time(ev1) / args.control_steps
     log(f"[bench] matched control (G=1) {ms:.3f} ms/call")
     del q, k, v, out, lse
+    torch.cuda.empty_cache()
+    return ms
+
+
+def bench_unfused(torch, jl, args, w, x):
+    """The same call computed unfused: three separate attention passes and
+    their inclusion-exclusion merge (jl_bifocal_prefill_unfused)."""
+    q, k, v = (to_dev(torch, x[n], w.dtype) for n in "qkv")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device="cuda")
+    table = jl.alloc_table(w.L, w.D, w.rope_base)
+    ws = jl.alloc_prefill_unfused_workspace(q, k, w.w_pretrained)
+
+    def step():
+        jl.jl_bifocal_prefill_unfused(q, k, v, out, lse, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table,
+                                      workspace=ws)
+
+    step()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.unfused_steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.unfused_steps
+    log(f"[bench] unfused (three passes + merge) {ms:.3f} ms/call")
+    del q, k, v, out, lse, ws
     torch.cuda.empty_cache()
     return ms
 
@@ -323,6 +354,12 @@ def main():
             "what": "same kernel and inputs with w_pretrained = L (G = 1, every pair local)",
             "ms_per_call": round(cms, 4), "tflops": round(flops / (cms * 1e-3) / 1e12, 2),
             "bifocal_over_control": round(cms / ms, 4)}
+    if args.unfused_steps > 0:
+        ums = bench_unfused(torch, jl, args, w, x)
+        result["unfused"] = {
+            "what": "three separate passes (stored view over the window, corrected view over all keys and over "
+                    "the window) and their inclusion-exclusion merge",
+            "ms_per_call": round(ums, 4), "fused_speedup": round(ums / ms, 4)}
     if not args.skip_decode:
         dw, us, gbs, bytes_step, us_median, extra = bench_decode(torch, jl, si, args)
         result["decode"] = {

@@ -139,6 +139,45 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
                        void* hip_stream);
 
 /*
+ * jl_bifocal_prefill_unfused_workspace -- device bytes of scratch
+ * jl_bifocal_prefill_unfused needs: the keys in their remote view (bf16
+ * inputs with G > 1, as for jl_bifocal_prefill), then three fp32 pass
+ * outputs [B, L, Hq, D] and three fp32 log-sum-exps [B, Hq, L], each part at
+ * a 256-byte boundary.  Pure host call.  Errors as for
+ * jl_bifocal_prefill_workspace (Hq < 1 -> JL_EINVAL as well).
+ */
+JL_API int jl_bifocal_prefill_unfused_workspace(int in_dtype, int64_t B, int64_t L, int64_t Hq,
+                                                int64_t Hkv, int64_t D, int64_t w_pretrained,
+                                                size_t* bytes);
+
+/*
+ * jl_bifocal_prefill_unfused -- the same result as jl_bifocal_prefill,
+ * computed the way §3.3 Eq. (6) writes it: three separate causal attention
+ * passes, then their inclusion-exclusion merge.
+ *
+ *   A: stored vectors, keys q - w0 <= k <= q        (the local window)
+ *   B: remote view (§3.2 Eq. 5), every key k <= q
+ *   C: remote view, keys q - w0 <= k <= q
+ *   out = (W_A O_A + W_B O_B - W_C O_C) / (W_A + W_B - W_C),
+ *   lse = log(W_A + W_B - W_C)
+ *
+ * with O_X a pass's normalised output and W_X its softmax denominator (the
+ * passes keep fp32 outputs and log-sum-exps in the workspace).  It is the
+ * unfused baseline that the fused kernel is measured against; the fused call
+ * is the one to use.  Arguments, layouts, dtypes and errors as for
+ * jl_bifocal_prefill, except that `workspace` (never NULL) must hold
+ * jl_bifocal_prefill_unfused_workspace(...) bytes (JL_ESPACE otherwise).
+ * Four or five kernel launches on `hip_stream` (key rotation, A, B, C,
+ * merge, plus each pass's overflow check).
+ */
+JL_API int jl_bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* out,
+                                      float* lse, int in_dtype, int out_dtype, int64_t B, int64_t L,
+                                      int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                                      int64_t w_pretrained, double rope_base, float sm_scale,
+                                      const void* table, size_t table_bytes, void* workspace,
+                                      size_t workspace_bytes, void* hip_stream);
+
+/*
  * jl_bifocal_prefill_chunk -- a chunk of Lq new tokens appended to a cache
  * (chunked prefill, or several decode tokens at once): the rows at positions
  * L-Lq .. L-1 of jl_bifocal_prefill over L tokens (§3 Eq. 1, §3.2 Eqs. 4-5,

@@ -25,10 +25,11 @@ def test_exports_every_declared_symbol():
     syms = header_symbols()
     assert syms == sorted(["jl_last_error", "jl_version", "jl_schedule", "jl_bifocal_prefill_workspace",
                            "jl_bifocal_prefill", "jl_bifocal_prefill_chunk", "jl_bifocal_decode_workspace",
-                           "jl_bifocal_decode", "jl_bifocal_decode_paged", "jl_table_fill_host"])
+                           "jl_bifocal_decode", "jl_bifocal_decode_paged", "jl_table_fill_host",
+                           "jl_bifocal_prefill_unfused_workspace", "jl_bifocal_prefill_unfused"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 4
+    assert jl.jl_version() == 5
 
 
 def test_schedule_golden_and_table_size():
@@ -100,6 +101,44 @@ def test_prefill_without_workspace_when_none_is_needed_passes_validation_order()
     # G == 1: a NULL workspace is accepted; the call still fails later, on the
     # unsupported head_dim, before any HIP call
     assert _prefill(L=64, wp=64, ws=None, wsb=0, D=96) == jl.JL_EUNSUPPORTED
+
+
+def _unfused(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, L=256, Hq=4,
+             Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE, tb=1 << 30, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_prefill_unfused(a["q"], a["k"], a["v"], a["out"], a["lse"], a["i"], a["o"], a["B"],
+                                             a["L"], a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"], a["base"],
+                                             a["sc"], a["table"], a["tb"], a["ws"], a["wsb"], None)
+
+
+# bf16, B 1, L 256, Hq 4, Hkv 2, D 128, w_pretrained 64 (G = 4): rotated keys
+# 256*2*128*2 B, then three fp32 outputs of 256*4*128*4 B and three fp32
+# log-sum-exps of 4*256*4 B, every part a multiple of 256 B already
+UNFUSED_WS = 256 * 2 * 128 * 2 + 3 * 256 * 4 * 128 * 4 + 3 * 4 * 256 * 4
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), jl.JL_EINVAL), (dict(table=None), jl.JL_EINVAL), (dict(out=FAKE + 2), jl.JL_EINVAL),
+    (dict(lse=FAKE + 4), jl.JL_EINVAL), (dict(B=0), jl.JL_EINVAL), (dict(L=0), jl.JL_EINVAL),
+    (dict(Hq=3), jl.JL_EINVAL), (dict(w0=-1), jl.JL_EINVAL), (dict(wp=0), jl.JL_EINVAL),
+    (dict(sc=0.0), jl.JL_EINVAL), (dict(D=96), jl.JL_EUNSUPPORTED), (dict(i=jl.JL_F32, o=jl.JL_BF16),
+                                                                     jl.JL_EUNSUPPORTED),
+    (dict(Hq=32, Hkv=2), jl.JL_EUNSUPPORTED), (dict(tb=100), jl.JL_ESPACE), (dict(ws=None), jl.JL_EINVAL),
+    (dict(wsb=UNFUSED_WS - 1), jl.JL_ESPACE), (dict(ws=FAKE + 8), jl.JL_EINVAL),
+])
+def test_prefill_unfused_validation(over, code):
+    assert _unfused(**over) == code
+    assert jl.jl_last_error()
+
+
+def test_prefill_unfused_workspace_size():
+    assert jl.jl_bifocal_prefill_unfused_workspace(jl.JL_BF16, 1, 256, 4, 2, 128, 64) == UNFUSED_WS
+    # fp32 inputs: no rotated keys; 100 rows: 3 * 100*8*64*4 B outputs and
+    # 3 * 8*100*4 B = 3200 B log-sum-exps, each rounded up to 256 B (3328)
+    assert jl.jl_bifocal_prefill_unfused_workspace(jl.JL_F32, 1, 100, 8, 2, 64, 64) == 3 * 204800 + 3 * 3328
+    with pytest.raises(jl.JetLongError):
+        jl.jl_bifocal_prefill_unfused_workspace(jl.JL_BF16, 1, 10, 0, 1, 64, 4)
 
 
 def _chunk(**over):

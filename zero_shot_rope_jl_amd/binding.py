@@ -45,6 +45,12 @@ def _load():
     L.jl_bifocal_prefill_workspace.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.POINTER(sz)]
     L.jl_bifocal_prefill.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                      i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
+    L.jl_bifocal_prefill_unfused_workspace.restype = ctypes.c_int
+    L.jl_bifocal_prefill_unfused_workspace.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                                       ctypes.POINTER(sz)]
+    L.jl_bifocal_prefill_unfused.restype = ctypes.c_int
+    L.jl_bifocal_prefill_unfused.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                             i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
     L.jl_bifocal_prefill_chunk.restype = ctypes.c_int
     L.jl_bifocal_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                            i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp,
@@ -193,6 +199,46 @@ def jl_bifocal_prefill(q, k, v, out, lse, w0: int, w_pretrained: int, rope_base:
                                   _dtype_code(out), B, L, Hq, Hkv, D, w0, w_pretrained, rope_base,
                                   sm_scale, _ptr(table), table.numel() * table.element_size(),
                                   _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def jl_bifocal_prefill_unfused_workspace(in_dtype: int, B: int, L: int, Hq: int, Hkv: int, D: int,
+                                         w_pretrained: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.jl_bifocal_prefill_unfused_workspace(in_dtype, B, L, Hq, Hkv, D, w_pretrained, ctypes.byref(n)))
+    return n.value
+
+
+def alloc_prefill_unfused_workspace(q, k, w_pretrained: int, device="cuda"):
+    """Scratch for jl_bifocal_prefill_unfused over q [B, L, Hq, D] and k [B, L, Hkv, D]."""
+    torch = _torch()
+    B, L, Hq, D = q.shape
+    n = jl_bifocal_prefill_unfused_workspace(_dtype_code(q), B, L, Hq, k.shape[2], D, w_pretrained)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def jl_bifocal_prefill_unfused(q, k, v, out, lse, w0: int, w_pretrained: int, rope_base: float,
+                               sm_scale: float, table, workspace=None, stream=None):
+    """The three-pass form of jl_bifocal_prefill (same arguments); `workspace`
+    as from alloc_prefill_unfused_workspace, allocated through torch if None."""
+    _need_device(q, k, v, out, lse, table, workspace)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, L, Hkv, D) or tuple(v.shape) != (B, L, Hkv, D):
+        raise ValueError("k and v must be [B, L, Hkv, D] matching q")
+    if tuple(out.shape) != (B, L, Hq, D):
+        raise ValueError("out must be [B, L, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq, L) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq, L]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if workspace is None:
+        workspace = alloc_prefill_unfused_workspace(q, k, w_pretrained, device=q.device)
+    _check(lib.jl_bifocal_prefill_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
+                                          _dtype_code(out), B, L, Hq, Hkv, D, w0, w_pretrained, rope_base,
+                                          sm_scale, _ptr(table), table.numel() * table.element_size(),
+                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
     return out, lse
 
 

@@ -67,7 +67,7 @@ extern "C" {
 
 JL_API const char* jl_last_error(void) { return g_err.c_str(); }
 
-JL_API int jl_version(void) { return 4; }
+JL_API int jl_version(void) { return 5; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -120,13 +120,13 @@ JL_API int jl_bifocal_prefill_workspace(int in_dtype, int64_t B, int64_t L, int6
 
 namespace {
 
-// Both prefill entry points: Lq queries at positions L - Lq .. L - 1 over keys
-// 0..L-1 held in k/v with Lkv rows per batch entry.
-int prefill_impl(const char* who, const void* q, const void* k, const void* v, void* out, float* lse, int in_dtype,
-                 int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Lkv, int64_t Hq, int64_t Hkv, int64_t D,
-                 int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
-                 size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
-    g_err.clear();
+// Argument checks shared by every prefill entry point (all but the
+// workspace size): Lq queries at positions L - Lq .. L - 1 over keys 0..L-1
+// held in k/v with Lkv rows per batch entry.
+int check_prefill(const char* who, const void* q, const void* k, const void* v, const void* out, const float* lse,
+                  int in_dtype, int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Lkv, int64_t Hq,
+                  int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale,
+                  const void* table, size_t table_bytes, const void* workspace) {
     if (!q || !k || !v || !out || !table) return fail(JL_EINVAL, "%s: q, k, v, out and table must be non-NULL", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(table) ||
         !aligned16(lse) || !aligned16(workspace))
@@ -143,15 +143,17 @@ int prefill_impl(const char* who, const void* q, const void* k, const void* v, v
     const size_t need = jl::table_bytes_for(L, (int)D);
     if (table_bytes < need)
         return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
-    size_t ws_need = 0;
-    jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D, w_pretrained, &ws_need);
-    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
-        return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : (size_t)0,
-                    ws_need);
-    const int BQ = 256 / (int)R;
-    const int64_t n_qtiles = (Lq + BQ - 1) / BQ;
+    const int64_t n_qtiles = (Lq + 256 / R - 1) / (256 / R);
     if (n_qtiles * Hkv * B > 0x7fffffffLL) return fail(JL_EINVAL, "grid too large");
+    return JL_OK;
+}
 
+jl::PrefillParams make_prefill_params(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                                      int64_t Lq, int64_t L, int64_t Lkv, int64_t Hq, int64_t Hkv, int64_t D,
+                                      int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale,
+                                      const void* table, void* krot) {
+    const int64_t R = Hq / Hkv;
+    const int BQ = 256 / (int)R;
     jl::PrefillParams p{};
     p.q = q;
     p.k = k;
@@ -169,17 +171,64 @@ int prefill_impl(const char* who, const void* q, const void* k, const void* v, v
     p.Hkv = Hkv;
     p.R = (int)R;
     p.BQ = BQ;
-    p.n_qtiles = (int)n_qtiles;
+    p.n_qtiles = (int)((Lq + BQ - 1) / BQ);
     p.w0 = w0 < L ? w0 : L;   // any w0 >= L-1 makes every pair local
     p.G = group_size(L, w_pretrained);
     p.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
     p.rope_base = rope_base;
     p.head_dim = (int)D;
-    p.krot = workspace;
+    p.krot = krot;
+    p.mode = jl::kFused;
+    return p;
+}
+
+// Both fused prefill entry points.
+int prefill_impl(const char* who, const void* q, const void* k, const void* v, void* out, float* lse, int in_dtype,
+                 int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Lkv, int64_t Hq, int64_t Hkv, int64_t D,
+                 int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
+                 size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    g_err.clear();
+    if (int rc = check_prefill(who, q, k, v, out, lse, in_dtype, out_dtype, B, Lq, L, Lkv, Hq, Hkv, D, w0,
+                               w_pretrained, rope_base, sm_scale, table, table_bytes, workspace))
+        return rc;
+    size_t ws_need = 0;
+    jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D, w_pretrained, &ws_need);
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
+        return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                    ws_need);
+    const jl::PrefillParams p = make_prefill_params(q, k, v, out, lse, B, Lq, L, Lkv, Hq, Hkv, D, w0, w_pretrained,
+                                                    rope_base, sm_scale, table, workspace);
     (void)hipGetLastError();
     hipError_t e = jl::launch_prefill(p, in_dtype, out_dtype, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
     return JL_OK;
+}
+
+// Workspace of the unfused prefill: the rotated keys (bf16 inputs, G > 1),
+// then the three passes' fp32 outputs and log-sum-exps, each at a 256-byte
+// boundary.
+struct UnfusedLayout {
+    size_t krot, o[3], l[3], total;
+};
+
+UnfusedLayout unfused_layout(int in_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
+                             int64_t w_pretrained) {
+    auto up = [](size_t x) { return (x + 255u) & ~(size_t)255u; };
+    UnfusedLayout u{};
+    size_t off = 0;
+    const bool rotated_keys = in_dtype == JL_BF16 && group_size(L, w_pretrained) > 1;
+    u.krot = off;
+    off = up(off + (rotated_keys ? (size_t)B * (size_t)L * (size_t)Hkv * (size_t)D * 2u : 0u));
+    for (int i = 0; i < 3; ++i) {
+        u.o[i] = off;
+        off = up(off + (size_t)B * (size_t)L * (size_t)Hq * (size_t)D * 4u);
+    }
+    for (int i = 0; i < 3; ++i) {
+        u.l[i] = off;
+        off = up(off + (size_t)B * (size_t)Hq * (size_t)L * 4u);
+    }
+    u.total = off;
+    return u;
 }
 
 }  // namespace
@@ -202,6 +251,65 @@ JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const vo
     return prefill_impl("prefill_chunk", q, k_cache, v_cache, out, lse, in_dtype, out_dtype, B, Lq, L, Lmax, Hq,
                         Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
                         workspace_bytes, hip_stream);
+}
+
+JL_API int jl_bifocal_prefill_unfused_workspace(int in_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv,
+                                                int64_t D, int64_t w_pretrained, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(JL_EINVAL, "bytes is NULL");
+    if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || L > kMaxLen)
+        return fail(JL_EINVAL, "B, Hq, Hkv, L must be >= 1 and L <= 2^30");
+    if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1 (got %lld)", (long long)w_pretrained);
+    if (D != 64 && D != 128) return fail(JL_EUNSUPPORTED, "head_dim %lld not supported", (long long)D);
+    if (in_dtype != JL_F32 && in_dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "unknown in_dtype %d", in_dtype);
+    *bytes = unfused_layout(in_dtype, B, L, Hq, Hkv, D, w_pretrained).total;
+    return JL_OK;
+}
+
+JL_API int jl_bifocal_prefill_unfused(const void* q, const void* k, const void* v, void* out, float* lse,
+                                      int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv,
+                                      int64_t D, int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale,
+                                      const void* table, size_t table_bytes, void* workspace,
+                                      size_t workspace_bytes, void* hip_stream) {
+    const char* who = "prefill_unfused";
+    g_err.clear();
+    if (int rc = check_prefill(who, q, k, v, out, lse, in_dtype, out_dtype, B, L, L, L, Hq, Hkv, D, w0,
+                               w_pretrained, rope_base, sm_scale, table, table_bytes, workspace))
+        return rc;
+    if (!workspace) return fail(JL_EINVAL, "%s: workspace must be non-NULL", who);
+    const UnfusedLayout u = unfused_layout(in_dtype, B, L, Hq, Hkv, D, w_pretrained);
+    if (workspace_bytes < u.total)
+        return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace_bytes, u.total);
+    char* ws = static_cast<char*>(workspace);
+    const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    (void)hipGetLastError();
+    // passes A, B, C (B rotates the keys into the workspace, C reuses them)
+    const int modes[3] = {jl::kLocalWindow, jl::kRemoteAll, jl::kRemoteWindow};
+    for (int i = 0; i < 3; ++i) {
+        jl::PrefillParams p = make_prefill_params(q, k, v, ws + u.o[i], reinterpret_cast<float*>(ws + u.l[i]), B, L,
+                                                  L, L, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table,
+                                                  ws + u.krot);
+        p.mode = modes[i];
+        p.krot_ready = i == 2;
+        const hipError_t e = jl::launch_prefill(p, in_dtype, JL_F32, stream);
+        if (e != hipSuccess) return fail(JL_EHIP, "%s pass %d launch failed: %s", who, i, hipGetErrorString(e));
+    }
+    jl::MergeParams m{};
+    m.o_a = reinterpret_cast<const float*>(ws + u.o[0]);
+    m.o_b = reinterpret_cast<const float*>(ws + u.o[1]);
+    m.o_c = reinterpret_cast<const float*>(ws + u.o[2]);
+    m.lse_a = reinterpret_cast<const float*>(ws + u.l[0]);
+    m.lse_b = reinterpret_cast<const float*>(ws + u.l[1]);
+    m.lse_c = reinterpret_cast<const float*>(ws + u.l[2]);
+    m.out = out;
+    m.lse = lse;
+    m.B = B;
+    m.Lq = L;
+    m.Hq = Hq;
+    m.D = D;
+    const hipError_t e = jl::launch_ie_merge(m, out_dtype, stream);
+    if (e != hipSuccess) return fail(JL_EHIP, "%s merge launch failed: %s", who, hipGetErrorString(e));
+    return JL_OK;
 }
 
 JL_API int jl_bifocal_decode_workspace(int64_t B, int64_t Hq, int64_t D, int64_t L, size_t* bytes) {

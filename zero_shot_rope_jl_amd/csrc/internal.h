@@ -34,6 +34,19 @@ struct PrefillParams {
     // bf16 kernel only: B*L*Hkv*D bf16 workspace that receives the keys in
     // their corrected view when G > 1 (laid out like k)
     void* krot;
+    // which pairs and which view (Jet-Long §3.3 Eq. 6): kFused is the bifocal
+    // rule in one softmax; the other three are the separate passes of the
+    // inclusion-exclusion merge, each one plain masked attention in one view
+    int mode;
+    // bf16 kernel only: krot already holds this call's rotated keys
+    int krot_ready;
+};
+
+enum PrefillMode {
+    kFused = 0,        // q - k <= w0 in the stored view, the rest in the corrected view
+    kLocalWindow = 1,  // A: stored view, keys q - w0 <= k <= q
+    kRemoteAll = 2,    // B: corrected view, keys k <= q
+    kRemoteWindow = 3, // C: corrected view, keys q - w0 <= k <= q
 };
 
 struct DecodeParams {
@@ -93,7 +106,21 @@ hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double 
                              hipStream_t stream);
 void table_fill_host(void* table, int64_t n_cover, int head_dim, double rope_base);
 
+// The three pass outputs of the unfused prefill and where their merge goes.
+struct MergeParams {
+    const float* o_a;     // [B, Lq, Hq, D] normalised pass outputs
+    const float* o_b;
+    const float* o_c;
+    const float* lse_a;   // [B, Hq, Lq] natural-log sums of the passes
+    const float* lse_b;
+    const float* lse_c;
+    void* out;            // [B, Lq, Hq, D], bf16 or fp32
+    float* lse;           // [B, Hq, Lq] or null
+    int64_t B, Lq, Hq, D;
+};
+
 hipError_t launch_prefill(const PrefillParams& p, int in_dtype, int out_dtype, hipStream_t stream);
+hipError_t launch_ie_merge(const MergeParams& p, int out_dtype, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams& p, int out_dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int out_dtype, hipStream_t stream);
 

@@ -350,12 +350,29 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     // ---- pass schedule (uniform over the workgroup) -------------------------
     // tile kt covers keys [64kt, 64kt + 63]; the last one is padded with zero
     // rows beyond L, which every mask below excludes.
+    // The corrected-view phase walks tiles r0 .. r0 + nR - 1, then the
+    // stored-view phase tiles nL0 .. nkt - 1.
     const int nkt = q_hi / BN + 1;
-    int nR = 0;    // remote phase: tiles [0, nR) hold a pair with q - k > w0
-    int nL0 = 0;   // local phase: tiles [nL0, nkt) hold a pair with 0 <= q - k <= w0
-    if (G > 1) {
-        nR = q_hi - w0 > 0 ? min(nkt, (q_hi - w0 + BN - 1) / BN) : 0;
-        nL0 = q0 - w0 - (BN - 1) > 0 ? (q0 - w0) / BN : 0;
+    const int mode = p.mode;
+    int nR = 0;    // fused: tiles [0, nR) hold a pair with q - k > w0
+    int nL0 = 0;   // fused: tiles [nL0, nkt) hold a pair with 0 <= q - k <= w0
+    int r0 = 0;
+    // first tile holding a key of some row's window [q - w0, q]
+    const int win0 = q0 - w0 - (BN - 1) > 0 ? (q0 - w0) / BN : 0;
+    if (mode == kFused) {
+        if (G > 1) {
+            nR = q_hi - w0 > 0 ? min(nkt, (q_hi - w0 + BN - 1) / BN) : 0;
+            nL0 = win0;
+        }
+    } else if (mode == kLocalWindow) {
+        nL0 = win0;
+    } else if (mode == kRemoteAll) {
+        nR = nkt;
+        nL0 = nkt;
+    } else {
+        r0 = win0;
+        nR = nkt - win0;
+        nL0 = nkt;
     }
     const int NP = nR + (nkt - nL0);
 
@@ -369,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const int kr = tid >> 3;             // key row of this thread
     const int f0 = (tid & 7) * PPT;      // K: first frequency of this thread
     const int v0 = (tid & 7) * Lay::VPT; // V: first dim of this thread
-    auto pass_k0 = [&](int pi) { return (pi < nR ? pi : nL0 + (pi - nR)) * BN; };
+    auto pass_k0 = [&](int pi) { return (pi < nR ? r0 + pi : nL0 + (pi - nR)) * BN; };
     auto stage_load = [&](int pi) {
         const int kpos = pass_k0(pi) + kr;
         const bool ok = kpos < L;
@@ -425,19 +442,29 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             const int k0 = pass_k0(pi);
             const int k1 = k0 + BN - 1;
             bool act, masked;
-            if (rem) {
-                act = p_hi - k0 > w0;
-                masked = p0 - k1 <= w0;                          // some local pair here
-            } else {
-                act = k0 <= p_hi && (G == 1 || p0 - k1 <= w0);
-                masked = k1 > p0 || (G > 1 && p_hi - k0 > w0);  // causal edge or remote pairs
-            }
-            if (act) {
+            int klo, khi;
+            if (mode == kFused) {
+                if (rem) {
+                    act = p_hi - k0 > w0;
+                    masked = p0 - k1 <= w0;                          // some local pair here
+                } else {
+                    act = k0 <= p_hi && (G == 1 || p0 - k1 <= w0);
+                    masked = k1 > p0 || (G > 1 && p_hi - k0 > w0);  // causal edge or remote pairs
+                }
                 // masked tiles keep keys in [klo, khi]: the remote view keeps
                 // q - k > w0, the local view 0 <= q - k <= w0 (no lower bound
                 // if G == 1)
-                const int klo = (rem || G == 1) ? INT_MIN / 2 : my_q - w0;
-                const int khi = rem ? my_q - w0 - 1 : my_q;
+                klo = (rem || G == 1) ? INT_MIN / 2 : my_q - w0;
+                khi = rem ? my_q - w0 - 1 : my_q;
+            } else {
+                // one pass of the merge: keys [q - w0, q], or every k <= q
+                const bool all = mode == kRemoteAll;
+                act = k0 <= p_hi && (all || p0 - k1 <= w0);
+                masked = k1 > p0 || (!all && p_hi - k0 > w0);
+                klo = all ? INT_MIN / 2 : my_q - w0;
+                khi = my_q;
+            }
+            if (act) {
                 const int off = k0 + (BF16 ? 8 * hh : 4 * hh);
                 tile_step<D, BF16>(sK[buf], sV[buf], qv, acc, m_run, l_run, col, hh, lane, masked, klo - off,
                                    khi - off, scale2);

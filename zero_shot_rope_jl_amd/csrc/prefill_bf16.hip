@@ -83,7 +83,7 @@ __device__ inline int vswz(int row, int c) {
     return c ^ ((4 * (row & 3)) & (Lay5<D>::CH - 1));
 }
 
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p) {
     using Lay = Lay5<D>;
     constexpr int HALF = Lay::HALF;
@@ -179,12 +179,30 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     }
 
     // ---- pass schedule (uniform over the workgroup) -------------------------
+    // The corrected-view phase walks tiles r0 .. r0 + nR - 1, then the
+    // stored-view phase tiles nL0 .. nkt - 1.
     const int nkt = q_hi / BN + 1;
-    int nR = 0;    // remote phase: tiles [0, nR) hold a pair with q - k > w0
-    int nL0 = 0;   // local phase: tiles [nL0, nkt) hold a pair with 0 <= q - k <= w0
-    if (G > 1) {
-        nR = q_hi - w0 > 0 ? min(nkt, (q_hi - w0 + BN - 1) / BN) : 0;
-        nL0 = q0 - w0 - (BN - 1) > 0 ? (q0 - w0) / BN : 0;
+    int nR = 0;    // fused: tiles [0, nR) hold a pair with q - k > w0
+    int nL0 = 0;   // fused: tiles [nL0, nkt) hold a pair with 0 <= q - k <= w0
+    int r0 = 0;
+    if constexpr (MODE == kFused) {
+        if (G > 1) {
+            nR = q_hi - w0 > 0 ? min(nkt, (q_hi - w0 + BN - 1) / BN) : 0;
+            nL0 = q0 - w0 - (BN - 1) > 0 ? (q0 - w0) / BN : 0;
+        }
+    } else {
+        // first tile holding a key of some row's window [q - w0, q]
+        const int win0 = q0 - w0 - (BN - 1) > 0 ? (q0 - w0) / BN : 0;
+        if constexpr (MODE == kLocalWindow) {
+            nL0 = win0;
+        } else if constexpr (MODE == kRemoteAll) {
+            nR = nkt;
+            nL0 = nkt;
+        } else {
+            r0 = win0;
+            nR = nkt - win0;
+            nL0 = nkt;
+        }
     }
     const int NP = nR + (nkt - nL0);
 
@@ -247,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
     for (int u = 0; u < KU; ++u) k_voff[u] = k_slot_voff((u * kWaves + wave) * 64 + lane);
     k_voff[KU] = wave < KREM ? k_slot_voff((KU * kWaves + wave) * 64 + lane) : 0u;
-    auto tile_k0 = [&](int pi) __attribute__((always_inline)) { return (pi < nR ? pi : nL0 + (pi - nR)) * BN; };
+    auto tile_k0 = [&](int pi) __attribute__((always_inline)) { return (pi < nR ? r0 + pi : nL0 + (pi - nR)) * BN; };
     // staging is issued in two parts spread over the tile, so that the
     // vector-memory queue never fills and stalls the wave: K at the start, V
     // with the first PV half
@@ -359,12 +377,19 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // written with selects so that it compiles without branches.
     auto block_state = [&](int j, bool rem, int k0, bool& act, bool& msk) __attribute__((always_inline)) {
         const int k1 = k0 + BN - 1;
-        const bool act_r = pjhi[j] - k0 > w0;
-        const bool msk_r = pj0[j] - k1 <= w0;
-        const bool act_l = (k0 <= pjhi[j]) & ((G == 1) | (pj0[j] - k1 <= w0));
-        const bool msk_l = (k1 > pj0[j]) | ((G > 1) & (pjhi[j] - k0 > w0));
-        act = (rem ? act_r : act_l) & (pj0[j] < L);
-        msk = (rem ? msk_r : msk_l) | !act;
+        if constexpr (MODE == kFused) {
+            const bool act_r = pjhi[j] - k0 > w0;
+            const bool msk_r = pj0[j] - k1 <= w0;
+            const bool act_l = (k0 <= pjhi[j]) & ((G == 1) | (pj0[j] - k1 <= w0));
+            const bool msk_l = (k1 > pj0[j]) | ((G > 1) & (pjhi[j] - k0 > w0));
+            act = (rem ? act_r : act_l) & (pj0[j] < L);
+            msk = (rem ? msk_r : msk_l) | !act;
+        } else {
+            // kept keys [q - w0, q], or every k <= q for the all-keys pass
+            constexpr bool all = MODE == kRemoteAll;
+            act = (k0 <= pjhi[j]) & (all | (pj0[j] - k1 <= w0)) & (pj0[j] < L);
+            msk = (k1 > pj0[j]) | (!all & (pjhi[j] - k0 > w0)) | !act;
+        }
     };
     auto edge_fix = [&](f32x16 (&s)[NJ], int kb, bool rem, int k0) {
 #pragma unroll
@@ -372,8 +397,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             // kept key window [rlo, rhi] relative to the lane's first key k0 + 8hh
             bool act, msk;
             block_state(j, rem, k0, act, msk);
-            const int klo = (rem || G == 1) ? INT_MIN / 2 : my_q[j] - w0;
-            const int khi = rem ? my_q[j] - w0 - 1 : my_q[j];
+            int klo, khi;
+            if constexpr (MODE == kFused) {
+                klo = (rem || G == 1) ? INT_MIN / 2 : my_q[j] - w0;
+                khi = rem ? my_q[j] - w0 - 1 : my_q[j];
+            } else {
+                klo = MODE == kRemoteAll ? INT_MIN / 2 : my_q[j] - w0;
+                khi = my_q[j];
+            }
             int rlo = act ? klo - k0 - 8 * hh : 1;
             int rhi = act ? khi - k0 - 8 * hh : 0;
             rlo = msk ? rlo : INT_MIN / 2;   // every pair kept
@@ -564,25 +595,36 @@ __global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restri
     *reinterpret_cast<bf16x8*>(dst + HALF) = yo;
 }
 
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, int MODE>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-    if (p.G > 1) {
+    if (p.G > 1 && MODE != kLocalWindow && !p.krot_ready) {
         const int64_t n_items = p.B * p.L * p.Hkv * (D / 16);
         hipLaunchKernelGGL((rotate_keys_kernel<D>), dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0, stream,
                            static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.krot), p.TF, n_items, p.L,
                            p.Lkv, (int)p.Hkv, p.G);
     }
     const int64_t blocks = (int64_t)p.n_qtiles * p.Hkv * p.B;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16, MODE>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       p);
     return hipGetLastError();
+}
+
+template <int D, bool OUT_BF16>
+hipError_t launch_mode(const PrefillParams& p, hipStream_t stream) {
+    switch (p.mode) {
+        case kLocalWindow: return launch_one<D, OUT_BF16, kLocalWindow>(p, stream);
+        case kRemoteAll: return launch_one<D, OUT_BF16, kRemoteAll>(p, stream);
+        case kRemoteWindow: return launch_one<D, OUT_BF16, kRemoteWindow>(p, stream);
+        default: return launch_one<D, OUT_BF16, kFused>(p, stream);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int out_dtype, hipStream_t stream) {
     const bool ob = out_dtype == 1;
-    if (p.head_dim == 128) return ob ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
-    return ob ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+    if (p.head_dim == 128) return ob ? launch_mode<128, true>(p, stream) : launch_mode<128, false>(p, stream);
+    return ob ? launch_mode<64, true>(p, stream) : launch_mode<64, false>(p, stream);
 }
 
 }  // namespace jl
