@@ -1,5 +1,7 @@
 // Causal GQA bifocal-attention prefill for gfx950, generic kernel (serves
-// fp32 inputs; bf16 inputs go to the 64-rows-per-wave kernel).
+// fp32 inputs and the overflow fixup of bf16 calls; bf16 inputs go to the
+// kernel of prefill_bf16.hip).  Like that kernel it also runs the three
+// separate passes of the unfused form (PrefillParams::mode).
 //
 // Method (Jet-Long, §3 Eq. 1; §3.1 Eqs. 2-3; §3.2 Eq. 5; §3.3 Eq. 6): a
 // query/key pair with q - k <= w0 scores with the stored RoPE vectors; a pair
@@ -514,7 +516,7 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillParams& p, int in_dtype, int out_dtype, hipStream_t stream) {
     if (in_dtype == 1) {
-        // bf16 inputs: the 64-rows-per-wave kernel, then the fixup pass that
+        // bf16 inputs: the kernel of prefill_bf16.hip, then the fixup pass that
         // recomputes (with the online softmax here) any workgroup whose rows
         // it marked as non-finite; the pass exits at once when none is marked.
         const hipError_t e = launch_prefill_bf16(p, out_dtype, stream);

@@ -40,6 +40,12 @@
 //   subtraction and the accumulators are touched by MFMAs only.  Probabilities above 1 are
 //   harmless (fp32 and bf16 share the exponent range; the final division
 //   restores the scale).
+//
+// The kernel's MODE template parameter also gives the three separate passes
+// of the unfused form of §3.3 Eq. (6): the stored view over each row's window
+// [q - w0, q], the corrected view over every key k <= q, and the corrected
+// view over the window.  A mode changes only which tiles a workgroup visits
+// and which keys each row keeps; kFused is the bifocal rule itself.
 #include <limits.h>
 #include <math.h>
 
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         __bf16* sVd = decltype(buf)::value ? sV1 : sV0;
         const int k0 = tile_k0(pi);
         const uint32_t tile_bytes = (uint32_t)min(L - k0, BN) * row_bytes;
-        // V: 64 rows x CH chunks
+        // V: BN rows x CH chunks, VRU rows per copy step
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)k0 * kv_row, tile_bytes);
 #pragma unroll
         for (int u = 0; u < VU; ++u)
