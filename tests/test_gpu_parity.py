@@ -260,6 +260,37 @@ def test_small_decode_matches_oracle(L):
         assert max_err(lse.cpu().numpy(), ref_lse) <= TOL_BF16
 
 
+DEC_EDGE = [  # (L, Hq, Hkv, D, w_pre, w0)
+    (65, 4, 2, 64, 1, 3),          # w_pre = 1: G = L, every remote key aliased to position 0
+    (600, 8, 8, 128, 256, 0),      # w0 = 0: only the newest key is local; no GQA (R = 1)
+    (300, 16, 2, 128, 100, 400),   # w0 >= L: every key local; GQA 8
+    (1000, 4, 2, 64, 300, 64),     # D = 64, GQA 2, G = 4
+    (33, 8, 1, 128, 16, 5),        # one KV head, G = 3, L just past a 32-key step
+]
+
+
+@pytest.mark.parametrize("case", DEC_EDGE, ids=[f"L{c[0]}_H{c[1]}x{c[2]}_D{c[3]}_wp{c[4]}_w0{c[5]}" for c in DEC_EDGE])
+def test_decode_degenerate_cases_match_oracle(case):
+    require_gpu()
+    L, Hq, Hkv, D, w_pre, w0 = case
+    B, base, scale = 2, 1e4, D ** -0.5
+    rng = np.random.default_rng(L + Hq)
+    bits = lambda shape: si.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32))
+    qb, kb, vb = bits((B, 1, Hq, D)), bits((B, L + 7, Hkv, D)), bits((B, L + 7, Hkv, D))
+    table = jl.alloc_table(L + 7, D, base)
+    ws = jl.alloc_decode_workspace(B, Hq, D, L + 7)
+    out = torch.empty((B, 1, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    jl.jl_bifocal_decode(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), out, lse, L, w0, w_pre,
+                         base, scale, table, ws)
+    torch.cuda.synchronize()
+    f64 = lambda a: si.f32_from_bf16_bits(a).astype(np.float64)
+    ref, ref_lse = oracle.decode_attention(f64(qb)[:, 0], f64(kb), f64(vb), L, w0, w_pre, base, scale)
+    e, el = max_err(out.cpu().numpy()[:, 0], ref), max_err(lse.cpu().numpy(), ref_lse)
+    print(case, "G", oracle.group_size(L, w_pre), "decode err", e, "lse", el)
+    assert e <= TOL_BF16 and el <= TOL_BF16
+
+
 def test_decode_equals_prefill_last_row():
     require_gpu()
     w = small_workload(1500, 8, 2, 128, 400, 128, seed=21)
