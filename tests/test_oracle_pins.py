@@ -36,10 +36,12 @@ def rope_complex(x, pos, base):
     return np.concatenate([z.real, z.imag], axis=-1)
 
 
-def brute_force(q, k, v, w0, w_pre, base, scale):
+def brute_force(q, k, v, w0, w_pre, base, scale, interleaved=False):
     """Scalar loops: remote scores rebuild RoPE(x, f(p)) by undoing the
     stored phase p and applying f(p) (two rotations per vector, from cos/sin
-    of p*theta and f(p)*theta), instead of the oracle's single offset."""
+    of p*theta and f(p)*theta), instead of the oracle's single offset.
+    Frequency i rotates the channel pair (i, i + D/2), or (2i, 2i + 1) when
+    ``interleaved``."""
     B, L, Hq, D = q.shape
     Hkv = k.shape[2]
     R = Hq // Hkv
@@ -51,10 +53,11 @@ def brute_force(q, k, v, w0, w_pre, base, scale):
         fp = p // G
         out = [0.0] * D
         for i in range(h2):
-            z = complex(vec[i], vec[i + h2])
+            a, c = (2 * i, 2 * i + 1) if interleaved else (i, i + h2)
+            z = complex(vec[a], vec[c])
             z = z * cmath.exp(-1j * p * th[i])      # undo stored phase
             z = z * cmath.exp(1j * fp * th[i])      # aliased phase
-            out[i], out[i + h2] = z.real, z.imag
+            out[a], out[c] = z.real, z.imag
         return out
 
     out = np.zeros((B, L, Hq, D))
@@ -194,6 +197,23 @@ def test_bruteforce_sweep_small():
             want = brute_force(q, k, v, w0, w_pre, 100.0, 0.5)
             got, _ = oracle.bifocal_attention(q, k, v, w0, w_pre, 100.0, 0.5, block=4)
             np.testing.assert_allclose(got, want, atol=1e-12, rtol=0)
+
+
+def test_interleaved_pairing_is_a_channel_permutation():
+    # A model whose RoPE pairs channels (2i, 2i+1) uses the rotate-half path
+    # with q and k channels permuted so that pair i lands on (i, i + D/2):
+    # the scores, hence the output, do not change (v is not permuted).
+    L, w_pre, w0, D, Hq, Hkv = 23, 5, 3, 8, 2, 1
+    q, k, v = rand_qkv(77, 1, L, Hq, Hkv, D)
+    q *= 1.5
+    k *= 1.5
+    want = brute_force(q, k, v, w0, w_pre, 1e4, 0.4, interleaved=True)
+    perm = [2 * j for j in range(D // 2)] + [2 * j + 1 for j in range(D // 2)]
+    got, _ = oracle.bifocal_attention(q[..., perm], k[..., perm], v, w0, w_pre, 1e4, 0.4, block=5)
+    np.testing.assert_allclose(got, want, atol=1e-12, rtol=0)
+    # without the permutation the two conventions differ
+    other, _ = oracle.bifocal_attention(q, k, v, w0, w_pre, 1e4, 0.4, block=5)
+    assert np.abs(other - want).max() > 1e-3
 
 
 # ------------------------------------------------------ I1 exact identity
