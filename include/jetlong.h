@@ -208,6 +208,42 @@ JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const vo
                              size_t workspace_bytes, void* hip_stream);
 
 /*
+ * jl_bifocal_prefill_chunk_paged -- jl_bifocal_prefill_chunk over a paged
+ * cache: the chunk's rows at positions L-Lq .. L-1 attend to keys 0..L-1
+ * held in pages (§3 Eq. 1, §3.2 Eqs. 4-5, §3.3 Eq. 6), under G(L).
+ *
+ *   q                [B, Lq, Hq, D]                 bf16
+ *   k_pages, v_pages [n_pages, page_size, Hkv, D]   bf16
+ *   block_table      [B, max_pages] int32 (device): key position p of
+ *                    sequence b is row p % page_size of page
+ *                    block_table[b * max_pages + p / page_size]
+ *   out, lse         as for jl_bifocal_prefill_chunk
+ *
+ * page_size must be a positive multiple of 128 (a 128-key tile never
+ * crosses a page) and max_pages * page_size >= L.  The workspace is the
+ * prefill's (jl_bifocal_prefill_workspace(JL_BF16, B, L, Hkv, D,
+ * w_pretrained) bytes); the keys in their remote view go there laid out by
+ * position, not by page.  Results are bit-identical to
+ * jl_bifocal_prefill_chunk over the same keys held contiguously.  A block
+ * table entry outside [0, n_pages) is never followed: every output row whose
+ * workgroup needs that page (at least every row at or after the page's first
+ * position) is written as NaN.
+ *
+ * Errors: as for jl_bifocal_prefill_chunk, plus JL_EINVAL for a NULL or
+ * misaligned block_table, a page_size that is not a positive multiple of 128,
+ * n_pages < 1 or max_pages * page_size < L; in_dtype other than JL_BF16 ->
+ * JL_EUNSUPPORTED.
+ */
+JL_API int jl_bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pages,
+                                          const int32_t* block_table, void* out, float* lse,
+                                          int in_dtype, int out_dtype, int64_t B, int64_t Lq,
+                                          int64_t L, int64_t n_pages, int64_t page_size,
+                                          int64_t max_pages, int64_t Hq, int64_t Hkv, int64_t D,
+                                          int64_t w0, int64_t w_pretrained, double rope_base,
+                                          float sm_scale, const void* table, size_t table_bytes,
+                                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * jl_bifocal_decode_workspace -- bytes of fp32 scratch that jl_bifocal_decode
  * needs for a step that attends L keys (split-KV partials).  Pure host call.
  */

@@ -26,10 +26,11 @@ def test_exports_every_declared_symbol():
     assert syms == sorted(["jl_last_error", "jl_version", "jl_schedule", "jl_bifocal_prefill_workspace",
                            "jl_bifocal_prefill", "jl_bifocal_prefill_chunk", "jl_bifocal_decode_workspace",
                            "jl_bifocal_decode", "jl_bifocal_decode_paged", "jl_table_fill_host",
-                           "jl_bifocal_prefill_unfused_workspace", "jl_bifocal_prefill_unfused"])
+                           "jl_bifocal_prefill_unfused_workspace", "jl_bifocal_prefill_unfused",
+                           "jl_bifocal_prefill_chunk_paged"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 5
+    assert jl.jl_version() == 6
 
 
 def test_schedule_golden_and_table_size():
@@ -161,6 +162,30 @@ def _chunk(**over):
 ])
 def test_prefill_chunk_validation(over, code):
     assert _chunk(**over) == code
+    assert jl.jl_last_error()
+
+
+def _chunk_paged(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, Lq=64, L=600,
+             npg=10, ps=128, mp=5, Hq=8, Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE, tb=1 << 30,
+             ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_prefill_chunk_paged(a["q"], a["k"], a["v"], a["bt"], a["out"], a["lse"], a["i"],
+                                                 a["o"], a["B"], a["Lq"], a["L"], a["npg"], a["ps"], a["mp"],
+                                                 a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"], a["base"], a["sc"],
+                                                 a["table"], a["tb"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(bt=None), jl.JL_EINVAL), (dict(bt=FAKE + 2), jl.JL_EINVAL), (dict(ps=64), jl.JL_EINVAL),
+    (dict(ps=192), jl.JL_EINVAL), (dict(ps=0), jl.JL_EINVAL), (dict(npg=0), jl.JL_EINVAL),
+    (dict(mp=4), jl.JL_EINVAL), (dict(mp=0), jl.JL_EINVAL), (dict(Lq=0), jl.JL_EINVAL),
+    (dict(Lq=601), jl.JL_EINVAL), (dict(q=None), jl.JL_EINVAL), (dict(D=96), jl.JL_EUNSUPPORTED),
+    (dict(i=jl.JL_F32, o=jl.JL_F32), jl.JL_EUNSUPPORTED), (dict(tb=100), jl.JL_ESPACE),
+    (dict(ws=None), jl.JL_ESPACE), (dict(wsb=600 * 2 * 128 * 2 - 1), jl.JL_ESPACE),
+])
+def test_prefill_chunk_paged_validation(over, code):
+    assert _chunk_paged(**over) == code
     assert jl.jl_last_error()
 
 

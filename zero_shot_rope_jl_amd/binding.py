@@ -51,6 +51,10 @@ def _load():
     L.jl_bifocal_prefill_unfused.restype = ctypes.c_int
     L.jl_bifocal_prefill_unfused.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                              i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
+    L.jl_bifocal_prefill_chunk_paged.restype = ctypes.c_int
+    L.jl_bifocal_prefill_chunk_paged.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                                 i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
+                                                 ctypes.c_float, vp, sz, vp, sz, vp]
     L.jl_bifocal_prefill_chunk.restype = ctypes.c_int
     L.jl_bifocal_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                            i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp,
@@ -267,6 +271,35 @@ def jl_bifocal_prefill_chunk(q, k_cache, v_cache, out, lse, L: int, w0: int, w_p
                                         w_pretrained, rope_base, sm_scale, _ptr(table),
                                         table.numel() * table.element_size(), _ptr(workspace), ws_bytes,
                                         _stream(stream)))
+    return out, lse
+
+
+def jl_bifocal_prefill_chunk_paged(q, k_pages, v_pages, block_table, out, lse, L: int, w0: int, w_pretrained: int,
+                                   rope_base: float, sm_scale: float, table, workspace=None, stream=None):
+    """q [B,Lq,Hq,D] bf16 at positions L-Lq..L-1; pages [n_pages, page_size, Hkv, D] bf16;
+    block_table [B, max_pages] int32; out [B,Lq,Hq,D]; lse [B,Hq,Lq] fp32 or None.  `workspace`
+    as for jl_bifocal_prefill (sized for L keys); allocated through torch when None and needed."""
+    torch = _torch()
+    _need_device(q, k_pages, v_pages, block_table, out, lse, table, workspace)
+    B, Lq, Hq, D = q.shape
+    n_pages, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("the pages must be [n_pages, page_size, Hkv, D] matching q")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if tuple(out.shape) != (B, Lq, Hq, D):
+        raise ValueError("out must be [B, Lq, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq, Lq) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq, Lq]")
+    if workspace is None:
+        n = jl_bifocal_prefill_workspace(_dtype_code(q), B, L, Hkv, D, w_pretrained)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.jl_bifocal_prefill_chunk_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(out),
+                                              _ptr(lse), _dtype_code(q), _dtype_code(out), B, Lq, L, n_pages,
+                                              page_size, block_table.shape[1], Hq, Hkv, D, w0, w_pretrained,
+                                              rope_base, sm_scale, _ptr(table), table.numel() * table.element_size(),
+                                              _ptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
 
 

@@ -67,7 +67,7 @@ extern "C" {
 
 JL_API const char* jl_last_error(void) { return g_err.c_str(); }
 
-JL_API int jl_version(void) { return 5; }
+JL_API int jl_version(void) { return 6; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -309,6 +309,45 @@ JL_API int jl_bifocal_prefill_unfused(const void* q, const void* k, const void* 
     m.D = D;
     const hipError_t e = jl::launch_ie_merge(m, out_dtype, stream);
     if (e != hipSuccess) return fail(JL_EHIP, "%s merge launch failed: %s", who, hipGetErrorString(e));
+    return JL_OK;
+}
+
+JL_API int jl_bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pages,
+                                          const int32_t* block_table, void* out, float* lse, int in_dtype,
+                                          int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t n_pages,
+                                          int64_t page_size, int64_t max_pages, int64_t Hq, int64_t Hkv, int64_t D,
+                                          int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale,
+                                          const void* table, size_t table_bytes, void* workspace,
+                                          size_t workspace_bytes, void* hip_stream) {
+    const char* who = "prefill_chunk_paged";
+    g_err.clear();
+    if (!block_table) return fail(JL_EINVAL, "%s: block_table must be non-NULL", who);
+    if (reinterpret_cast<uintptr_t>(block_table) & 3u)
+        return fail(JL_EINVAL, "%s: block_table must be 4-byte aligned", who);
+    if (int rc = check_prefill(who, q, k_pages, v_pages, out, lse, in_dtype, out_dtype, B, Lq, L, L, Hq, Hkv, D, w0,
+                               w_pretrained, rope_base, sm_scale, table, table_bytes, workspace))
+        return rc;
+    if (page_size < 128 || page_size % 128 != 0 || page_size > kMaxLen)
+        return fail(JL_EINVAL, "%s: page_size must be a positive multiple of 128 (got %lld)", who,
+                    (long long)page_size);
+    if (n_pages < 1 || max_pages < 1 || max_pages > kMaxLen || max_pages * page_size < L)
+        return fail(JL_EINVAL, "%s: need n_pages >= 1 and max_pages * page_size >= L (%lld, %lld, L=%lld)", who,
+                    (long long)n_pages, (long long)max_pages, (long long)L);
+    if (in_dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "%s reads a bf16 cache only", who);
+    size_t ws_need = 0;
+    jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D, w_pretrained, &ws_need);
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
+        return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                    ws_need);
+    jl::PrefillParams p = make_prefill_params(q, k_pages, v_pages, out, lse, B, Lq, L, L, Hq, Hkv, D, w0,
+                                              w_pretrained, rope_base, sm_scale, table, workspace);
+    p.block_table = block_table;
+    p.page_size = page_size;
+    p.max_pages = max_pages;
+    p.n_pages = n_pages;
+    (void)hipGetLastError();
+    hipError_t e = jl::launch_prefill(p, in_dtype, out_dtype, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
     return JL_OK;
 }
 

@@ -40,6 +40,11 @@ struct PrefillParams {
     int mode;
     // bf16 kernel only: krot already holds this call's rotated keys
     int krot_ready;
+    // paged caches (null block_table: k/v are [B, Lkv, Hkv, D]): key k of
+    // sequence b is row k % page_size of page block_table[b * max_pages +
+    // k / page_size] of k/v, which hold n_pages pages of page_size rows
+    const int32_t* block_table;
+    int64_t page_size, max_pages, n_pages;
 };
 
 enum PrefillMode {

@@ -309,8 +309,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const T* __restrict__ vg = static_cast<const T*>(p.v);
     const float2* __restrict__ TF = p.TF;
     const int64_t kv_row = (int64_t)Hkv * D;
-    const T* __restrict__ kbase = kg + (int64_t)b * Lkv * kv_row + (int64_t)g * D;
-    const T* __restrict__ vbase = vg + (int64_t)b * Lkv * kv_row + (int64_t)g * D;
+    const bool paged = p.block_table != nullptr;
+    const int64_t kv_b = paged ? 0 : (int64_t)b * Lkv * kv_row;
+    const T* __restrict__ kbase = kg + kv_b + (int64_t)g * D;
+    const T* __restrict__ vbase = vg + kv_b + (int64_t)g * D;
+    // Cache row of key k0 (a multiple of BN).  Paged caches: the page size is
+    // a multiple of BN, so a tile lies in one page.  An entry outside
+    // [0, n_pages) reads page 0 instead and this workgroup's rows are
+    // written as NaN, so no load leaves the pages.
+    bool bad_page = false;
+    auto cache_row = [&](int k0) -> int64_t {
+        if (!paged) return k0;
+        const int ps = (int)p.page_size;
+        int pg = p.block_table[(int64_t)b * p.max_pages + k0 / ps];
+        if (pg < 0 || pg >= p.n_pages) {
+            bad_page = true;
+            pg = 0;
+        }
+        return (int64_t)pg * ps + k0 % ps;
+    };
 
     if (p.fixup) {
         // Fixup pass: only a workgroup with a marked row (NaN in element 0)
@@ -390,10 +407,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const int v0 = (tid & 7) * Lay::VPT; // V: first dim of this thread
     auto pass_k0 = [&](int pi) { return (pi < nR ? r0 + pi : nL0 + (pi - nR)) * BN; };
     auto stage_load = [&](int pi) {
-        const int kpos = pass_k0(pi) + kr;
+        const int tk0 = pass_k0(pi);
+        const int kpos = tk0 + kr;
         const bool ok = kpos < L;
-        const T* krow = kbase + (int64_t)(ok ? kpos : 0) * kv_row;
-        const T* vrow = vbase + (int64_t)(ok ? kpos : 0) * kv_row;
+        // the tile's first key is below L, so its row exists; rows past L
+        // read that row and are zeroed below
+        const int64_t trow = cache_row(tk0);
+        const int64_t crow = ok ? trow + kr : trow;
+        const T* krow = kbase + crow * kv_row;
+        const T* vrow = vbase + crow * kv_row;
         st.x = ok ? *reinterpret_cast<const typename St::KV*>(krow + f0) : typename St::KV{};
         st.y = ok ? *reinterpret_cast<const typename St::KV*>(krow + HALF + f0) : typename St::KV{};
         st.v = ok ? *reinterpret_cast<const typename St::VV*>(vrow + v0) : typename St::VV{};
@@ -479,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     // ---- epilogue ---------------------------------------------------------------
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (q_ok) {
-        const float inv = 1.f / l_tot;
+        const float inv = bad_page ? NAN : 1.f / l_tot;
         const int64_t o = (((int64_t)b * Lq + (my_q - q_off)) * Hq + head) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -500,7 +522,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             }
         }
         if (hh == 0 && p.lse)
-            p.lse[((int64_t)b * Hq + head) * Lq + (my_q - q_off)] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+            p.lse[((int64_t)b * Hq + head) * Lq + (my_q - q_off)] =
+                bad_page ? NAN : (m_run + log2f(l_tot)) * 0.69314718055994531f;
     }
 }
 

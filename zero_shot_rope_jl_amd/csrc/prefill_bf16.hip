@@ -89,7 +89,7 @@ __device__ inline int vswz(int row, int c) {
     return c ^ ((4 * (row & 3)) & (Lay5<D>::CH - 1));
 }
 
-template <int D, bool OUT_BF16, int MODE>
+template <int D, bool OUT_BF16, int MODE, bool PAGED>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p) {
     using Lay = Lay5<D>;
     constexpr int HALF = Lay::HALF;
@@ -156,8 +156,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const float2* __restrict__ TF = p.TF;
     const int64_t kv_row = (int64_t)Hkv * D;
     const uint32_t row_bytes = (uint32_t)kv_row * 2u;
-    const __bf16* __restrict__ kbase = static_cast<const __bf16*>(p.k) + (int64_t)b * Lkv * kv_row + (int64_t)g * D;
-    const __bf16* __restrict__ vbase = static_cast<const __bf16*>(p.v) + (int64_t)b * Lkv * kv_row + (int64_t)g * D;
+    const int64_t kv_b = PAGED ? 0 : (int64_t)b * Lkv * kv_row;
+    const __bf16* __restrict__ kbase = static_cast<const __bf16*>(p.k) + kv_b + (int64_t)g * D;
+    const __bf16* __restrict__ vbase = static_cast<const __bf16*>(p.v) + kv_b + (int64_t)g * D;
     // keys in their corrected view (only read by remote tiles, which exist only
     // when G > 1), laid out like k with L rows per batch entry
     const __bf16* __restrict__ krbase =
@@ -272,6 +273,27 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     for (int u = 0; u < KU; ++u) k_voff[u] = k_slot_voff((u * kWaves + wave) * 64 + lane);
     k_voff[KU] = wave < KREM ? k_slot_voff((KU * kWaves + wave) * 64 + lane) : 0u;
     auto tile_k0 = [&](int pi) __attribute__((always_inline)) { return (pi < nR ? r0 + pi : nL0 + (pi - nR)) * BN; };
+    // Cache row of key k0 (a multiple of BN).  Paged caches: BN divides the
+    // page size, so a tile lies in one page; its block-table entry is read
+    // through the constant address space (a scalar load: the table is not
+    // written during the kernel).  An entry outside [0, n_pages) reads page
+    // 0 instead and marks this workgroup's rows, which the fixup pass then
+    // writes as NaN, so no load leaves the pages.
+    bool bad_page = false;
+    auto cache_row = [&](int k0) __attribute__((always_inline)) -> int64_t {
+        if constexpr (!PAGED) {
+            return k0;
+        } else {
+            typedef const __attribute__((address_space(4))) int32_t* ctab;
+            const int ps = (int)p.page_size;
+            int pg = ((ctab)(p.block_table + (int64_t)b * p.max_pages))[k0 / ps];
+            if (pg < 0 || pg >= p.n_pages) {
+                bad_page = true;
+                pg = 0;
+            }
+            return (int64_t)pg * ps + k0 % ps;
+        }
+    };
     // staging is issued in two parts spread over the tile, so that the
     // vector-memory queue never fills and stalls the wave: K at the start, V
     // with the first PV half
@@ -279,7 +301,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         char* sKd = reinterpret_cast<char*>(decltype(buf)::value ? sK1 : sK0);
         const int k0 = tile_k0(pi);
         const uint32_t tile_bytes = (uint32_t)min(L - k0, BN) * row_bytes;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc((pi < nR ? krbase : kbase) + (int64_t)k0 * kv_row, tile_bytes);
+        // corrected-view tiles read the rotated keys, laid out by position
+        const __bf16* src = pi < nR ? krbase + (int64_t)k0 * kv_row : kbase + cache_row(k0) * kv_row;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(src, tile_bytes);
 #pragma unroll
         for (int u = 0; u < KU; ++u) buffer_lds16(rk, sKd + (u * kWaves + wave) * 1024, k_voff[u], 0);
         if (KREM > 0 && wave < KREM) buffer_lds16(rk, sKd + (KU * kWaves + wave) * 1024, k_voff[KU], 0);
@@ -289,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         const int k0 = tile_k0(pi);
         const uint32_t tile_bytes = (uint32_t)min(L - k0, BN) * row_bytes;
         // V: BN rows x CH chunks, VRU rows per copy step
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)k0 * kv_row, tile_bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + cache_row(k0) * kv_row, tile_bytes);
 #pragma unroll
         for (int u = 0; u < VU; ++u)
             buffer_lds16(rv, &sVd[(u * kWaves + wave) * 64 * 8], v_voff, (uint32_t)(u * VRU) * row_bytes);
@@ -532,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) finite = finite && fabsf(acc[j][db][i] * inv) < INFINITY;
-        const bool row_ok = finite && __shfl_xor((int)finite, 32);
+        const bool row_ok = finite && __shfl_xor((int)finite, 32) && !bad_page;
         if (!qok[j]) continue;
         const int64_t o = (((int64_t)b * Lq + (my_q[j] - q_off)) * Hq + head[j]) * D;
 #pragma unroll
@@ -565,10 +589,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 // floor(k/G), rounded to bf16.  One thread per 8 rotation pairs of a row;
 // HBM-bound (one read and one write of K, table rows shared by the KV heads
 // of a position through L2).
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kr,
                                                           const float2* __restrict__ TF, int64_t n_items, int64_t L,
-                                                          int64_t Lkv, int Hkv, int64_t G) {
+                                                          int64_t Lkv, int Hkv, int64_t G, PrefillParams pp) {
     constexpr int HALF = D / 2;
     constexpr int CPR = HALF / 8;   // 8-pair items per row
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -578,8 +602,18 @@ __global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restri
     const int64_t bp = row / Hkv;
     const int64_t pos = bp % L;
     const int64_t n = pos - pos / G;
-    // k holds Lkv rows per batch entry, the output L
-    const __bf16* src = k + (((bp / L) * Lkv + pos) * Hkv + row % Hkv) * D + 8 * c;
+    // k holds Lkv rows per batch entry (or pages), the output L
+    int64_t crow;
+    if constexpr (PAGED) {
+        // an entry outside [0, n_pages) reads page 0; the attention kernel
+        // marks the rows that use it
+        int64_t pg = pp.block_table[(bp / L) * pp.max_pages + pos / pp.page_size];
+        pg = (pg < 0 || pg >= pp.n_pages) ? 0 : pg;
+        crow = pg * pp.page_size + pos % pp.page_size;
+    } else {
+        crow = (bp / L) * Lkv + pos;
+    }
+    const __bf16* src = k + (crow * Hkv + row % Hkv) * D + 8 * c;
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(src);
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(src + HALF);
     const float4* cs = reinterpret_cast<const float4*>(TF + n * HALF + 8 * c);
@@ -601,22 +635,23 @@ __global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restri
     *reinterpret_cast<bf16x8*>(dst + HALF) = yo;
 }
 
-template <int D, bool OUT_BF16, int MODE>
+template <int D, bool OUT_BF16, int MODE, bool PAGED = false>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
     if (p.G > 1 && MODE != kLocalWindow && !p.krot_ready) {
         const int64_t n_items = p.B * p.L * p.Hkv * (D / 16);
-        hipLaunchKernelGGL((rotate_keys_kernel<D>), dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0, stream,
-                           static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.krot), p.TF, n_items, p.L,
-                           p.Lkv, (int)p.Hkv, p.G);
+        hipLaunchKernelGGL((rotate_keys_kernel<D, PAGED>), dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0,
+                           stream, static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.krot), p.TF, n_items, p.L,
+                           p.Lkv, (int)p.Hkv, p.G, p);
     }
     const int64_t blocks = (int64_t)p.n_qtiles * p.Hkv * p.B;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16, MODE>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16, MODE, PAGED>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
 template <int D, bool OUT_BF16>
 hipError_t launch_mode(const PrefillParams& p, hipStream_t stream) {
+    if (p.block_table) return launch_one<D, OUT_BF16, kFused, true>(p, stream);   // paged caches: fused only
     switch (p.mode) {
         case kLocalWindow: return launch_one<D, OUT_BF16, kLocalWindow>(p, stream);
         case kRemoteAll: return launch_one<D, OUT_BF16, kRemoteAll>(p, stream);
