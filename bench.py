@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query rows in the CPU-oracle sample")
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--chunk-steps", type=int, default=5,
+                    help="calls of the last-4096-token chunk timed, contiguous and paged (0 skips it)")
     ap.add_argument("--unfused-steps", type=int, default=3,
                     help="calls of the unfused three-pass prefill timed (0 skips it)")
     ap.add_argument("--control-steps", type=int, default=5,
@@ -181,6 +183,48 @@ def bench_unfused(torch, jl, args, w, x):
     del q, k, v, out, lse, ws
     torch.cuda.empty_cache()
     return ms
+
+
+def bench_chunk(torch, jl, args, w, x, Lq=4096, page_size=256):
+    """The last Lq-token chunk of the workload over its cache, contiguous and
+    held in shuffled pages (jl_bifocal_prefill_chunk / _chunk_paged)."""
+    q, k, v = (to_dev(torch, x[n], w.dtype) for n in "qkv")
+    qc = q[:, w.L - Lq:].contiguous()
+    del q
+    out = torch.empty((w.B, Lq, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    table = jl.alloc_table(w.L, w.D, w.rope_base)
+    ws = jl.alloc_prefill_workspace(k, w.w_pretrained)
+    max_pages = (w.L + page_size - 1) // page_size
+    perm = np.random.Generator(np.random.PCG64([w.seed, 23])).permutation(w.B * max_pages)
+    kp = torch.empty((w.B * max_pages, page_size, w.Hkv, w.D), dtype=k.dtype, device="cuda")
+    vp = torch.empty_like(kp)
+    for b in range(w.B):
+        idx = torch.from_numpy(perm[b * max_pages:(b + 1) * max_pages].astype(np.int64)).cuda()
+        kp[idx] = k[b].view(max_pages, page_size, w.Hkv, w.D)
+        vp[idx] = v[b].view(max_pages, page_size, w.Hkv, w.D)
+    bt = torch.from_numpy(perm.reshape(w.B, max_pages).astype(np.int32)).cuda()
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, call in (("contiguous", lambda: jl.jl_bifocal_prefill_chunk(
+                            qc, k, v, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table,
+                            workspace=ws)),
+                       ("paged_256", lambda: jl.jl_bifocal_prefill_chunk_paged(
+                            qc, kp, vp, bt, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table,
+                            workspace=ws))):
+        call()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.chunk_steps):
+            call()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round(ev0.elapsed_time(ev1) / args.chunk_steps, 4)
+    log(f"[bench] last {Lq}-token chunk: {res['contiguous_ms']:.3f} ms contiguous, "
+        f"{res['paged_256_ms']:.3f} ms over 256-key pages")
+    del k, v, qc, out, kp, vp, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(torch, jl, si, args):
@@ -360,6 +404,9 @@ def main():
             "what": "three separate passes (stored view over the window, corrected view over all keys and over "
                     "the window) and their inclusion-exclusion merge",
             "ms_per_call": round(ums, 4), "fused_speedup": round(ums / ms, 4)}
+    if args.chunk_steps > 0:
+        result["chunk"] = {"what": "last 4096 tokens of the workload as one chunk over the other 126976 keys",
+                           **bench_chunk(torch, jl, args, w, x)}
     if not args.skip_decode:
         dw, us, gbs, bytes_step, us_median, extra = bench_decode(torch, jl, si, args)
         result["decode"] = {
