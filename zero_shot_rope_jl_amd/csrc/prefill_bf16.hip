@@ -359,44 +359,22 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
                 s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[j][c], c == 0 ? negm[j] : s[j], 0, 0, 0);
         }
     };
-    // O^T += V^T P^T for one 32-key half; each V^T fragment feeds every block.
-    auto pv = [&](const __bf16* V, int kb, const bf16x8 (&P)[NJ][2]) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int r0 = 32 * kb + 16 * h + tr_row;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                // logical chunk of dims 32db + tr_dim and its swizzled place
-                const int lc = (32 * db + tr_dim) >> 3;
-                const int wi = tr_dim & 7;
-                const bf16x4 lo = lds_read_tr16(V + r0 * D + 8 * vswz<D>(r0, lc) + wi);
-                const bf16x4 hi = lds_read_tr16(V + (r0 + 4) * D + 8 * vswz<D>(r0 + 4, lc) + wi);
-                const bf16x8 A = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    acc[j][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[j][h], acc[j][db], 0, 0, 0);
-            }
-        }
+    // One MFMA operand fragment from LDS: K rows of 32-key block kb, chunk c
+    // (the A operand of S^T = K Q^T), or V^T fragment t = 4h + db of block kb
+    // (the A operand of O^T += V^T P^T: dims 32db.., keys 16h.. of the block)
+    // through the transposing read.
+    auto kfrag = [&](const __bf16* K, int kb, int c) __attribute__((always_inline)) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(K + (32 * kb + krow_l) * KSTR + 8 * hh + 16 * c);
     };
-    // P = exp2(S - m_ref) as rounded for the MFMA, and the row sums of those
-    // rounded values.
-    auto probs = [&](const f32x16 (&s)[NJ], bf16x8 (&P)[NJ][2]) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) P[j][h][e] = (__bf16)fast_exp2(s[j][8 * h + e]);
-            float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][0], P[j][h][1]}, ones, ls0, false);
-                ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][2], P[j][h][3]}, ones, ls1, false);
-                ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][4], P[j][h][5]}, ones, ls0, false);
-                ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[j][h][6], P[j][h][7]}, ones, ls1, false);
-            }
-            l_run[j] += ls0 + ls1;
-        }
+    auto vfrag = [&](const __bf16* V, int kb, int t) __attribute__((always_inline)) -> bf16x8 {
+        const int h = t / NDB, db = t % NDB;
+        const int r0 = 32 * kb + 16 * h + tr_row;
+        // logical chunk of dims 32db + tr_dim and its swizzled place
+        const int lc = (32 * db + tr_dim) >> 3;
+        const int wi = tr_dim & 7;
+        const bf16x4 lo = lds_read_tr16(V + r0 * D + 8 * vswz<D>(r0, lc) + wi);
+        const bf16x4 hi = lds_read_tr16(V + (r0 + 4) * D + 8 * vswz<D>(r0 + 4, lc) + wi);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
     // Window-edge, causal-diagonal and ragged tiles mask scores per element;
@@ -460,46 +438,100 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         }
     };
 
-    // One tile as straight-line regions, so that MFMAs and VALU work
-    // interleave: S(b+1) with softmax(b), then PV(b), for each 32-key block
-    // b.  S(0) is issued by the caller right after the barrier.  The rare
-    // edge work sits in uniform branches between regions and never touches
-    // the accumulators.
-    constexpr int NKB = BN / 32;   // 32-key score blocks per tile
-    auto tile_body = [&](auto buf, int pn, bool edge, bool rem, int k0, f32x16 (&s0)[NJ]) __attribute__((always_inline)) {
+    // One region: PV of block kbp (with its probabilities Pold), the scores
+    // of block kbq into Snew, and the probabilities of the scores Scur into
+    // Pnew with their row sums.  The three are independent, so the region is
+    // written in the order it should issue, fenced by scheduling barriers:
+    // PV and score MFMAs alternate, each operand fragment is read from LDS
+    // PFD MFMAs ahead of its use, and each MFMA is followed by its share of
+    // the exponentials, bf16 packs and row-sum dot products.  The row sum is
+    // pinned in the region: left alone, the compiler sinks every row sum to
+    // the tile's end, which keeps all four blocks' probabilities live and
+    // leaves no registers for the fragments in flight.
+    static_assert(NJ == 1, "the region schedule assumes one query block per wave");
+    constexpr int PFD = 3;
+    auto region = [&](auto has_pv, auto has_qk, auto has_probs, const __bf16* K, const __bf16* V, int kbp, int kbq,
+                      const bf16x8 (&Pold)[NJ][2], f32x16 (&Snew)[NJ], const f32x16 (&Scur)[NJ],
+                      bf16x8 (&Pnew)[NJ][2]) __attribute__((always_inline)) {
+        constexpr bool HP = decltype(has_pv)::value, HQ = decltype(has_qk)::value;
+        constexpr bool HPR = decltype(has_probs)::value;
+        constexpr int M = (HP ? 2 * NDB : 0) + (HQ ? NC : 0);   // MFMAs in the region
+        constexpr int PER = HPR ? 16 / M : 0;                    // exponentials per MFMA
+        auto is_pv = [](int m) { return (HP && HQ) ? (m & 1) == 0 : HP; };
+        auto idx = [](int m) { return (HP && HQ) ? (m >> 1) : m; };
+        auto frag = [&](int m) __attribute__((always_inline)) {
+            return is_pv(m) ? vfrag(V, kbp, idx(m)) : kfrag(K, kbq, idx(m));
+        };
+        bf16x8 F[M];
+#pragma unroll
+        for (int m = 0; m < PFD && m < M; ++m) F[m] = frag(m);
+        float pe[16];
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            if (m + PFD < M) F[m + PFD] = frag(m + PFD);
+            if (is_pv(m)) {
+                const int t = idx(m), h = t / NDB, db = t % NDB;
+                acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[m], Pold[0][h], acc[0][db], 0, 0, 0);
+            } else {
+                // the chain of block kbq starts from -m_ref
+                const int c = idx(m);
+                Snew[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[m], qv[0][c], c == 0 ? negm[0] : Snew[0], 0, 0, 0);
+            }
+            if (HPR) {
+                // P = exp2(S - m_ref) as rounded for the MFMA, and the row sums
+                // of those rounded values
+#pragma unroll
+                for (int e = m * PER; e < (m + 1) * PER; ++e) {
+                    pe[e] = fast_exp2(Scur[0][e]);
+                    if (e & 1) {
+                        const int h = e / 8, i = e % 8;
+                        Pnew[0][h][i - 1] = (__bf16)pe[e - 1];
+                        Pnew[0][h][i] = (__bf16)pe[e];
+                        const bf16x2 pr = {Pnew[0][h][i - 1], Pnew[0][h][i]};
+                        if (((i - 1) / 2) % 2 == 0) ls0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls0, false);
+                        else ls1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls1, false);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (HPR) {
+            l_run[0] += ls0 + ls1;
+            asm volatile("" : "+v"(l_run[0]));
+            // the probabilities stay in this region too, not beside their PV
+            asm volatile("" ::"v"(Pnew[0][0]), "v"(Pnew[0][1]));
+        }
+    };
+
+    // One tile: S(0) was issued by the caller right after the barrier; then
+    // the regions S(1)+softmax(0), PV(0)+S(2)+softmax(1), PV(1)+S(3)+softmax(2),
+    // PV(2)+softmax(3) and PV(3).  The rare edge work (masks, reference max)
+    // sits in uniform branches between regions and never touches the
+    // accumulators.
+    static_assert(BN == 128, "four 32-key score blocks per tile");
+    auto tile_body = [&](auto buf, int pn, bool edge, bool rem, int k0, f32x16 (&S0)[NJ]) __attribute__((always_inline)) {
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
+        using T = std::true_type;
+        using F = std::false_type;
         const __bf16* K = decltype(buf)::value ? sK1 : sK0;
         const __bf16* V = decltype(buf)::value ? sV1 : sV0;
-        f32x16 sa[NJ], sb[NJ];
-        bf16x8 Pa[NJ][2];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) sa[j] = s0[j];
-        if (edge) edge_fix(sa, 0, rem, k0);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            // the scores of block kb are in sa; block kb + 1 goes into sb
-            // the wave issuing score MFMAs wins issue arbitration against its
-            // SIMD partner (about 0.5% at 128K)
-            __builtin_amdgcn_s_setprio(1);
-            if (kb + 1 < NKB) qk(K, kb + 1, sb);
-            __builtin_amdgcn_s_setprio(0);
-            probs(sa, Pa);
-            // keep softmax(kb) in the region of S(kb + 1): without a use here
-            // the compiler sinks it below the branch, next to PV(kb)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) asm volatile("" ::"v"(Pa[j][0]), "v"(Pa[j][1]));
-            if (kb + 1 < NKB && edge) edge_fix(sb, kb + 1, rem, k0);
-            if (kb == 0) {
-                stage_load_v(pn, Other{});
-                // the copies have no users in the kernel's data flow; left
-                // alone the scheduler sinks them to the tile's end, where the
-                // closing wait would then see their whole latency
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            pv(V, kb, Pa);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) sa[j] = sb[j];
-        }
+        f32x16 S1[NJ], S2[NJ], S3[NJ];
+        bf16x8 P0[NJ][2], P1[NJ][2], P2[NJ][2], P3[NJ][2];
+        if (edge) edge_fix(S0, 0, rem, k0);
+        region(F{}, T{}, T{}, K, V, 0, 1, P3, S1, S0, P0);   // P3 unused (no PV)
+        if (edge) edge_fix(S1, 1, rem, k0);
+        stage_load_v(pn, Other{});
+        // the copies have no users in the kernel's data flow; left alone the
+        // scheduler sinks them to the tile's end, where the closing wait would
+        // then see their whole latency
+        __builtin_amdgcn_sched_barrier(0);
+        region(T{}, T{}, T{}, K, V, 0, 2, P0, S2, S1, P1);
+        if (edge) edge_fix(S2, 2, rem, k0);
+        region(T{}, T{}, T{}, K, V, 1, 3, P1, S3, S2, P2);
+        if (edge) edge_fix(S3, 3, rem, k0);
+        region(T{}, F{}, T{}, K, V, 2, 0, P2, S1, S3, P3);    // S1 unused (no scores)
+        region(T{}, F{}, F{}, K, V, 3, 0, P3, S1, S3, P0);    // PV only
     };
 
     using Buf0 = std::integral_constant<int, 0>;
