@@ -388,7 +388,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.L, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": pick(traffic, "jl::prefill_bf16_kernel<128, true, 0>"),
+                     "traffic": pick(traffic, "jl::prefill_bf16_kernel<128, true, 0, false>"),
                      "flops_per_launch": flops},
         "prefill_ms_per_call": pstats,
     }

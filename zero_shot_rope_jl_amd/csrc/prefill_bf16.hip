@@ -347,18 +347,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     const int tr_dim = 16 * (Gq & 1) + 4 * (cq & 3);
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // S^T - m_ref for one 32-key block, every query block of the wave (each K
-    // fragment feeds all of them); the chain starts from -m_ref.
-    auto qk = [&](const __bf16* K, int kb, f32x16 (&s)[NJ]) {
-        const __bf16* kp = K + (32 * kb + krow_l) * KSTR + 8 * hh;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const bf16x8 A = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qv[j][c], c == 0 ? negm[j] : s[j], 0, 0, 0);
-        }
-    };
     // One MFMA operand fragment from LDS: K rows of 32-key block kb, chunk c
     // (the A operand of S^T = K Q^T), or V^T fragment t = 4h + db of block kb
     // (the A operand of O^T += V^T P^T: dims 32db.., keys 16h.. of the block)
@@ -504,7 +492,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         }
     };
 
-    // One tile: S(0) was issued by the caller right after the barrier; then
+    // One tile: S(0) was issued by the caller right after the barrier (a
+    // region of its own); then
     // the regions S(1)+softmax(0), PV(0)+S(2)+softmax(1), PV(1)+S(3)+softmax(2),
     // PV(2)+softmax(3) and PV(3).  The rare edge work (masks, reference max)
     // sits in uniform branches between regions and never touches the
@@ -541,9 +530,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
         if (pi == nR && nR > 0) load_q(false);   // the local phase starts: stored Q
         // the first score MFMAs go out right after the barrier, ahead of the
-        // tile's scalar set-up
+        // tile's scalar set-up: a region with S(0) only
         f32x16 s0[NJ];
-        qk(decltype(buf)::value ? sK1 : sK0, 0, s0);
+        {
+            bf16x8 noP[NJ][2];   // not read: the region has no PV and no softmax
+            f32x16 noS[NJ];
+            region(std::false_type{}, std::true_type{}, std::false_type{}, decltype(buf)::value ? sK1 : sK0,
+                   decltype(buf)::value ? sV1 : sV0, 0, 0, noP, s0, noS, noP);
+        }
         const int pn = pi + 1 < NP ? pi + 1 : pi;   // the last tile refills the idle buffer
         stage_load_k(pn, Other{});
         const bool rem = pi < nR;
