@@ -316,16 +316,41 @@ def bench_decode(torch, jl, si, args):
     us_graph = ev0.elapsed_time(ev1) * 1e3 / dw.steps
     graph_ok = bool(torch.equal(out, eager_out))
     del graph
+
+    # the same steps with a rotated-key cache: each timed pass starts from an
+    # empty cache, so its first step rotates every remote key and the later
+    # steps one new row each; that cost is inside the per-step figure
+    rkc = jl.RotatedKeyCache(kc)
+
+    def rkc_pass():
+        rkc.reset()
+        for s in range(dw.steps):
+            L = dw.prompt_len + s + 1
+            jl.jl_bifocal_decode_rkc(qs[s], kc, vc, rkc, out, None, L, dw.w0, dw.w_pretrained, dw.rope_base,
+                                     dw.sm_scale, table, ws)
+
+    rkc_pass()
+    ev0.record(stream)
+    for _ in range(args.decode_passes):
+        rkc_pass()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_rkc = ev0.elapsed_time(ev1) * 1e3 / (args.decode_passes * dw.steps)
+    rkc_ok = bool((out.float() - eager_out.float()).abs().max().item() <= 2e-2)
+    del rkc
     mean_L = dw.prompt_len + (dw.steps + 1) / 2.0
     bytes_step = 2.0 * dw.B * mean_L * dw.Hkv * dw.D * 2
     gbs = bytes_step / (us * 1e-6) / 1e9
     log(f"[bench] decode {us:.2f} us/step (per-step median {us_median:.2f}, paged cache {us_paged:.2f}, "
-        f"graph {us_graph:.2f}{'' if graph_ok else ' MISMATCH'}), {gbs:.0f} GB/s")
+        f"graph {us_graph:.2f}{'' if graph_ok else ' MISMATCH'}, rotated-key cache {us_rkc:.2f}"
+        f"{'' if rkc_ok else ' MISMATCH'}), {gbs:.0f} GB/s")
     del kc, vc
     torch.cuda.empty_cache()
     return dw, us, gbs, bytes_step, us_median, {"us_per_step_paged_256": round(us_paged, 3),
                                                "us_per_step_graph": round(us_graph, 3),
-                                               "graph_matches_eager": graph_ok}
+                                               "graph_matches_eager": graph_ok,
+                                               "us_per_step_rotated_keys": round(us_rkc, 3),
+                                               "rotated_keys_match": rkc_ok}
 
 
 def cpu_baseline(si, w, x, n_rows):

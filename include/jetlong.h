@@ -302,6 +302,49 @@ JL_API int jl_bifocal_decode_paged(const void* q, const void* k_pages, const voi
                             void* hip_stream);
 
 /*
+ * jl_rotated_keys -- host-side state of a rotated-key cache: the rows
+ * 0 .. rows-1 of the cache hold their keys in the remote view under group
+ * size G.  Start from {0, 0}; the library updates it on each call.
+ */
+typedef struct jl_rotated_keys {
+    int64_t G;
+    int64_t rows;
+} jl_rotated_keys;
+
+/*
+ * jl_bifocal_decode_rkc -- jl_bifocal_decode with a rotated-key cache: the
+ * same step (§3.2 Eqs. 4-5), with every remote key read already in its
+ * remote view R(f(k) - k)·k from `krot_cache` instead of being rotated as it
+ * is read.  k_cache itself is never written.
+ *
+ *   krot_cache [B, Lmax, Hkv, D] bf16, caller-owned, laid out like k_cache
+ *   state      host jl_rotated_keys describing krot_cache; {0, 0} for a new
+ *              cache (or after the caller rewrites rows of k_cache it covers)
+ *
+ * Before the step the call enqueues, on `hip_stream`, the rotation of the
+ * rows that the step needs and `state` does not cover: every row
+ * k < L-1-w0 under this step's G.  The step itself also writes row L-1-w0
+ * (still local) rotated under G, the row the next step reads as remote, so
+ * consecutive steps under one G enqueue no rotation; when G changes (every
+ * w_pretrained tokens) the rotation covers every remote row (one pass over
+ * the keys).  After a step with remote keys, state = {G, L-w0}.  `state` is
+ * updated at enqueue time, so calls that share a cache must be ordered on
+ * one stream.  The result equals jl_bifocal_decode's up to bf16 rounding
+ * (the remote view of each key is rounded once, in the cache).  Everything
+ * else as for jl_bifocal_decode.
+ *
+ * Errors: as for jl_bifocal_decode, plus JL_EINVAL for a NULL or
+ * misaligned krot_cache, a NULL state, or state->rows outside [0, Lmax].
+ */
+JL_API int jl_bifocal_decode_rkc(const void* q, const void* k_cache, const void* v_cache,
+                                 void* krot_cache, jl_rotated_keys* state, void* out, float* lse,
+                                 int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Lmax,
+                                 int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                                 int64_t w_pretrained, double rope_base, float sm_scale,
+                                 const void* table, size_t table_bytes, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
+
+/*
  * jl_table_fill_host -- fill a HOST buffer with the same table jl_schedule
  * writes on the device (same layout, same float64 formulas compiled for the
  * host).  Lets the table builder be checked without a GPU.  Errors as for

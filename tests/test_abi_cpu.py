@@ -27,10 +27,10 @@ def test_exports_every_declared_symbol():
                            "jl_bifocal_prefill", "jl_bifocal_prefill_chunk", "jl_bifocal_decode_workspace",
                            "jl_bifocal_decode", "jl_bifocal_decode_paged", "jl_table_fill_host",
                            "jl_bifocal_prefill_unfused_workspace", "jl_bifocal_prefill_unfused",
-                           "jl_bifocal_prefill_chunk_paged"])
+                           "jl_bifocal_prefill_chunk_paged", "jl_bifocal_decode_rkc"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 6
+    assert jl.jl_version() == 7
 
 
 def test_schedule_golden_and_table_size():
@@ -187,6 +187,31 @@ def _chunk_paged(**over):
 def test_prefill_chunk_paged_validation(over, code):
     assert _chunk_paged(**over) == code
     assert jl.jl_last_error()
+
+
+def _decode_rkc(state, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kr=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, L=600, Lmax=700,
+             Hq=8, Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE, tb=1 << 30, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_decode_rkc(a["q"], a["k"], a["v"], a["kr"], state, a["out"], a["lse"], a["i"], a["o"],
+                                        a["B"], a["L"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"],
+                                        a["base"], a["sc"], a["table"], a["tb"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,rows,code", [
+    (dict(kr=None), 0, jl.JL_EINVAL), (dict(kr=FAKE + 8), 0, jl.JL_EINVAL), (dict(), -1, jl.JL_EINVAL),
+    (dict(), 701, jl.JL_EINVAL), (dict(Lmax=599), 0, jl.JL_EINVAL), (dict(ws=None), 0, jl.JL_EINVAL),
+    (dict(i=jl.JL_F32, o=jl.JL_F32), 0, jl.JL_EUNSUPPORTED), (dict(tb=100), 0, jl.JL_ESPACE),
+])
+def test_decode_rkc_validation_leaves_state_alone(over, rows, code):
+    st = jl.JLRotatedKeys(3, rows)
+    assert _decode_rkc(ctypes.byref(st), **over) == code
+    assert jl.jl_last_error()
+    assert (st.G, st.rows) == (3, rows)
+
+
+def test_decode_rkc_null_state():
+    assert _decode_rkc(None) == jl.JL_EINVAL
 
 
 def _decode(**over):

@@ -17,6 +17,12 @@ class JetLongError(RuntimeError):
         self.code = code
 
 
+class JLRotatedKeys(ctypes.Structure):
+    """jl_rotated_keys: rows 0..rows-1 of a rotated-key cache hold their keys in
+    the remote view under group size G."""
+    _fields_ = [("G", ctypes.c_int64), ("rows", ctypes.c_int64)]
+
+
 def _load():
     # PyTorch-ROCm ships its own HIP runtime (torch/lib/libamdhip64.so).  If
     # libjetlong.so were loaded first, the process would map two HIP/HSA
@@ -64,6 +70,10 @@ def _load():
     L.jl_bifocal_decode.restype = ctypes.c_int
     L.jl_bifocal_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                     i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
+    L.jl_bifocal_decode_rkc.restype = ctypes.c_int
+    L.jl_bifocal_decode_rkc.argtypes = [vp, vp, vp, vp, ctypes.POINTER(JLRotatedKeys), vp, vp, ctypes.c_int,
+                                        ctypes.c_int, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
+                                        ctypes.c_float, vp, sz, vp, sz, vp]
     L.jl_bifocal_decode_paged.restype = ctypes.c_int
     L.jl_bifocal_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                           i64, i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz,
@@ -332,6 +342,43 @@ def jl_bifocal_decode(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrain
                                  w_pretrained, rope_base, sm_scale, _ptr(table),
                                  table.numel() * table.element_size(), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+class RotatedKeyCache:
+    """A rotated-key cache for jl_bifocal_decode_rkc: device keys laid out like
+    the key cache they cover, and the host state the library keeps current.
+    Call reset() after rewriting rows of the key cache that it covers."""
+
+    def __init__(self, k_cache):
+        self.keys = _torch().empty_like(k_cache)
+        self.state = JLRotatedKeys(0, 0)
+
+    def reset(self):
+        self.state.G = 0
+        self.state.rows = 0
+
+
+def jl_bifocal_decode_rkc(q, k_cache, v_cache, rkc, out, lse, L: int, w0: int, w_pretrained: int,
+                          rope_base: float, sm_scale: float, table, workspace, stream=None):
+    """jl_bifocal_decode with the remote keys read from `rkc` (a RotatedKeyCache
+    of k_cache), which the call brings up to date first."""
+    _need_device(q, k_cache, v_cache, rkc.keys, out, lse, table, workspace)
+    B, one, Hq, D = q.shape
+    _, Lmax, Hkv, Dk = k_cache.shape
+    if one != 1 or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B:
+        raise ValueError("q must be [B,1,Hq,D] and the caches [B,Lmax,Hkv,D]")
+    if tuple(rkc.keys.shape) != tuple(k_cache.shape) or rkc.keys.dtype != k_cache.dtype:
+        raise ValueError("the rotated-key cache must match k_cache")
+    if tuple(out.shape) != (B, 1, Hq, D):
+        raise ValueError("out must be [B, 1, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq]")
+    _check(lib.jl_bifocal_decode_rkc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(rkc.keys),
+                                     ctypes.byref(rkc.state), _ptr(out), _ptr(lse), _dtype_code(q),
+                                     _dtype_code(out), B, L, Lmax, Hq, Hkv, D, w0, w_pretrained, rope_base,
+                                     sm_scale, _ptr(table), table.numel() * table.element_size(), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 

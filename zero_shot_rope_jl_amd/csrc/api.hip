@@ -67,7 +67,7 @@ extern "C" {
 
 JL_API const char* jl_last_error(void) { return g_err.c_str(); }
 
-JL_API int jl_version(void) { return 6; }
+JL_API int jl_version(void) { return 7; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -371,7 +371,8 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
                 int64_t page_size, int64_t max_pages, int64_t n_pages, void* out, float* lse, int in_dtype,
                 int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
                 int64_t w_pretrained, double rope_base, float sm_scale, const void* table, size_t table_bytes,
-                void* workspace, size_t workspace_bytes, void* hip_stream) {
+                void* workspace, size_t workspace_bytes, void* hip_stream, void* krot = nullptr,
+                jl_rotated_keys* rk_state = nullptr) {
     g_err.clear();
     if (!q || !k_cache || !v_cache || !out || !table || !workspace)
         return fail(JL_EINVAL, "%s: q, the caches, out, table and workspace must be non-NULL", who);
@@ -407,6 +408,12 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     if (Hkv > 65535) return fail(JL_EINVAL, "Hkv exceeds 65535");
     if (Hkv % 8 != 0 && 8 % Hkv != 0)
         return fail(JL_EUNSUPPORTED, "decode needs Hkv dividing 8 or a multiple of 8 (got %lld)", (long long)Hkv);
+    if (krot) {
+        if (!aligned16(krot)) return fail(JL_EINVAL, "%s: the rotated-key cache must be 16-byte aligned", who);
+        if (!rk_state) return fail(JL_EINVAL, "%s: state is NULL", who);
+        if (rk_state->rows < 0 || rk_state->rows > Lmax)
+            return fail(JL_EINVAL, "%s: state.rows must be in [0, Lmax] (got %lld)", who, (long long)rk_state->rows);
+    }
 
     jl::DecodeParams p{};
     p.q = q;
@@ -434,7 +441,28 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     p.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
     p.rope_base = rope_base;
     p.head_dim = (int)D;
+    p.krot = krot;
+    p.rot_row = -1;
     (void)hipGetLastError();
+    if (krot) {
+        // bring the rotated-key cache up to date for this step: every key with
+        // (L-1) - k > w0 must be there, rotated under this step's G.  The
+        // decode kernel itself then writes row kloc (local now, the first
+        // remote row of the next step if G stays), so a step that follows
+        // its predecessor under the same G needs no separate rotation.
+        const int64_t kloc = p.G == 1 ? 0 : (L - 1 - p.w0 > 0 ? L - 1 - p.w0 : 0);
+        int64_t r0 = rk_state->G == p.G ? rk_state->rows : 0;
+        if (r0 > kloc) r0 = kloc;
+        hipError_t er = jl::launch_rotate_rows(k_cache, krot, p.TF, B, Lmax, Hkv, (int)D, r0, kloc, p.G,
+                                               static_cast<hipStream_t>(hip_stream));
+        if (er != hipSuccess) return fail(JL_EHIP, "%s key rotation launch failed: %s", who, hipGetErrorString(er));
+        if (kloc > 0) {
+            p.rot_row = kloc;
+            if (rk_state->G != p.G) rk_state->rows = 0;
+            rk_state->G = p.G;
+            if (rk_state->rows < kloc + 1) rk_state->rows = kloc + 1;
+        }
+    }
     hipError_t e = jl::launch_decode(p, out_dtype, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
     return JL_OK;
@@ -452,6 +480,20 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
     return decode_impl("decode", q, k_cache, v_cache, nullptr, 0, 0, 0, out, lse, in_dtype, out_dtype, B, L, Lmax,
                        Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
                        workspace_bytes, hip_stream);
+}
+
+JL_API int jl_bifocal_decode_rkc(const void* q, const void* k_cache, const void* v_cache, void* krot_cache,
+                                 jl_rotated_keys* state, void* out, float* lse, int in_dtype, int out_dtype, int64_t B,
+                                 int64_t L, int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                                 int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
+                                 size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!krot_cache) {
+        g_err.clear();
+        return fail(JL_EINVAL, "decode_rkc: krot_cache must be non-NULL");
+    }
+    return decode_impl("decode_rkc", q, k_cache, v_cache, nullptr, 0, 0, 0, out, lse, in_dtype, out_dtype, B, L, Lmax,
+                       Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
+                       workspace_bytes, hip_stream, krot_cache, state);
 }
 
 JL_API int jl_bifocal_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -96,7 +96,7 @@ __device__ inline void load_v(DecodeTile<D>& t, const __bf16* __restrict__ vc, i
     }
 }
 
-template <int D, bool OUT_BF16, bool PAGED>
+template <int D, bool OUT_BF16, bool PAGED, bool RKC>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeParams p) {
     constexpr int HALF = D / 2;
     constexpr int NC = D / 32;
@@ -134,6 +134,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const int kloc = (G == 1) ? 0 : (int)max<int64_t>(0, (int64_t)qpos - p.w0);
     const float scale2 = p.sm_scale_log2;
     const __bf16* __restrict__ kc = static_cast<const __bf16*>(p.k);
+    // rotated-key cache (RKC): remote keys are read in their corrected view
+    // instead of being rotated here; a step is read from it when all of its
+    // keys are remote
+    const __bf16* __restrict__ krc = static_cast<const __bf16*>(p.krot);
+    auto ksrc = [&](int kb) -> const __bf16* { return (RKC && kb + kWaveKeys <= kloc) ? krc : kc; };
     const __bf16* __restrict__ vc = static_cast<const __bf16*>(p.v);
     const float2* __restrict__ TF = p.TF;
     const int64_t row = p.Hkv * D;
@@ -178,10 +183,24 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     int pg_ahead = 0;     // block-table entry of the step after next
     if (wstart < wend0) {
         const int64_t r0 = row_of(wstart);
-        load_k<D>(cur, kc, cache_b, row, wstart, r0, wend0, colh, gq);
+        load_k<D>(cur, ksrc(wstart), cache_b, row, wstart, r0, wend0, colh, gq);
         load_v<D>(cur, vc, cache_b, row, wstart, r0, wend0, lane);
         if (wstart + kWaveKeys < wend0) r_next = row_of(wstart + kWaveKeys);
         if (wstart + 2 * kWaveKeys < wend0) pg_ahead = page_of(wstart + 2 * kWaveKeys);
+    }
+
+    // rotated-key cache: one wave per (batch, KV head) reads the row that the
+    // next step will need as remote (its wait falls in the first step's);
+    // the rotated row is stored after the key loop
+    const bool write_ahead = RKC && p.rot_row >= 0 && split == 0 && sub == 0 && lane < HALF;
+    float wa_x = 0.f, wa_y = 0.f;
+    float2 wa_cs = make_float2(1.f, 0.f);
+    int64_t wa_o = 0;
+    if (write_ahead) {
+        wa_o = cache_b + p.rot_row * row + lane;
+        wa_x = (float)kc[wa_o];
+        wa_y = (float)kc[wa_o + HALF];
+        wa_cs = TF[(p.rot_row - p.rot_row / G) * HALF + lane];
     }
 
     if (tid == 0) {
@@ -191,7 +210,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     }
     // rows 0..32 of the table are cos/sin(dn * theta_i); only rows < L are
     // guaranteed to exist and dn <= L-1, so copy no further
-    for (int i = tid; i < min(JROWS, L) * HALF; i += kDecThreads) sJ[(i / HALF) * JSTR + i % HALF] = TF[i];
+    if (!RKC)
+        for (int i = tid; i < min(JROWS, L) * HALF; i += kDecThreads) sJ[(i / HALF) * JSTR + i % HALF] = TF[i];
     __syncthreads();
     const bool bad = s_bad;
 
@@ -236,7 +256,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     // read once, then advanced by the step's offset increment (<= 32) from the
     // LDS rows, so no step waits on a table load.
     float2 base = make_float2(1.f, 0.f);
-    if (lane < HALF && wstart < wend && G > 1) base = TF[(int64_t)(wstart - wstart / G) * HALF + lane];
+    if (!RKC && lane < HALF && wstart < wend && G > 1) base = TF[(int64_t)(wstart - wstart / G) * HALF + lane];
 
     // the corrected query for the current step: R(nb) applied to R(-n_q) q
     bf16x8 qit[NC];
@@ -256,7 +276,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
                 qit[c + NC / 2][j] = (__bf16)(x * cs.y + y * cs.x);
             }
     };
-    if (G > 1 && wstart < wend && wstart < kloc) rotate_query(wstart);
+    if (!RKC && G > 1 && wstart < wend && wstart < kloc) rotate_query(wstart);
 
     // One register tile (loaded above): each part is reloaded for the next
     // step as soon as this step has consumed it (V after its transpose, each
@@ -292,7 +312,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
                 for (int c = 0; c < NC; ++c)
                     sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[blk][c], qf[c], sl, 0, 0, 0);
             }
-            if (w_rem) {
+            if (RKC && w_rem) {
+                // a step with local keys was read from the stored cache: read
+                // this half's rows again, rotated, for its remote keys
+                if (w_loc) load_k_blk<D>(cur, krc, cache_b, row, kbase, kbase, wend, colh, gq, blk);
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[blk][c], qrem[c], sr, 0, 0, 0);
+            } else if (w_rem) {
                 const int key = kbase + 8 * (colh >> 2) + 4 * blk + (colh & 3);
                 const int dn = (key < wend) ? (key - key / G) - nb : 0;
                 bf16x8 kr[NC];
@@ -317,7 +344,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
                 s[blk][i] = kk < wend ? v * scale2 : -INFINITY;
             }
             // this half's K registers are free: start the next step's loads
-            if (knext < wend) load_k_blk<D>(cur, kc, cache_b, row, knext, r_next, wend, colh, gq, blk);
+            if (knext < wend) load_k_blk<D>(cur, ksrc(knext), cache_b, row, knext, r_next, wend, colh, gq, blk);
         }
 
         // ---- online softmax per head column: 8 values here, 4 quads per head --
@@ -352,20 +379,26 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
             const bf16x8 A = *reinterpret_cast<const bf16x8*>(&myV[(16 * db + colh) * VSTR + 8 * gq]);
             acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bp, acc[db], 0, 0, 0);
         }
-        if (w_rem && knext < wend && lane < HALF) {
+        if (!RKC && w_rem && knext < wend && lane < HALF) {
             const int step = (knext - knext / G) - nb;   // 0 <= step <= 32, step < L
             const float2 j2 = sJ[step * JSTR + lane];
             base = make_float2(base.x * j2.x - base.y * j2.y, base.y * j2.x + base.x * j2.y);
         }
         // the next step's corrected query, computed here so that it is off the
         // path from K's arrival to the next K loads
-        if (G > 1 && knext < wend && knext < kloc) rotate_query(knext);
+        if (!RKC && G > 1 && knext < wend && knext < kloc) rotate_query(knext);
         // rows of the step after next (its table entry was read a step ago);
         // then the table entry of the step after that
         r_next = knext + kWaveKeys < wend ? row_in(pg_ahead, knext + kWaveKeys) : 0;
         if (PAGED && knext + 2 * kWaveKeys < wend) pg_ahead = page_of(knext + 2 * kWaveKeys);
     }
     if (bad_page) l_run = NAN;   // poisons this head's output through the merge
+    if (write_ahead) {
+        rotate_back(wa_x, wa_y, wa_cs);
+        __bf16* kw = static_cast<__bf16*>(const_cast<void*>(p.krot));
+        kw[wa_o] = (__bf16)wa_x;
+        kw[wa_o + HALF] = (__bf16)wa_y;
+    }
 
     // ---- merge the NW waves of each head, write this split's partials -------
     float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -482,8 +515,12 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeParams p) {
 template <int D, bool OUT_BF16>
 hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
     const dim3 grid(p.n_split, p.Hkv / p.heads_per_wg, p.B);
-    if (p.block_table) hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, true>), grid, dim3(kDecThreads), 0, stream, p);
-    else hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false>), grid, dim3(kDecThreads), 0, stream, p);
+    if (p.block_table)
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, true, false>), grid, dim3(kDecThreads), 0, stream, p);
+    else if (p.krot)
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false, true>), grid, dim3(kDecThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false, false>), grid, dim3(kDecThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(p.Hq, p.B, D / 32), dim3(1024), 0, stream, p);
@@ -491,6 +528,67 @@ hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+namespace {
+
+// Rows [r0, r1) of every (batch, KV head) of a [B, Lmax, Hkv, D] bf16 key
+// cache rotated by their correction offset, table row n(k) = k - floor(k/G),
+// rounded to bf16, into the same place of krot (§3.2 Eq. 5 applied to the
+// cached keys).  One thread per 8 rotation pairs of a row; HBM-bound.
+template <int D>
+__global__ __launch_bounds__(256) void rotate_rows_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kr,
+                                                          const float2* __restrict__ TF, int64_t n_items,
+                                                          int64_t Lmax, int Hkv, int64_t r0, int64_t nrows,
+                                                          int64_t G) {
+    constexpr int HALF = D / 2;
+    constexpr int CPR = HALF / 8;   // 8-pair items per row
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n_items) return;
+    const int c = (int)(t % CPR);
+    const int64_t rh = t / CPR;     // (batch, row, head), head fastest
+    const int h = (int)(rh % Hkv);
+    const int64_t br = rh / Hkv;
+    const int64_t pos = r0 + br % nrows;
+    const int64_t b = br / nrows;
+    const int64_t n = pos - pos / G;
+    const int64_t o = ((b * Lmax + pos) * Hkv + h) * D + 8 * c;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(k + o);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(k + o + HALF);
+    const float4* cs = reinterpret_cast<const float4*>(TF + n * HALF + 8 * c);
+    bf16x8 xo, yo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float4 c4 = cs[e];
+        float x0 = (float)x[2 * e], y0 = (float)y[2 * e];
+        float x1 = (float)x[2 * e + 1], y1 = (float)y[2 * e + 1];
+        rotate_back(x0, y0, make_float2(c4.x, c4.y));
+        rotate_back(x1, y1, make_float2(c4.z, c4.w));
+        xo[2 * e] = (__bf16)x0;
+        yo[2 * e] = (__bf16)y0;
+        xo[2 * e + 1] = (__bf16)x1;
+        yo[2 * e + 1] = (__bf16)y1;
+    }
+    *reinterpret_cast<bf16x8*>(kr + o) = xo;
+    *reinterpret_cast<bf16x8*>(kr + o + HALF) = yo;
+}
+
+}  // namespace
+
+hipError_t launch_rotate_rows(const void* k, void* krot, const float2* TF, int64_t B, int64_t Lmax, int64_t Hkv,
+                              int head_dim, int64_t r0, int64_t r1, int64_t G, hipStream_t stream) {
+    if (r1 <= r0) return hipSuccess;
+    const int64_t n_items = B * (r1 - r0) * Hkv * (head_dim / 16);
+    const unsigned blocks = (unsigned)((n_items + 255) / 256);
+    if (head_dim == 128)
+        hipLaunchKernelGGL((rotate_rows_kernel<128>), dim3(blocks), dim3(256), 0, stream,
+                           static_cast<const __bf16*>(k), static_cast<__bf16*>(krot), TF, n_items, Lmax, (int)Hkv, r0,
+                           r1 - r0, G);
+    else
+        hipLaunchKernelGGL((rotate_rows_kernel<64>), dim3(blocks), dim3(256), 0, stream,
+                           static_cast<const __bf16*>(k), static_cast<__bf16*>(krot), TF, n_items, Lmax, (int)Hkv, r0,
+                           r1 - r0, G);
+    return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeParams& p, int out_dtype, hipStream_t stream) {
     const bool ob = out_dtype == 1;

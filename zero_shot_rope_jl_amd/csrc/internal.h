@@ -78,13 +78,29 @@ struct DecodeParams {
     float sm_scale_log2;
     double rope_base;
     int head_dim;
+    // contiguous caches only: [B, Lmax, Hkv, D] bf16 holding every remote
+    // key (rows < L-1-w0) already in its corrected view under this G, or null
+    const void* krot;
+    // with krot: the row to write into krot, rotated under this G, for the
+    // next step (the first local row, which the next step reads as remote
+    // when G stays); -1 for none
+    int64_t rot_row;
 };
 
-// Decode split plan.  A workgroup has 8 waves that cover up to 8 KV heads
+// Rows [r0, r1) of a [B, Lmax, Hkv, D] bf16 key cache rotated into their
+// corrected view under G (the rotated-key cache of jl_bifocal_decode_rkc).
+hipError_t launch_rotate_rows(const void* k, void* krot, const float2* TF, int64_t B, int64_t Lmax, int64_t Hkv,
+                              int head_dim, int64_t r0, int64_t r1, int64_t G, hipStream_t stream);
+
+// Decode split plan.  A workgroup has 8 waves that cover up to 4 KV heads
 // (wave w -> head w % WH, key sub-range w / WH) over one key range, so each
-// key row (all heads contiguous) is streamed whole; the grid holds about one
-// workgroup per compute unit.
+// key row is read in runs of WH heads (1 KB at D = 128); the grid holds about
+// one workgroup per compute unit.  Four heads per workgroup (two waves per
+// head, merged in LDS) measured faster than eight (whole rows) for the
+// contiguous cache and clearly faster for the paged one; one or two heads
+// (256-512 B runs) measured slower.
 constexpr int kDecodeWaves = 8;
+constexpr int kDecodeMaxHeadsPerWG = 4;
 constexpr int kDecodeTargetWGs = 256;
 constexpr int kDecodeMaxSplits = 256;
 
@@ -93,7 +109,9 @@ inline int64_t decode_max_splits(int64_t L) {
     return n < kDecodeMaxSplits ? n : kDecodeMaxSplits;
 }
 
-inline int decode_heads_per_wg(int64_t Hkv) { return Hkv >= kDecodeWaves ? kDecodeWaves : (int)Hkv; }
+inline int decode_heads_per_wg(int64_t Hkv) {
+    return Hkv >= kDecodeMaxHeadsPerWG ? kDecodeMaxHeadsPerWG : (int)Hkv;
+}
 
 inline void decode_split_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* wave_chunk) {
     const int64_t WH = decode_heads_per_wg(Hkv);
