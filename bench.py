@@ -439,7 +439,7 @@ def main():
             "steps_timed": args.decode_passes * dw.steps,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": pick(traffic, "jl::decode_split_kernel<128, true, false>",
+                         "traffic": pick(traffic, "jl::decode_split_kernel<128, true, false, false>",
                                          "jl::decode_combine_kernel"),
                          "bytes_per_step": bytes_step},
         }
