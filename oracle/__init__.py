@@ -13,5 +13,6 @@ textbook library routine).  No function here is "parity unpinned".
 from .jetlong_oracle import (  # noqa: F401
     group_size, alias_position, correction_offset, inv_freq, rope_rotate,
     remote_view, bifocal_attention, plain_causal_attention, decode_attention,
-    inclusion_exclusion_attention, softmax_rows,
+    inclusion_exclusion_attention, softmax_rows, fi_scale, fi_ramp, fi_inv_freq, fi_remote_view,
+    bifocal_attention_fi, decode_attention_fi,
 )

@@ -37,6 +37,8 @@ __all__ = [
     "group_size", "alias_position", "correction_offset", "inv_freq",
     "rope_rotate", "remote_view", "softmax_rows", "bifocal_attention",
     "plain_causal_attention", "decode_attention", "inclusion_exclusion_attention",
+    "fi_scale", "fi_ramp", "fi_inv_freq", "fi_remote_view", "bifocal_attention_fi",
+    "decode_attention_fi",
 ]
 
 
@@ -101,18 +103,21 @@ def softmax_rows(S: np.ndarray, V: np.ndarray):
 
 
 # ---------------------------------------------------------- core (dense)
-def _attend(qv, q_pos, k, v, G, w0, base, sm_scale, bifocal, block):
+def _attend(qv, q_pos, k, v, G, w0, base, sm_scale, bifocal, block, remote=None):
     """Dense bifocal (or plain) causal attention for the query vectors
-    qv [B, n, Hq, D] at positions q_pos [n] over keys 0..Lk-1."""
+    qv [B, n, Hq, D] at positions q_pos [n] over keys 0..Lk-1.  ``remote``
+    (u, positions) -> remote view; by default the aliased view under G."""
     B, n, Hq, D = qv.shape
     Lk, Hkv = k.shape[1], k.shape[2]
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     R = Hq // Hkv
     q_pos = np.asarray(q_pos, dtype=np.int64)
+    if remote is None:
+        remote = lambda u, pos: remote_view(u, pos, G, base)
     if bifocal:
-        k_rem = remote_view(k, np.arange(Lk), G, base)
-        q_rem = remote_view(qv, q_pos, G, base)
+        k_rem = remote(k, np.arange(Lk))
+        q_rem = remote(qv, q_pos)
     out = np.empty((B, n, Hq, D), dtype=np.float64)
     lse = np.empty((B, Hq, n), dtype=np.float64)
     for b in range(B):
@@ -211,3 +216,69 @@ def inclusion_exclusion_attention(q, k, v, w0: int, w_pretrained: int,
             num = wA[:, None] * oA + wB[:, None] * oB - wC[:, None] * oC
             out[b, :, h] = num / (wA + wB - wC)[:, None]
     return out
+
+
+# ------------------------- §4.7 ablation: frequency interpolation (remote)
+# The remote view moves each stored phase p*theta_i to p*theta'_i, where
+# theta' are YaRN-style interpolated frequencies for the continuous ratio
+# s = max(1, L / w_pretrained) of §3.1.  The local window is unchanged.  The
+# pages do not give the ramp; the reading here is YaRN's: with
+# r_i = w_pretrained / lambda_i (turns of pair i over the pretrained window,
+# lambda_i = 2 pi / theta_i), gamma_i = 0 for r_i < alpha (interpolated:
+# theta_i / s), 1 for r_i > beta (kept: theta_i), linear in between; no
+# attention temperature.
+def fi_scale(L: int, w_pretrained: int) -> float:
+    """§3.1: the continuous scaling ratio s = max(1, L / w_pretrained)."""
+    return max(1.0, float(L) / float(w_pretrained))
+
+
+def fi_ramp(D: int, base: float, w_pretrained: int, alpha: float, beta: float) -> np.ndarray:
+    """gamma_i in [0, 1] for each rotation pair (see the note above)."""
+    r = float(w_pretrained) * inv_freq(D, base) / (2.0 * np.pi)
+    return np.clip((r - alpha) / (beta - alpha), 0.0, 1.0)
+
+
+def fi_inv_freq(D: int, base: float, L: int, w_pretrained: int, alpha: float, beta: float) -> np.ndarray:
+    """theta'_i = (1 - gamma_i) theta_i / s + gamma_i theta_i."""
+    theta = inv_freq(D, base)
+    g = fi_ramp(D, base, w_pretrained, alpha, beta)
+    return (1.0 - g) * theta / fi_scale(L, w_pretrained) + g * theta
+
+
+def fi_remote_view(u: np.ndarray, positions, L: int, w_pretrained: int, base: float,
+                   alpha: float, beta: float) -> np.ndarray:
+    """Stored vectors u[B, n, H, D] = RoPE(x, p) at ``positions`` moved to the
+    interpolated phase: pair i rotated by p (theta'_i - theta_i)."""
+    u = np.asarray(u, dtype=np.float64)
+    D = u.shape[-1]
+    dtheta = fi_inv_freq(D, base, L, w_pretrained, alpha, beta) - inv_freq(D, base)
+    ang = np.asarray(positions, dtype=np.float64)[None, :, None, None] * dtheta
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = u[..., : D // 2], u[..., D // 2:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def bifocal_attention_fi(q, k, v, w0: int, w_pretrained: int, rope_base: float, alpha: float,
+                         beta: float, sm_scale: float, rows=None, block: int = 64):
+    """Prefill with the interpolated remote view: the score rule of §3 Eq. 1
+    (stored vectors when q - k <= w0) with the remote pairs scored in the
+    frequency-interpolation view for this call's L.  Returns (out, lse) as
+    bifocal_attention."""
+    q = np.asarray(q, dtype=np.float64)
+    L = q.shape[1]
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    remote = lambda u, pos: fi_remote_view(u, pos, L, w_pretrained, rope_base, alpha, beta)
+    return _attend(q[:, rows], rows, np.asarray(k, np.float64), np.asarray(v, np.float64),
+                   0, int(w0), rope_base, sm_scale, True, block, remote)
+
+
+def decode_attention_fi(q_tok, k_cache, v_cache, L: int, w0: int, w_pretrained: int,
+                        rope_base: float, alpha: float, beta: float, sm_scale: float):
+    """One decode step with the interpolated remote view, s from this L."""
+    q_tok = np.asarray(q_tok, dtype=np.float64)
+    remote = lambda u, pos: fi_remote_view(u, pos, L, w_pretrained, rope_base, alpha, beta)
+    o, ls = _attend(q_tok[:, None], np.array([L - 1]),
+                    np.asarray(k_cache[:, :L], np.float64),
+                    np.asarray(v_cache[:, :L], np.float64),
+                    0, int(w0), rope_base, sm_scale, True, 1, remote)
+    return o[:, 0], ls[:, :, 0]
