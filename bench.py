@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--chunk-steps", type=int, default=5,
                     help="calls of the last-4096-token chunk timed, contiguous and paged (0 skips it)")
+    ap.add_argument("--fi-steps", type=int, default=3,
+                    help="timed calls of the prefill with the frequency-interpolation view (0: skip)")
     ap.add_argument("--unfused-steps", type=int, default=3,
                     help="calls of the unfused three-pass prefill timed (0 skips it)")
     ap.add_argument("--control-steps", type=int, default=5,
@@ -185,6 +187,47 @@ def bench_unfused(torch, jl, args, w, x):
     return ms
 
 
+FI_RAMP = (1.0, 32.0)   # YaRN's ramp bounds, in turns per pretrained window
+
+
+def bench_fi(torch, jl, args, w, x):
+    """The same call with the frequency-interpolation remote view
+    (jl_bifocal_prefill_fi, YaRN's ramp bounds): its table build, then the
+    prefill with the table in place."""
+    q, k, v = (to_dev(torch, x[n], w.dtype) for n in "qkv")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device="cuda")
+    ws = jl.alloc_prefill_workspace(k, w.w_pretrained)
+    table = torch.empty(jl.jl_fi_table(w.L, w.w_pretrained, w.D, w.rope_base, *FI_RAMP), dtype=torch.uint8,
+                        device="cuda")
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    jl.jl_fi_table(w.L, w.w_pretrained, w.D, w.rope_base, *FI_RAMP, table=table)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    jl.jl_fi_table(w.L, w.w_pretrained, w.D, w.rope_base, *FI_RAMP, table=table)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    table_ms = ev0.elapsed_time(ev1)
+
+    def step():
+        jl.jl_bifocal_prefill_fi(q, k, v, out, lse, w.w0, w.w_pretrained, w.rope_base, *FI_RAMP, w.sm_scale, table,
+                                 workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.fi_steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.fi_steps
+    log(f"[bench] frequency-interpolation view: {ms:.3f} ms/call, table build {table_ms:.3f} ms")
+    del q, k, v, out, lse, ws, table
+    torch.cuda.empty_cache()
+    return ms, table_ms
+
+
 def bench_chunk(torch, jl, args, w, x, Lq=4096, page_size=256):
     """The last Lq-token chunk of the workload over its cache, contiguous and
     held in shuffled pages (jl_bifocal_prefill_chunk / _chunk_paged)."""
@@ -317,6 +360,21 @@ def bench_decode(torch, jl, si, args):
     graph_ok = bool(torch.equal(out, eager_out))
     del graph
 
+    # the same steps with the frequency-interpolation remote view (s from
+    # each step's L, no table)
+    def fi_pass():
+        for s in range(dw.steps):
+            L = dw.prompt_len + s + 1
+            jl.jl_bifocal_decode_fi(qs[s], kc, vc, out, None, L, dw.w0, dw.w_pretrained, dw.rope_base, *FI_RAMP,
+                                    dw.sm_scale, ws)
+
+    fi_pass()
+    ev0.record(stream)
+    fi_pass()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_fi = ev0.elapsed_time(ev1) * 1e3 / dw.steps
+
     # the same steps with a rotated-key cache: each timed pass starts from an
     # empty cache, so its first step rotates every remote key and the later
     # steps one new row each; that cost is inside the per-step figure
@@ -342,7 +400,8 @@ def bench_decode(torch, jl, si, args):
     bytes_step = 2.0 * dw.B * mean_L * dw.Hkv * dw.D * 2
     gbs = bytes_step / (us * 1e-6) / 1e9
     log(f"[bench] decode {us:.2f} us/step (per-step median {us_median:.2f}, paged cache {us_paged:.2f}, "
-        f"graph {us_graph:.2f}{'' if graph_ok else ' MISMATCH'}, rotated-key cache {us_rkc:.2f}"
+        f"graph {us_graph:.2f}{'' if graph_ok else ' MISMATCH'}, rotated-key cache {us_rkc:.2f}, "
+        f"frequency interpolation {us_fi:.2f}"
         f"{'' if rkc_ok else ' MISMATCH'}), {gbs:.0f} GB/s")
     del kc, vc
     torch.cuda.empty_cache()
@@ -350,6 +409,7 @@ def bench_decode(torch, jl, si, args):
                                                "us_per_step_graph": round(us_graph, 3),
                                                "graph_matches_eager": graph_ok,
                                                "us_per_step_rotated_keys": round(us_rkc, 3),
+                                               "us_per_step_frequency_interpolation": round(us_fi, 3),
                                                "rotated_keys_match": rkc_ok}
 
 
@@ -429,6 +489,13 @@ def main():
             "what": "three separate passes (stored view over the window, corrected view over all keys and over "
                     "the window) and their inclusion-exclusion merge",
             "ms_per_call": round(ums, 4), "fused_speedup": round(ums / ms, 4)}
+    if args.fi_steps > 0:
+        fms, tms = bench_fi(torch, jl, args, w, x)
+        result["frequency_interpolation"] = {
+            "what": "same inputs, remote pairs in the YaRN-style frequency-interpolation view "
+                    "(ramp bounds 1 and 32 turns per pretrained window)",
+            "ms_per_call": round(fms, 4), "table_build_ms": round(tms, 4),
+            "tflops": round(flops / (fms * 1e-3) / 1e12, 2)}
     if args.chunk_steps > 0:
         result["chunk"] = {"what": "last 4096 tokens of the workload as one chunk over the other 126976 keys",
                            **bench_chunk(torch, jl, args, w, x)}

@@ -353,6 +353,81 @@ JL_API int jl_bifocal_decode_rkc(const void* q, const void* k_cache, const void*
 JL_API int jl_table_fill_host(int64_t L, int64_t head_dim, double rope_base, void* table,
                        size_t table_bytes);
 
+/*
+ * ---- Frequency-interpolation remote view (the ablation of §4.7) ----------
+ *
+ * The same bifocal rule with the remote pairs (q - k > w0) scored after
+ * YaRN-style frequency interpolation instead of position aliasing: the
+ * local window keeps RoPE(x, p); a remote query or key moves to the phase
+ * p * theta'_i, with
+ *     theta'_i = (1 - gamma_i) theta_i / s + gamma_i theta_i,
+ *     s = max(1, L / w_pretrained)        (the continuous ratio of §3.1),
+ *     gamma_i = clamp((r_i - fi_alpha) / (fi_beta - fi_alpha), 0, 1),
+ *     r_i = w_pretrained theta_i / (2 pi) (turns of pair i per window).
+ * The pages name the variant but give no ramp; this is YaRN's form, with
+ * its bounds as arguments (YaRN uses 1 and 32) and no attention
+ * temperature.  A stored vector reaches its remote view by the rotation
+ * R(-p phi_i), phi_i = theta_i - theta'_i, so the machinery of Eq. 5 applies
+ * with position-indexed rows.  Unlike G, s changes with every L.
+ */
+
+/*
+ * jl_fi_table -- the table of the frequency-interpolation view for one call:
+ * rows p < L of (cos, sin)(p * phi_i), angles formed in float64 and stored
+ * fp32, after a header recording (L, w_pretrained, fi_alpha, fi_beta,
+ * head_dim, rope_base).  Same size as jl_schedule's table for L
+ * (*table_bytes_needed); table may be NULL to query the size only.  The
+ * fill is enqueued on hip_stream.  jl_bifocal_prefill_fi checks the header
+ * and writes NaN outputs when it was built for anything else.
+ *
+ * Errors: JL_EINVAL (L outside [1, 2^30], w_pretrained < 1, rope_base not
+ * finite and > 1, fi_alpha / fi_beta not finite with fi_alpha < fi_beta, a
+ * misaligned table), JL_EUNSUPPORTED (head_dim not 64 or 128), JL_ESPACE
+ * (table_bytes too small), JL_EHIP.
+ */
+JL_API int jl_fi_table(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base,
+                       double fi_alpha, double fi_beta, void* table, size_t table_bytes,
+                       size_t* table_bytes_needed, void* hip_stream);
+
+/*
+ * jl_fi_table_fill_host -- the same table written into a HOST buffer (the
+ * same float64 formulas compiled for the host).  Errors as jl_fi_table,
+ * plus JL_EINVAL for a NULL table.
+ */
+JL_API int jl_fi_table_fill_host(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base,
+                                 double fi_alpha, double fi_beta, void* table, size_t table_bytes);
+
+/*
+ * jl_bifocal_prefill_fi -- jl_bifocal_prefill with the remote pairs in the
+ * frequency-interpolation view.  Arguments, layouts, workspace
+ * (jl_bifocal_prefill_workspace with the same w_pretrained) and errors as
+ * jl_bifocal_prefill, except that `table` comes from jl_fi_table for this
+ * (L, w_pretrained, fi_alpha, fi_beta), and fi_alpha / fi_beta are checked
+ * as there.  When L <= w_pretrained (s = 1) the result is plain causal
+ * attention.
+ */
+JL_API int jl_bifocal_prefill_fi(const void* q, const void* k, const void* v, void* out, float* lse,
+                                 int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Hq,
+                                 int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained,
+                                 double rope_base, double fi_alpha, double fi_beta, float sm_scale,
+                                 const void* table, size_t table_bytes, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
+
+/*
+ * jl_bifocal_decode_fi -- jl_bifocal_decode with the remote keys in the
+ * frequency-interpolation view for this step's L.  It takes no table: s
+ * changes every step, so the kernel forms the few rows it reads from
+ * per-pair phi_i computed on the host in float64.  Arguments, layouts,
+ * workspace and errors as jl_bifocal_decode (no table arguments), plus the
+ * fi_alpha / fi_beta check.
+ */
+JL_API int jl_bifocal_decode_fi(const void* q, const void* k_cache, const void* v_cache, void* out,
+                                float* lse, int in_dtype, int out_dtype, int64_t B, int64_t L,
+                                int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                                int64_t w_pretrained, double rope_base, double fi_alpha,
+                                double fi_beta, float sm_scale, void* workspace,
+                                size_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,10 +27,11 @@ def test_exports_every_declared_symbol():
                            "jl_bifocal_prefill", "jl_bifocal_prefill_chunk", "jl_bifocal_decode_workspace",
                            "jl_bifocal_decode", "jl_bifocal_decode_paged", "jl_table_fill_host",
                            "jl_bifocal_prefill_unfused_workspace", "jl_bifocal_prefill_unfused",
-                           "jl_bifocal_prefill_chunk_paged", "jl_bifocal_decode_rkc"])
+                           "jl_bifocal_prefill_chunk_paged", "jl_bifocal_decode_rkc", "jl_fi_table",
+                           "jl_fi_table_fill_host", "jl_bifocal_prefill_fi", "jl_bifocal_decode_fi"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 7
+    assert jl.jl_version() == 8
 
 
 def test_schedule_golden_and_table_size():
@@ -295,3 +296,83 @@ def test_single_hip_runtime_in_process():
     with open("/proc/self/maps") as fh:
         libs = {l.split()[-1] for l in fh if "libamdhip64" in l}
     assert len(libs) == 1, libs
+
+
+# ---- frequency-interpolation view ------------------------------------------
+@pytest.mark.parametrize("D,base,L,w_pre,alpha,beta", [
+    (64, 1e4, 512, 256, 1.0, 32.0), (128, 1e6, 131328, 32768, 1.0, 32.0), (128, 5e5, 300, 1000, 1.0, 32.0),
+    (128, 1e4, 1000, 100, -2.0, -1.0), (64, 1e4, 777, 64, 50.0, 100.0)])
+def test_host_fi_table_matches_oracle(D, base, L, w_pre, alpha, beta):
+    """Rows p of (cos, sin)(p (theta_i - theta'_i)), theta' from the oracle."""
+    import oracle
+    buf = jl.jl_fi_table_fill_host(L, w_pre, D, base, alpha, beta)
+    hdr = buf[:64]
+    assert hdr[:4].view(np.uint32)[0] == 0x3146544A
+    assert hdr[4:8].view(np.int32)[0] == D and hdr[8:16].view(np.int64)[0] == L
+    assert hdr[16:24].view(np.float64)[0] == base
+    assert hdr[24:32].view(np.int64)[0] == L and hdr[32:40].view(np.int64)[0] == w_pre
+    assert hdr[40:48].view(np.float64)[0] == alpha and hdr[48:56].view(np.float64)[0] == beta
+    ent = buf[64:].view(np.float32).reshape(L, D // 2, 2)
+    phi = oracle.inv_freq(D, base) - oracle.fi_inv_freq(D, base, L, w_pre, alpha, beta)
+    ang = np.arange(L, dtype=np.float64)[:, None] * phi[None, :]
+    want = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(ent.astype(np.float64) - want) <= ulp + 1e-10)
+    if L <= w_pre or alpha < 0:   # s = 1, or every pair kept: the identity
+        assert np.all(ent[..., 0] == 1.0) and np.all(ent[..., 1] == 0.0)
+
+
+@pytest.mark.parametrize("alpha,beta", [(2.0, 2.0), (3.0, 1.0), (float("nan"), 1.0), (0.0, float("inf"))])
+def test_fi_ramp_validation(alpha, beta):
+    need = ctypes.c_size_t(0)
+    assert jl.lib.jl_fi_table(100, 10, 128, 1e4, alpha, beta, None, 0, ctypes.byref(need), None) == jl.JL_EINVAL
+    assert jl.lib.jl_fi_table_fill_host(100, 10, 128, 1e4, alpha, beta, FAKE, 1 << 20) == jl.JL_EINVAL
+    assert _prefill_fi(alpha=alpha, beta=beta) == jl.JL_EINVAL
+    assert _decode_fi(alpha=alpha, beta=beta) == jl.JL_EINVAL
+
+
+def test_fi_table_size_and_space():
+    need = ctypes.c_size_t(0)
+    assert jl.lib.jl_fi_table(1000, 100, 128, 1e4, 1.0, 32.0, None, 0, ctypes.byref(need), None) == jl.JL_OK
+    assert need.value == 64 + 1000 * 64 * 8
+    assert jl.lib.jl_fi_table(1000, 100, 128, 1e4, 1.0, 32.0, FAKE, need.value - 1, None, None) == jl.JL_ESPACE
+    assert jl.lib.jl_fi_table(1000, 0, 128, 1e4, 1.0, 32.0, None, 0, None, None) == jl.JL_EINVAL
+    assert jl.lib.jl_fi_table(1000, 100, 96, 1e4, 1.0, 32.0, None, 0, None, None) == jl.JL_EUNSUPPORTED
+
+
+def _prefill_fi(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, L=600, Hq=8, Hkv=2,
+             D=128, w0=16, wp=64, base=1e4, alpha=1.0, beta=32.0, sc=0.125, table=FAKE, tb=1 << 30, ws=FAKE,
+             wsb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_prefill_fi(a["q"], a["k"], a["v"], a["out"], a["lse"], a["i"], a["o"], a["B"],
+                                        a["L"], a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"], a["base"],
+                                        a["alpha"], a["beta"], a["sc"], a["table"], a["tb"], a["ws"], a["wsb"],
+                                        None)
+
+
+def _decode_fi(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, L=600, Lmax=700,
+             Hq=8, Hkv=2, D=128, w0=16, wp=64, base=1e4, alpha=1.0, beta=32.0, sc=0.125, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_decode_fi(a["q"], a["k"], a["v"], a["out"], a["lse"], a["i"], a["o"], a["B"],
+                                       a["L"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"], a["base"],
+                                       a["alpha"], a["beta"], a["sc"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(table=None), jl.JL_EINVAL), (dict(tb=64), jl.JL_ESPACE), (dict(ws=None), jl.JL_ESPACE),
+    (dict(w0=-1), jl.JL_EINVAL), (dict(wp=0), jl.JL_EINVAL), (dict(D=96), jl.JL_EUNSUPPORTED),
+    (dict(i=jl.JL_F32, o=jl.JL_BF16), jl.JL_EUNSUPPORTED), (dict(q=FAKE + 4), jl.JL_EINVAL),
+])
+def test_prefill_fi_validation(over, code):
+    assert _prefill_fi(**over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ws=None), jl.JL_EINVAL), (dict(Lmax=599), jl.JL_EINVAL), (dict(wsb=16), jl.JL_ESPACE),
+    (dict(i=jl.JL_F32, o=jl.JL_F32), jl.JL_EUNSUPPORTED), (dict(w0=-3), jl.JL_EINVAL),
+    (dict(D=32), jl.JL_EUNSUPPORTED), (dict(k=FAKE + 8), jl.JL_EINVAL),
+])
+def test_decode_fi_validation(over, code):
+    assert _decode_fi(**over) == code

@@ -78,6 +78,17 @@ def _load():
     L.jl_bifocal_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                           i64, i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz,
                                           vp, sz, vp]
+    d = ctypes.c_double
+    L.jl_fi_table.restype = ctypes.c_int
+    L.jl_fi_table.argtypes = [i64, i64, i64, d, d, d, vp, sz, ctypes.POINTER(sz), vp]
+    L.jl_fi_table_fill_host.restype = ctypes.c_int
+    L.jl_fi_table_fill_host.argtypes = [i64, i64, i64, d, d, d, vp, sz]
+    L.jl_bifocal_prefill_fi.restype = ctypes.c_int
+    L.jl_bifocal_prefill_fi.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i64,
+                                        i64, i64, d, d, d, ctypes.c_float, vp, sz, vp, sz, vp]
+    L.jl_bifocal_decode_fi.restype = ctypes.c_int
+    L.jl_bifocal_decode_fi.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, i64,
+                                       i64, i64, i64, d, d, d, ctypes.c_float, vp, sz, vp]
     return L
 
 
@@ -403,4 +414,86 @@ def jl_bifocal_decode_paged(q, k_pages, v_pages, block_table, out, lse, L: int, 
                                        block_table.shape[1], Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale,
                                        _ptr(table), table.numel() * table.element_size(), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+# ---- frequency-interpolation remote view (the §4.7 ablation) -------------
+def jl_fi_table(L: int, w_pretrained: int, head_dim: int, rope_base: float, fi_alpha: float, fi_beta: float,
+                table=None, stream=None) -> int:
+    """Size of the interpolation table for this call; fills ``table`` (a
+    uint8 device tensor) on the stream when given."""
+    need = ctypes.c_size_t(0)
+    if table is not None:
+        _need_device(table)
+        rc = lib.jl_fi_table(L, w_pretrained, head_dim, rope_base, fi_alpha, fi_beta, _ptr(table),
+                             table.numel() * table.element_size(), ctypes.byref(need), _stream(stream))
+    else:
+        rc = lib.jl_fi_table(L, w_pretrained, head_dim, rope_base, fi_alpha, fi_beta, None, 0,
+                             ctypes.byref(need), None)
+    _check(rc)
+    return need.value
+
+
+def jl_fi_table_fill_host(L: int, w_pretrained: int, head_dim: int, rope_base: float, fi_alpha: float,
+                          fi_beta: float):
+    """Host-built interpolation table (numpy uint8 array), the device layout."""
+    import numpy as np
+    buf = np.zeros(jl_fi_table(L, w_pretrained, head_dim, rope_base, fi_alpha, fi_beta), dtype=np.uint8)
+    _check(lib.jl_fi_table_fill_host(L, w_pretrained, head_dim, rope_base, fi_alpha, fi_beta,
+                                     buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes))
+    return buf
+
+
+def alloc_fi_table(L: int, w_pretrained: int, head_dim: int, rope_base: float, fi_alpha: float, fi_beta: float,
+                   device="cuda", stream=None):
+    """Allocate a device interpolation table with torch and fill it."""
+    torch = _torch()
+    t = torch.empty(jl_fi_table(L, w_pretrained, head_dim, rope_base, fi_alpha, fi_beta), dtype=torch.uint8,
+                    device=device)
+    jl_fi_table(L, w_pretrained, head_dim, rope_base, fi_alpha, fi_beta, table=t, stream=stream)
+    return t
+
+
+def jl_bifocal_prefill_fi(q, k, v, out, lse, w0: int, w_pretrained: int, rope_base: float, fi_alpha: float,
+                          fi_beta: float, sm_scale: float, table, workspace=None, stream=None):
+    """jl_bifocal_prefill with the remote pairs in the frequency-interpolation
+    view; ``table`` from alloc_fi_table for this (L, w_pretrained, ramp)."""
+    _need_device(q, k, v, out, lse, table, workspace)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, L, Hkv, D) or tuple(v.shape) != (B, L, Hkv, D):
+        raise ValueError("k and v must be [B, L, Hkv, D] matching q")
+    if tuple(out.shape) != (B, L, Hq, D):
+        raise ValueError("out must be [B, L, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq, L) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq, L]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if workspace is None:
+        workspace = alloc_prefill_workspace(k, w_pretrained, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.jl_bifocal_prefill_fi(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
+                                     _dtype_code(out), B, L, Hq, Hkv, D, w0, w_pretrained, rope_base, fi_alpha,
+                                     fi_beta, sm_scale, _ptr(table), table.numel() * table.element_size(),
+                                     _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def jl_bifocal_decode_fi(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrained: int, rope_base: float,
+                         fi_alpha: float, fi_beta: float, sm_scale: float, workspace, stream=None):
+    """jl_bifocal_decode with the remote keys in the frequency-interpolation
+    view for this L (no table)."""
+    _need_device(q, k_cache, v_cache, out, lse, workspace)
+    B, one, Hq, D = q.shape
+    _, Lmax, Hkv, Dk = k_cache.shape
+    if one != 1 or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B:
+        raise ValueError("q must be [B,1,Hq,D] and the caches [B,Lmax,Hkv,D]")
+    if tuple(out.shape) != (B, 1, Hq, D):
+        raise ValueError("out must be [B, 1, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq]")
+    _check(lib.jl_bifocal_decode_fi(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _dtype_code(q),
+                                    _dtype_code(out), B, L, Lmax, Hq, Hkv, D, w0, w_pretrained, rope_base, fi_alpha,
+                                    fi_beta, sm_scale, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse

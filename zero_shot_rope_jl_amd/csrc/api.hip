@@ -40,6 +40,25 @@ int check_rope(int64_t head_dim, double rope_base) {
     return JL_OK;
 }
 
+// Ramp bounds of the frequency-interpolation view (turns per pretrained
+// window): finite, alpha < beta.
+int check_fi_ramp(double alpha, double beta) {
+    if (!std::isfinite(alpha) || !std::isfinite(beta) || !(alpha < beta))
+        return fail(JL_EINVAL, "fi_alpha and fi_beta must be finite with fi_alpha < fi_beta (got %g, %g)", alpha,
+                    beta);
+    return JL_OK;
+}
+
+// The frequency-interpolation view of one call, or none.
+struct FiArgs {
+    double alpha, beta;
+};
+
+// G handed to the kernels for the frequency-interpolation view: 1 when
+// s = 1 (every view is the stored one), else max(2, L), so that the row of
+// position p < L, p - floor(p/G), is p.
+int64_t fi_group(int64_t L, int64_t w_pretrained) { return L > w_pretrained ? (L > 2 ? L : 2) : 1; }
+
 int check_attention_common(int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
                            int64_t w_pretrained, double rope_base, float sm_scale, int in_dtype,
                            int out_dtype) {
@@ -67,7 +86,7 @@ extern "C" {
 
 JL_API const char* jl_last_error(void) { return g_err.c_str(); }
 
-JL_API int jl_version(void) { return 7; }
+JL_API int jl_version(void) { return 8; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -99,6 +118,41 @@ JL_API int jl_table_fill_host(int64_t L, int64_t head_dim, double rope_base, voi
     const size_t need = jl::table_bytes_for(L, (int)head_dim);
     if (table_bytes < need) return fail(JL_ESPACE, "table holds %zu bytes, %zu needed", table_bytes, need);
     jl::table_fill_host(table, L, (int)head_dim, rope_base);
+    return JL_OK;
+}
+
+JL_API int jl_fi_table(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, double fi_alpha,
+                       double fi_beta, void* table, size_t table_bytes, size_t* table_bytes_needed,
+                       void* hip_stream) {
+    g_err.clear();
+    if (L < 1 || L > kMaxLen) return fail(JL_EINVAL, "L must be in [1, 2^30] (got %lld)", (long long)L);
+    if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1 (got %lld)", (long long)w_pretrained);
+    if (int rc = check_rope(head_dim, rope_base)) return rc;
+    if (int rc = check_fi_ramp(fi_alpha, fi_beta)) return rc;
+    const size_t need = jl::table_bytes_for(L, (int)head_dim);
+    if (table_bytes_needed) *table_bytes_needed = need;
+    if (!table) return JL_OK;
+    if (!aligned16(table)) return fail(JL_EINVAL, "table must be 16-byte aligned");
+    if (table_bytes < need)
+        return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
+    (void)hipGetLastError();
+    hipError_t e = jl::launch_table_fill_fi(table, L, (int)head_dim, rope_base, w_pretrained, fi_alpha, fi_beta,
+                                            static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(JL_EHIP, "table fill launch failed: %s", hipGetErrorString(e));
+    return JL_OK;
+}
+
+JL_API int jl_fi_table_fill_host(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base,
+                                 double fi_alpha, double fi_beta, void* table, size_t table_bytes) {
+    g_err.clear();
+    if (!table) return fail(JL_EINVAL, "table is NULL");
+    if (L < 1 || L > kMaxLen) return fail(JL_EINVAL, "L must be in [1, 2^30] (got %lld)", (long long)L);
+    if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1 (got %lld)", (long long)w_pretrained);
+    if (int rc = check_rope(head_dim, rope_base)) return rc;
+    if (int rc = check_fi_ramp(fi_alpha, fi_beta)) return rc;
+    const size_t need = jl::table_bytes_for(L, (int)head_dim);
+    if (table_bytes < need) return fail(JL_ESPACE, "table holds %zu bytes, %zu needed", table_bytes, need);
+    jl::table_fill_fi_host(table, L, (int)head_dim, rope_base, w_pretrained, fi_alpha, fi_beta);
     return JL_OK;
 }
 
@@ -179,6 +233,7 @@ jl::PrefillParams make_prefill_params(const void* q, const void* k, const void* 
     p.head_dim = (int)D;
     p.krot = krot;
     p.mode = jl::kFused;
+    p.table_key = jl::TableKey{jl::kTableMagic, 0, 0, 0.0, 0.0};
     return p;
 }
 
@@ -186,18 +241,25 @@ jl::PrefillParams make_prefill_params(const void* q, const void* k, const void* 
 int prefill_impl(const char* who, const void* q, const void* k, const void* v, void* out, float* lse, int in_dtype,
                  int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Lkv, int64_t Hq, int64_t Hkv, int64_t D,
                  int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
-                 size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                 size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream,
+                 const FiArgs* fi = nullptr) {
     g_err.clear();
     if (int rc = check_prefill(who, q, k, v, out, lse, in_dtype, out_dtype, B, Lq, L, Lkv, Hq, Hkv, D, w0,
                                w_pretrained, rope_base, sm_scale, table, table_bytes, workspace))
         return rc;
+    if (fi)
+        if (int rc = check_fi_ramp(fi->alpha, fi->beta)) return rc;
     size_t ws_need = 0;
     jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D, w_pretrained, &ws_need);
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
         return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : (size_t)0,
                     ws_need);
-    const jl::PrefillParams p = make_prefill_params(q, k, v, out, lse, B, Lq, L, Lkv, Hq, Hkv, D, w0, w_pretrained,
-                                                    rope_base, sm_scale, table, workspace);
+    jl::PrefillParams p = make_prefill_params(q, k, v, out, lse, B, Lq, L, Lkv, Hq, Hkv, D, w0, w_pretrained,
+                                              rope_base, sm_scale, table, workspace);
+    if (fi) {
+        p.G = fi_group(L, w_pretrained);
+        p.table_key = jl::TableKey{jl::kTableMagicFI, L, w_pretrained, fi->alpha, fi->beta};
+    }
     (void)hipGetLastError();
     hipError_t e = jl::launch_prefill(p, in_dtype, out_dtype, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
@@ -241,6 +303,17 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
                               size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
     return prefill_impl("prefill", q, k, v, out, lse, in_dtype, out_dtype, B, L, L, L, Hq, Hkv, D, w0,
                         w_pretrained, rope_base, sm_scale, table, table_bytes, workspace, workspace_bytes, hip_stream);
+}
+
+JL_API int jl_bifocal_prefill_fi(const void* q, const void* k, const void* v, void* out, float* lse, int in_dtype,
+                                 int out_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                                 int64_t w_pretrained, double rope_base, double fi_alpha, double fi_beta,
+                                 float sm_scale, const void* table, size_t table_bytes, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+    const FiArgs fi{fi_alpha, fi_beta};
+    return prefill_impl("prefill_fi", q, k, v, out, lse, in_dtype, out_dtype, B, L, L, L, Hq, Hkv, D, w0,
+                        w_pretrained, rope_base, sm_scale, table, table_bytes, workspace, workspace_bytes, hip_stream,
+                        &fi);
 }
 
 JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
@@ -372,9 +445,9 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
                 int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
                 int64_t w_pretrained, double rope_base, float sm_scale, const void* table, size_t table_bytes,
                 void* workspace, size_t workspace_bytes, void* hip_stream, void* krot = nullptr,
-                jl_rotated_keys* rk_state = nullptr) {
+                jl_rotated_keys* rk_state = nullptr, const FiArgs* fi = nullptr) {
     g_err.clear();
-    if (!q || !k_cache || !v_cache || !out || !table || !workspace)
+    if (!q || !k_cache || !v_cache || !out || (!table && !fi) || !workspace)
         return fail(JL_EINVAL, "%s: q, the caches, out, table and workspace must be non-NULL", who);
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(table) ||
         !aligned16(workspace) || !aligned16(lse))
@@ -398,9 +471,13 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     const int64_t R = Hq / Hkv;
     if (R != 1 && R != 2 && R != 4 && R != 8 && R != 16)
         return fail(JL_EUNSUPPORTED, "GQA ratio Hq/Hkv = %lld not supported (1..16, power of 2)", (long long)R);
-    const size_t need = jl::table_bytes_for(L, (int)D);
-    if (table_bytes < need)
-        return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
+    if (fi) {
+        if (int rc = check_fi_ramp(fi->alpha, fi->beta)) return rc;
+    } else {
+        const size_t need = jl::table_bytes_for(L, (int)D);
+        if (table_bytes < need)
+            return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
+    }
     size_t ws_need = 0;
     jl_bifocal_decode_workspace(B, Hq, D, L, &ws_need);
     if (workspace_bytes < ws_need)
@@ -423,7 +500,8 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     p.lse = lse;
     p.ws = static_cast<float*>(workspace);
     p.table = static_cast<const jl::TableHeader*>(table);
-    p.TF = reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes);
+    p.TF = table ? reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes) : nullptr;
+    p.table_key = jl::TableKey{jl::kTableMagic, 0, 0, 0.0, 0.0};
     p.B = B;
     p.L = L;
     p.Lmax = block_table ? 0 : Lmax;
@@ -443,6 +521,12 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     p.head_dim = (int)D;
     p.krot = krot;
     p.rot_row = -1;
+    if (fi) {
+        p.G = fi_group(L, w_pretrained);
+        p.fi = 1;
+        for (int i = 0; i < (int)D / 2; ++i)
+            p.fi_phi[i] = jl::fi_phi(rope_base, (int)D, L, w_pretrained, fi->alpha, fi->beta, i);
+    }
     (void)hipGetLastError();
     if (krot) {
         // bring the rotated-key cache up to date for this step: every key with
@@ -494,6 +578,17 @@ JL_API int jl_bifocal_decode_rkc(const void* q, const void* k_cache, const void*
     return decode_impl("decode_rkc", q, k_cache, v_cache, nullptr, 0, 0, 0, out, lse, in_dtype, out_dtype, B, L, Lmax,
                        Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
                        workspace_bytes, hip_stream, krot_cache, state);
+}
+
+JL_API int jl_bifocal_decode_fi(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq,
+                                int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained, double rope_base,
+                                double fi_alpha, double fi_beta, float sm_scale, void* workspace,
+                                size_t workspace_bytes, void* hip_stream) {
+    const FiArgs fi{fi_alpha, fi_beta};
+    return decode_impl("decode_fi", q, k_cache, v_cache, nullptr, 0, 0, 0, out, lse, in_dtype, out_dtype, B, L, Lmax,
+                       Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, nullptr, 0, workspace, workspace_bytes,
+                       hip_stream, nullptr, nullptr, &fi);
 }
 
 JL_API int jl_bifocal_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -13,20 +13,63 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr uint32_t kTableMagic = 0x324C544Au;  // "JTL2"
+constexpr uint32_t kTableMagic = 0x324C544Au;    // "JTL2": offset table
+constexpr uint32_t kTableMagicFI = 0x3146544Au;  // "JTF1": interpolation table
 constexpr int kTableHeaderBytes = 64;
 
 // Device/host view of the correction-angle table header.  The header is
-// followed by rows TF[n][i] = (cos, sin)(n * theta_i), n < n_cover, i < D/2,
-// each angle formed in float64 and rounded once to fp32.
+// followed by rows TF[n][i] = (cos, sin)(n * phi_i), n < n_cover, i < D/2,
+// each angle formed in float64 and rounded once to fp32.  Offset tables
+// (the aliasing correction) have phi_i = theta_i and are indexed by the
+// offset n = p - floor(p/G); interpolation tables have
+// phi_i = theta_i - theta'_i (the frequency-interpolation remote view) and
+// are indexed by the position p.
 struct TableHeader {
     uint32_t magic;
     int32_t head_dim;
-    int64_t n_cover;     // covers offsets n < n_cover
+    int64_t n_cover;     // covers rows n < n_cover
     double rope_base;
-    int64_t pad[5];
+    // interpolation tables only, zero in offset tables: the length and
+    // pretrained window that fix s = L / w_pretrained, and the ramp bounds
+    int64_t fi_L;
+    int64_t fi_w_pretrained;
+    double fi_alpha;
+    double fi_beta;
+    int64_t pad;
 };
 static_assert(sizeof(TableHeader) == kTableHeaderBytes, "header size");
+
+// What a kernel expects of the table it is given (compared with the header
+// before any row is read).
+struct TableKey {
+    uint32_t magic;
+    int64_t fi_L;
+    int64_t fi_w_pretrained;
+    double fi_alpha;
+    double fi_beta;
+};
+
+__host__ __device__ inline bool table_matches(const TableHeader* th, const TableKey& key, int D, double base,
+                                              int64_t L) {
+    return th->magic == key.magic && th->head_dim == D && th->rope_base == base && th->n_cover >= L &&
+           th->fi_L == key.fi_L && th->fi_w_pretrained == key.fi_w_pretrained && th->fi_alpha == key.fi_alpha &&
+           th->fi_beta == key.fi_beta;
+}
+
+// phi_i = theta_i - theta'_i of the frequency-interpolation remote view:
+// theta'_i = (1 - gamma_i) theta_i / s + gamma_i theta_i with
+// s = max(1, L / w_pretrained) and gamma_i a linear ramp from 0 (at alpha)
+// to 1 (at beta) over r_i = w_pretrained theta_i / (2 pi), the turns of
+// pair i over the pretrained window.  So phi_i = theta_i (1 - gamma_i)(1 - 1/s).
+__host__ __device__ inline double fi_phi(double base, int D, int64_t L, int64_t w_pretrained, double alpha,
+                                         double beta, int i) {
+    const double theta = pow(base, -(2.0 * (double)i) / (double)D);
+    const double s = (double)L > (double)w_pretrained ? (double)L / (double)w_pretrained : 1.0;
+    const double r = (double)w_pretrained * theta / 6.283185307179586476925286766559;
+    double g = (r - alpha) / (beta - alpha);
+    g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+    return theta * (1.0 - g) * (1.0 - 1.0 / s);
+}
 
 __host__ __device__ inline size_t table_bytes_for(int64_t n_cover, int head_dim) {
     return (size_t)kTableHeaderBytes + (size_t)n_cover * (size_t)(head_dim / 2) * 8u;

@@ -96,7 +96,20 @@ __device__ inline void load_v(DecodeTile<D>& t, const __bf16* __restrict__ vc, i
     }
 }
 
-template <int D, bool OUT_BF16, bool PAGED, bool RKC>
+// (cos, sin)(n * phi) of the frequency-interpolation view, formed in the
+// kernel: the angle is reduced to [-pi, pi] in float64 (n * phi reaches
+// ~1e5 rad), then sin and cos are taken in fp32 (error ~2e-7 rad).
+__device__ inline float2 fi_cs(double phi, int64_t n) {
+    constexpr double kInvTwoPi = 0.15915494309189533577;
+    constexpr double kTwoPi = 6.283185307179586476925;
+    const double turns = (double)n * phi * kInvTwoPi;
+    const float a = (float)((turns - rint(turns)) * kTwoPi);
+    float sn, cs;
+    sincosf(a, &sn, &cs);
+    return make_float2(cs, sn);
+}
+
+template <int D, bool OUT_BF16, bool PAGED, bool RKC, bool FI>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeParams p) {
     constexpr int HALF = D / 2;
     constexpr int NC = D / 32;
@@ -141,6 +154,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     auto ksrc = [&](int kb) -> const __bf16* { return (RKC && kb + kWaveKeys <= kloc) ? krc : kc; };
     const __bf16* __restrict__ vc = static_cast<const __bf16*>(p.v);
     const float2* __restrict__ TF = p.TF;
+    // row n, pair i of the correction table (formed here for the
+    // frequency-interpolation view, which has no table)
+    auto tf = [&](int64_t n, int i) -> float2 {
+        if constexpr (FI) return fi_cs(p.fi_phi[i], n);
+        else return TF[n * HALF + i];
+    };
     const int64_t row = p.Hkv * D;
     const int64_t cache_b = PAGED ? (int64_t)g * D : (int64_t)b * p.Lmax * row + (int64_t)g * D;
 
@@ -200,18 +219,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         wa_o = cache_b + p.rot_row * row + lane;
         wa_x = (float)kc[wa_o];
         wa_y = (float)kc[wa_o + HALF];
-        wa_cs = TF[(p.rot_row - p.rot_row / G) * HALF + lane];
+        wa_cs = tf(p.rot_row - p.rot_row / G, lane);
     }
 
-    if (tid == 0) {
-        const TableHeader* th = p.table;
-        s_bad = !(th->magic == kTableMagic && th->head_dim == D && th->rope_base == p.rope_base &&
-                  th->n_cover >= p.L);
-    }
+    if (tid == 0) s_bad = FI ? 0 : !table_matches(p.table, p.table_key, D, p.rope_base, p.L);
     // rows 0..32 of the table are cos/sin(dn * theta_i); only rows < L are
     // guaranteed to exist and dn <= L-1, so copy no further
     if (!RKC)
-        for (int i = tid; i < min(JROWS, L) * HALF; i += kDecThreads) sJ[(i / HALF) * JSTR + i % HALF] = TF[i];
+        for (int i = tid; i < min(JROWS, L) * HALF; i += kDecThreads)
+            sJ[(i / HALF) * JSTR + i % HALF] = tf(i / HALF, i % HALF);
     __syncthreads();
     const bool bad = s_bad;
 
@@ -236,7 +252,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     float x = (float)qf[c][j], y = (float)qf[c + NC / 2][j];
-                    rotate_back(x, y, TF[(int64_t)nq * HALF + 32 * c + 8 * gq + j]);
+                    rotate_back(x, y, tf(nq, 32 * c + 8 * gq + j));
                     qrem[c][j] = (__bf16)x;
                     qrem[c + NC / 2][j] = (__bf16)y;
                 }
@@ -256,7 +272,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     // read once, then advanced by the step's offset increment (<= 32) from the
     // LDS rows, so no step waits on a table load.
     float2 base = make_float2(1.f, 0.f);
-    if (!RKC && lane < HALF && wstart < wend && G > 1) base = TF[(int64_t)(wstart - wstart / G) * HALF + lane];
+    if (!RKC && lane < HALF && wstart < wend && G > 1) base = tf(wstart - wstart / G, lane);
 
     // the corrected query for the current step: R(nb) applied to R(-n_q) q
     bf16x8 qit[NC];
@@ -516,11 +532,17 @@ template <int D, bool OUT_BF16>
 hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
     const dim3 grid(p.n_split, p.Hkv / p.heads_per_wg, p.B);
     if (p.block_table)
-        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, true, false>), grid, dim3(kDecThreads), 0, stream, p);
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, true, false, false>), grid, dim3(kDecThreads), 0,
+                           stream, p);
     else if (p.krot)
-        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false, true>), grid, dim3(kDecThreads), 0, stream, p);
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false, true, false>), grid, dim3(kDecThreads), 0,
+                           stream, p);
+    else if (p.fi)
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false, false, true>), grid, dim3(kDecThreads), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false, false>), grid, dim3(kDecThreads), 0, stream, p);
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false, false, false>), grid, dim3(kDecThreads), 0,
+                           stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(p.Hq, p.B, D / 32), dim3(1024), 0, stream, p);

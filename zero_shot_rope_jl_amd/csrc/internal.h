@@ -45,6 +45,11 @@ struct PrefillParams {
     // k / page_size] of k/v, which hold n_pages pages of page_size rows
     const int32_t* block_table;
     int64_t page_size, max_pages, n_pages;
+    // the table the kernels expect: an offset table, or for the
+    // frequency-interpolation view a position-indexed table for this call
+    // (then G is set to max(2, L) when L > w_pretrained, so that the row of
+    // position p, p - floor(p/G), is p itself)
+    TableKey table_key;
 };
 
 enum PrefillMode {
@@ -85,6 +90,12 @@ struct DecodeParams {
     // next step (the first local row, which the next step reads as remote
     // when G stays); -1 for none
     int64_t rot_row;
+    TableKey table_key;
+    // frequency-interpolation remote view: no table; the kernel forms the
+    // rows it reads, (cos, sin)(n * fi_phi[i]) at positions n, from the
+    // per-pair phi_i below (G = max(2, L) as for prefill); 0 otherwise
+    int fi;
+    double fi_phi[64];
 };
 
 // Rows [r0, r1) of a [B, Lmax, Hkv, D] bf16 key cache rotated into their
@@ -128,6 +139,10 @@ inline void decode_split_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, i
 hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double rope_base,
                              hipStream_t stream);
 void table_fill_host(void* table, int64_t n_cover, int head_dim, double rope_base);
+hipError_t launch_table_fill_fi(void* table, int64_t L, int head_dim, double rope_base, int64_t w_pretrained,
+                                double alpha, double beta, hipStream_t stream);
+void table_fill_fi_host(void* table, int64_t L, int head_dim, double rope_base, int64_t w_pretrained, double alpha,
+                        double beta);
 
 // The three pass outputs of the unfused prefill and where their merge goes.
 struct MergeParams {

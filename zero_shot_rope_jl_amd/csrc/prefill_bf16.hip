@@ -166,8 +166,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 
     if (tid == 0) {
         const TableHeader* th = p.table;
-        s_bad = !(th->magic == kTableMagic && th->head_dim == D && th->rope_base == p.rope_base &&
-                  th->n_cover >= p.L);
+        s_bad = !table_matches(th, p.table_key, D, p.rope_base, p.L);
     }
     __syncthreads();
     if (s_bad) {

@@ -36,6 +36,59 @@ __global__ void table_fill_kernel(char* table, int64_t n_cover, int D, double ba
     }
 }
 
+// Frequency-interpolation table for one (L, w_pretrained, alpha, beta):
+// rows p < L of (cos, sin)(p * phi_i), the rotation that moves a stored
+// RoPE(x, p) to the interpolated phase p * theta'_i (Jet-Long §4.7 ablation).
+__host__ __device__ inline TableHeader make_fi_header(int64_t L, int D, double base, int64_t w_pre, double alpha,
+                                                      double beta) {
+    TableHeader h = make_header(L, D, base);
+    h.magic = kTableMagicFI;
+    h.fi_L = L;
+    h.fi_w_pretrained = w_pre;
+    h.fi_alpha = alpha;
+    h.fi_beta = beta;
+    return h;
+}
+
+__host__ __device__ inline float2 fi_entry(double phi, int64_t p) {
+    const double a = (double)p * phi;
+    return make_float2((float)cos(a), (float)sin(a));
+}
+
+__global__ void table_fill_fi_kernel(char* table, int64_t L, int D, double base, int64_t w_pre, double alpha,
+                                     double beta) {
+    const int half = D / 2;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    float2* ent = reinterpret_cast<float2*>(table + kTableHeaderBytes);
+    if (idx < L * half) {
+        const int i = (int)(idx % half);
+        ent[idx] = fi_entry(fi_phi(base, D, L, w_pre, alpha, beta, i), idx / half);
+    }
+    if (idx == 0) *reinterpret_cast<TableHeader*>(table) = make_fi_header(L, D, base, w_pre, alpha, beta);
+}
+
+hipError_t launch_table_fill_fi(void* table, int64_t L, int head_dim, double rope_base, int64_t w_pretrained,
+                                double alpha, double beta, hipStream_t stream) {
+    const int64_t total = L * (head_dim / 2);
+    const int threads = 256;
+    const int blocks = (int)((total + threads - 1) / threads);
+    hipLaunchKernelGGL(table_fill_fi_kernel, dim3(blocks), dim3(threads), 0, stream, static_cast<char*>(table), L,
+                       head_dim, rope_base, w_pretrained, alpha, beta);
+    return hipGetLastError();
+}
+
+void table_fill_fi_host(void* table, int64_t L, int head_dim, double rope_base, int64_t w_pretrained, double alpha,
+                        double beta) {
+    const int half = head_dim / 2;
+    TableHeader h = make_fi_header(L, head_dim, rope_base, w_pretrained, alpha, beta);
+    memcpy(table, &h, sizeof(h));
+    float2* ent = reinterpret_cast<float2*>(static_cast<char*>(table) + kTableHeaderBytes);
+    for (int i = 0; i < half; ++i) {
+        const double phi = fi_phi(rope_base, head_dim, L, w_pretrained, alpha, beta, i);
+        for (int64_t p = 0; p < L; ++p) ent[p * half + i] = fi_entry(phi, p);
+    }
+}
+
 hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double rope_base,
                              hipStream_t stream) {
     const int64_t total = n_cover * (head_dim / 2);
