@@ -28,6 +28,12 @@
 // Each workgroup leaves one fp32 partial (acc[D], m, l) per query head; the
 // combine kernel merges a head's partials with the log-sum-exp rule (§3.3
 // Eq. 6 with disjoint key sets).
+//
+// Variants of the split kernel (template flags): PAGED reads the cache
+// through a block table; RKC reads remote keys already rotated from a
+// second cache (and writes ahead the row the next step needs); FI uses the
+// frequency-interpolation remote view of the §4.7 ablation, whose table
+// rows (cos, sin)(n * phi_i) the kernel forms itself.
 #include <math.h>
 
 #include "internal.h"
