@@ -438,6 +438,30 @@ def cpu_baseline(si, w, x, n_rows):
                       f"(float64 NumPy oracle incl. the remote view of all {w.L} keys), {sec:.1f} s"}
 
 
+def cpu_baseline_decode(si, n_steps=2):
+    """The float64 oracle on the first n_steps decode steps of the 128K-cache
+    workload (one query token over every cached key per step)."""
+    import oracle
+    dw = si.DECODE_WORKLOAD
+    kc_np, vc_np = si.make_decode_prompt(dw)
+    kc = si.f32_from_bf16_bits(kc_np).astype(np.float64)
+    vc = si.f32_from_bf16_bits(vc_np).astype(np.float64)
+    del kc_np, vc_np
+    sec = 0.0
+    for s in range(1, n_steps + 1):
+        q, kn, vn = si.make_decode_step(dw, s)
+        row = dw.prompt_len + s - 1
+        kc[:, row] = si.f32_from_bf16_bits(kn[:, 0])
+        vc[:, row] = si.f32_from_bf16_bits(vn[:, 0])
+        q64 = si.f32_from_bf16_bits(q[:, 0]).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.decode_attention(q64, kc, vc, row + 1, dw.w0, dw.w_pretrained, dw.rope_base, dw.sm_scale)
+        sec += time.perf_counter() - t0
+    return {"value": sec / n_steps * 1e6, "unit": "µs/step", "kind": "oracle",
+            "sample": f"{dw.name}: the first {n_steps} of its {dw.steps} steps (float64 NumPy oracle, every "
+                      f"cached key incl. its remote view), {sec:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -513,6 +537,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
         result["cpu_baseline"] = cpu_baseline(si, w, x, args.cpu_rows)
+        if not args.skip_decode:
+            result["cpu_baseline_decode"] = cpu_baseline_decode(si)
     print(json.dumps(result), flush=True)
 
 
