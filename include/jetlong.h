@@ -354,6 +354,28 @@ JL_API int jl_table_fill_host(int64_t L, int64_t head_dim, double rope_base, voi
                        size_t table_bytes);
 
 /*
+ * jl_rope_interleaved_to_half -- for models whose RoPE rotates adjacent
+ * channel pairs (2i, 2i+1) instead of (i, i + D/2): reorder the channels of
+ * n_rows rows of D channels so that pair i lands on (i, i + D/2),
+ *     out[r][i] = x[r][2i],  out[r][i + D/2] = x[r][2i + 1].
+ * Applied to q and k alike (never to v), it makes every call of this
+ * library compute that model's scores exactly: a dot product is unchanged
+ * by a common permutation of its operands' channels, and each pair's
+ * rotation moves with the pair.  The output (a function of v) is not
+ * permuted.  (A model can instead permute its q and k projection weights
+ * once.)
+ *
+ *   x, out   device [n_rows, D] of `dtype` (JL_BF16 or JL_F32), 16-byte
+ *            aligned, not overlapping; q [B, L, Hq, D] is n_rows = B*L*Hq
+ *
+ * Enqueued on hip_stream.  Errors: JL_EINVAL (NULL, misaligned or
+ * overlapping buffers, unknown dtype, n_rows < 0), JL_EUNSUPPORTED (D not
+ * 64 or 128), JL_EHIP.
+ */
+JL_API int jl_rope_interleaved_to_half(const void* x, void* out, int dtype, int64_t n_rows, int64_t D,
+                                       void* hip_stream);
+
+/*
  * ---- Frequency-interpolation remote view (the ablation of §4.7) ----------
  *
  * The same bifocal rule with the remote pairs (q - k > w0) scored after

@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol():
                            "jl_bifocal_decode", "jl_bifocal_decode_paged", "jl_table_fill_host",
                            "jl_bifocal_prefill_unfused_workspace", "jl_bifocal_prefill_unfused",
                            "jl_bifocal_prefill_chunk_paged", "jl_bifocal_decode_rkc", "jl_fi_table",
-                           "jl_fi_table_fill_host", "jl_bifocal_prefill_fi", "jl_bifocal_decode_fi"])
+                           "jl_fi_table_fill_host", "jl_bifocal_prefill_fi", "jl_bifocal_decode_fi",
+                           "jl_rope_interleaved_to_half"])
     for s in syms:
         assert hasattr(jl.lib, s), s
     assert jl.jl_version() == 8
@@ -376,3 +377,15 @@ def test_prefill_fi_validation(over, code):
 ])
 def test_decode_fi_validation(over, code):
     assert _decode_fi(**over) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, jl.JL_BF16, 10, 128), jl.JL_EINVAL), ((FAKE, None, jl.JL_BF16, 10, 128), jl.JL_EINVAL),
+    ((FAKE, FAKE + 4096, 7, 10, 128), jl.JL_EINVAL), ((FAKE, FAKE + 4096, jl.JL_BF16, 10, 96), jl.JL_EUNSUPPORTED),
+    ((FAKE, FAKE + 4096, jl.JL_BF16, -1, 128), jl.JL_EINVAL), ((FAKE + 8, FAKE + 4096, jl.JL_BF16, 10, 128),
+                                                              jl.JL_EINVAL),
+    ((FAKE, FAKE + 2048, jl.JL_BF16, 10, 128), jl.JL_EINVAL),    # 10 rows of 256 B overlap
+    ((FAKE + 2048, FAKE, jl.JL_F32, 5, 128), jl.JL_EINVAL),      # 5 rows of 512 B overlap
+])
+def test_interleaved_to_half_validation(args, code):
+    assert jl.lib.jl_rope_interleaved_to_half(*args, None) == code

@@ -15,7 +15,7 @@ from .binding import (  # noqa: F401
     jl_bifocal_prefill_unfused, jl_bifocal_prefill_unfused_workspace, alloc_prefill_unfused_workspace,
     jl_bifocal_prefill_chunk_paged, jl_bifocal_decode_rkc, RotatedKeyCache, JLRotatedKeys,
     jl_bifocal_decode_paged, jl_fi_table, jl_fi_table_fill_host, alloc_fi_table, jl_bifocal_prefill_fi,
-    jl_bifocal_decode_fi,
+    jl_bifocal_decode_fi, jl_rope_interleaved_to_half,
     jl_bifocal_decode_workspace, jl_table_fill_host, alloc_table, alloc_prefill_workspace,
     alloc_decode_workspace,
 )

@@ -78,6 +78,8 @@ def _load():
     L.jl_bifocal_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                           i64, i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz,
                                           vp, sz, vp]
+    L.jl_rope_interleaved_to_half.restype = ctypes.c_int
+    L.jl_rope_interleaved_to_half.argtypes = [vp, vp, ctypes.c_int, i64, i64, vp]
     d = ctypes.c_double
     L.jl_fi_table.restype = ctypes.c_int
     L.jl_fi_table.argtypes = [i64, i64, i64, d, d, d, vp, sz, ctypes.POINTER(sz), vp]
@@ -497,3 +499,19 @@ def jl_bifocal_decode_fi(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretr
                                     fi_beta, sm_scale, _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
+
+
+def jl_rope_interleaved_to_half(x, out=None, stream=None):
+    """Channels of q or k [..., D] from interleaved RoPE pairs (2i, 2i+1) to
+    the rotate-half pairs (i, i + D/2); apply to q and k, not v."""
+    if out is None:
+        out = _torch().empty_like(x)
+    _need_device(x, out)
+    if tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype:
+        raise ValueError("out must match x")
+    if not x.is_contiguous() or not out.is_contiguous():
+        raise ValueError("x and out must be contiguous")
+    D = x.shape[-1]
+    _check(lib.jl_rope_interleaved_to_half(_ptr(x), _ptr(out), _dtype_code(x), x.numel() // D, D,
+                                           _stream(stream)))
+    return out

@@ -156,6 +156,24 @@ JL_API int jl_fi_table_fill_host(int64_t L, int64_t w_pretrained, int64_t head_d
     return JL_OK;
 }
 
+JL_API int jl_rope_interleaved_to_half(const void* x, void* out, int dtype, int64_t n_rows, int64_t D,
+                                       void* hip_stream) {
+    g_err.clear();
+    if (!x || !out) return fail(JL_EINVAL, "x and out must be non-NULL");
+    if (dtype != JL_F32 && dtype != JL_BF16) return fail(JL_EINVAL, "unknown dtype code %d", dtype);
+    if (D != 64 && D != 128) return fail(JL_EUNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)D);
+    if (n_rows < 0 || n_rows > (int64_t(1) << 40)) return fail(JL_EINVAL, "n_rows out of range (%lld)", (long long)n_rows);
+    if (!aligned16(x) || !aligned16(out)) return fail(JL_EINVAL, "x and out must be 16-byte aligned");
+    const int eb = dtype == JL_BF16 ? 2 : 4;
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(out);
+    const uintptr_t bytes = (uintptr_t)n_rows * (uintptr_t)D * (uintptr_t)eb;
+    if (n_rows > 0 && xa < oa + bytes && oa < xa + bytes) return fail(JL_EINVAL, "x and out overlap");
+    (void)hipGetLastError();
+    hipError_t e = jl::launch_interleaved_to_half(x, out, eb, n_rows, (int)D, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(JL_EHIP, "channel reorder launch failed: %s", hipGetErrorString(e));
+    return JL_OK;
+}
+
 JL_API int jl_bifocal_prefill_workspace(int in_dtype, int64_t B, int64_t L, int64_t Hkv, int64_t D,
                                         int64_t w_pretrained, size_t* bytes) {
     g_err.clear();

@@ -139,6 +139,10 @@ inline void decode_split_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, i
 hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double rope_base,
                              hipStream_t stream);
 void table_fill_host(void* table, int64_t n_cover, int head_dim, double rope_base);
+// Channel reorder (interleaved RoPE pairs -> rotate-half pairs) of n_rows
+// rows of D channels, elements of elem_bytes (2: bf16, 4: fp32).
+hipError_t launch_interleaved_to_half(const void* x, void* out, int elem_bytes, int64_t n_rows, int D,
+                                      hipStream_t stream);
 hipError_t launch_table_fill_fi(void* table, int64_t L, int head_dim, double rope_base, int64_t w_pretrained,
                                 double alpha, double beta, hipStream_t stream);
 void table_fill_fi_host(void* table, int64_t L, int head_dim, double rope_base, int64_t w_pretrained, double alpha,
