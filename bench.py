@@ -228,6 +228,30 @@ def bench_fi(torch, jl, args, w, x):
     return ms, table_ms
 
 
+def bench_reorder(torch, jl, w, x):
+    """jl_rope_interleaved_to_half over the workload's q and k (what a model
+    with interleaved RoPE pairs adds per call), ms for both."""
+    q, k = (to_dev(torch, x[n], w.dtype) for n in "qk")
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    jl.jl_rope_interleaved_to_half(q, qo)
+    jl.jl_rope_interleaved_to_half(k, ko)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(3):
+        jl.jl_rope_interleaved_to_half(q, qo)
+        jl.jl_rope_interleaved_to_half(k, ko)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 3
+    gbs = 2.0 * (q.numel() + k.numel()) * q.element_size() / (ms * 1e-3) / 1e9
+    log(f"[bench] interleaved-pair reorder of q and k: {ms:.3f} ms ({gbs:.0f} GB/s)")
+    del q, k, qo, ko
+    torch.cuda.empty_cache()
+    return ms, gbs
+
+
 def bench_chunk(torch, jl, args, w, x, Lq=4096, page_size=256):
     """The last Lq-token chunk of the workload over its cache, contiguous and
     held in shuffled pages (jl_bifocal_prefill_chunk / _chunk_paged)."""
@@ -520,6 +544,10 @@ def main():
                     "(ramp bounds 1 and 32 turns per pretrained window)",
             "ms_per_call": round(fms, 4), "table_build_ms": round(tms, 4),
             "tflops": round(flops / (fms * 1e-3) / 1e12, 2)}
+    if args.fi_steps > 0:
+        rms, rgbs = bench_reorder(torch, jl, w, x)
+        result["interleaved_reorder"] = {"what": "channel reorder of q and k for interleaved RoPE pairs",
+                                         "ms_per_call": round(rms, 4), "gb_per_s": round(rgbs, 1)}
     if args.chunk_steps > 0:
         result["chunk"] = {"what": "last 4096 tokens of the workload as one chunk over the other 126976 keys",
                            **bench_chunk(torch, jl, args, w, x)}
