@@ -72,6 +72,12 @@ def measured_traffic():
         return {}
 
 
+# the kernels whose HBM traffic the roofline objects report (names as the
+# profiler prints them)
+PREFILL_KERNEL = "jl::prefill_bf16_kernel<128, true, 0, false>"
+DECODE_KERNELS = ("jl::decode_split_kernel<128, true, false, false, false>", "jl::decode_combine_kernel<128, true>")
+
+
 def pick(traffic, *prefixes):
     """Summed bytes per dispatch of the kernels whose names start with any of the prefixes."""
     hits = [v for k, v in traffic.items() if k.startswith(prefixes)]
@@ -521,7 +527,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.L, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": pick(traffic, "jl::prefill_bf16_kernel<128, true, 0, false>"),
+                     "traffic": pick(traffic, PREFILL_KERNEL),
                      "flops_per_launch": flops},
         "prefill_ms_per_call": pstats,
     }
@@ -558,8 +564,7 @@ def main():
             "steps_timed": args.decode_passes * dw.steps,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": pick(traffic, "jl::decode_split_kernel<128, true, false, false>",
-                                         "jl::decode_combine_kernel"),
+                         "traffic": pick(traffic, *DECODE_KERNELS),
                          "bytes_per_step": bytes_step},
         }
     if not args.no_cpu_baseline:
