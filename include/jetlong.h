@@ -333,6 +333,10 @@ typedef struct jl_rotated_keys {
  * (the remote view of each key is rounded once, in the cache).  Everything
  * else as for jl_bifocal_decode.
  *
+ * A call given a table that does not match it (its output is NaN, as for
+ * jl_bifocal_decode) also writes NaN into the rows it rotates, so later
+ * steps stay NaN until `state` is reset to {0, 0}.
+ *
  * Errors: as for jl_bifocal_decode, plus JL_EINVAL for a NULL or
  * misaligned krot_cache, a NULL state, or state->rows outside [0, Lmax].
  */

@@ -103,3 +103,30 @@ def test_rkc_steps_across_a_change_of_g():
     torch.cuda.synchronize()
     assert fresh.state.rows == rows
     assert torch.equal(rkc.keys[:, :rows], fresh.keys[:, :rows])
+
+
+def test_rkc_a_mismatched_table_poisons_until_reset():
+    """A table built for another RoPE base: that step is NaN and so is the
+    next one with the right table under the same G (4 for L = 700 .. 702;
+    the cache rows it wrote are NaN); after a reset the steps match the
+    oracle again."""
+    require_gpu()
+    B, Lmax, Hq, Hkv, D, w_pre, w0, base = 1, 900, 8, 2, 128, 200, 50, 1e4
+    scale = D ** -0.5
+    qb, kb, vb = _cache(B, Lmax, Hq, Hkv, D, seed=11)
+    q, kc, vc = to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16")
+    good, wrong = jl.alloc_table(Lmax, D, base), jl.alloc_table(Lmax, D, 5e5)
+    ws = jl.alloc_decode_workspace(B, Hq, D, Lmax)
+    rkc = jl.RotatedKeyCache(kc)
+    out = torch.empty((B, 1, Hq, D), dtype=torch.float32, device="cuda")
+    jl.jl_bifocal_decode_rkc(q, kc, vc, rkc, out, None, 700, w0, w_pre, base, scale, wrong, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    jl.jl_bifocal_decode_rkc(q, kc, vc, rkc, out, None, 701, w0, w_pre, base, scale, good, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+    rkc.reset()
+    jl.jl_bifocal_decode_rkc(q, kc, vc, rkc, out, None, 702, w0, w_pre, base, scale, good, ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_attention(_f64(qb)[:, 0], _f64(kb), _f64(vb), 702, w0, w_pre, base, scale)
+    assert max_err(out.cpu().numpy()[:, 0], ref) <= TOL_BF16

@@ -555,8 +555,7 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
         const int64_t kloc = p.G == 1 ? 0 : (L - 1 - p.w0 > 0 ? L - 1 - p.w0 : 0);
         int64_t r0 = rk_state->G == p.G ? rk_state->rows : 0;
         if (r0 > kloc) r0 = kloc;
-        hipError_t er = jl::launch_rotate_rows(k_cache, krot, p.TF, B, Lmax, Hkv, (int)D, r0, kloc, p.G,
-                                               static_cast<hipStream_t>(hip_stream));
+        hipError_t er = jl::launch_rotate_rows(k_cache, krot, p, r0, kloc, static_cast<hipStream_t>(hip_stream));
         if (er != hipSuccess) return fail(JL_EHIP, "%s key rotation launch failed: %s", who, hipGetErrorString(er));
         if (kloc > 0) {
             p.rot_row = kloc;

@@ -416,7 +416,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     }
     if (bad_page) l_run = NAN;   // poisons this head's output through the merge
     if (write_ahead) {
-        rotate_back(wa_x, wa_y, wa_cs);
+        // a table that does not match the call leaves NaN in the cache, so
+        // later steps stay visibly wrong until the caller resets its state
+        if (bad) wa_x = wa_y = NAN;
+        else rotate_back(wa_x, wa_y, wa_cs);
         __bf16* kw = static_cast<__bf16*>(const_cast<void*>(p.krot));
         kw[wa_o] = (__bf16)wa_x;
         kw[wa_o + HALF] = (__bf16)wa_y;
@@ -562,12 +565,14 @@ namespace {
 // Rows [r0, r1) of every (batch, KV head) of a [B, Lmax, Hkv, D] bf16 key
 // cache rotated by their correction offset, table row n(k) = k - floor(k/G),
 // rounded to bf16, into the same place of krot (§3.2 Eq. 5 applied to the
-// cached keys).  One thread per 8 rotation pairs of a row; HBM-bound.
+// cached keys).  One thread per 8 rotation pairs of a row; HBM-bound.  A
+// table whose header does not match the call writes NaN rows instead.
 template <int D>
 __global__ __launch_bounds__(256) void rotate_rows_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kr,
                                                           const float2* __restrict__ TF, int64_t n_items,
                                                           int64_t Lmax, int Hkv, int64_t r0, int64_t nrows,
-                                                          int64_t G) {
+                                                          int64_t G, const TableHeader* table, TableKey key,
+                                                          double rope_base, int64_t L) {
     constexpr int HALF = D / 2;
     constexpr int CPR = HALF / 8;   // 8-pair items per row
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -596,25 +601,29 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const __bf16* __restri
         xo[2 * e + 1] = (__bf16)x1;
         yo[2 * e + 1] = (__bf16)y1;
     }
+    if (!table_matches(table, key, D, rope_base, L)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xo[e] = yo[e] = (__bf16)NAN;
+    }
     *reinterpret_cast<bf16x8*>(kr + o) = xo;
     *reinterpret_cast<bf16x8*>(kr + o + HALF) = yo;
 }
 
 }  // namespace
 
-hipError_t launch_rotate_rows(const void* k, void* krot, const float2* TF, int64_t B, int64_t Lmax, int64_t Hkv,
-                              int head_dim, int64_t r0, int64_t r1, int64_t G, hipStream_t stream) {
+hipError_t launch_rotate_rows(const void* k, void* krot, const DecodeParams& p, int64_t r0, int64_t r1,
+                              hipStream_t stream) {
     if (r1 <= r0) return hipSuccess;
-    const int64_t n_items = B * (r1 - r0) * Hkv * (head_dim / 16);
+    const int64_t n_items = p.B * (r1 - r0) * p.Hkv * (p.head_dim / 16);
     const unsigned blocks = (unsigned)((n_items + 255) / 256);
-    if (head_dim == 128)
+    if (p.head_dim == 128)
         hipLaunchKernelGGL((rotate_rows_kernel<128>), dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const __bf16*>(k), static_cast<__bf16*>(krot), TF, n_items, Lmax, (int)Hkv, r0,
-                           r1 - r0, G);
+                           static_cast<const __bf16*>(k), static_cast<__bf16*>(krot), p.TF, n_items, p.Lmax,
+                           (int)p.Hkv, r0, r1 - r0, p.G, p.table, p.table_key, p.rope_base, p.L);
     else
         hipLaunchKernelGGL((rotate_rows_kernel<64>), dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const __bf16*>(k), static_cast<__bf16*>(krot), TF, n_items, Lmax, (int)Hkv, r0,
-                           r1 - r0, G);
+                           static_cast<const __bf16*>(k), static_cast<__bf16*>(krot), p.TF, n_items, p.Lmax,
+                           (int)p.Hkv, r0, r1 - r0, p.G, p.table, p.table_key, p.rope_base, p.L);
     return hipGetLastError();
 }
 

@@ -99,9 +99,11 @@ struct DecodeParams {
 };
 
 // Rows [r0, r1) of a [B, Lmax, Hkv, D] bf16 key cache rotated into their
-// corrected view under G (the rotated-key cache of jl_bifocal_decode_rkc).
-hipError_t launch_rotate_rows(const void* k, void* krot, const float2* TF, int64_t B, int64_t Lmax, int64_t Hkv,
-                              int head_dim, int64_t r0, int64_t r1, int64_t G, hipStream_t stream);
+// corrected view under p.G (the rotated-key cache of jl_bifocal_decode_rkc),
+// with p's table, which is checked against p's key (NaN rows if it does not
+// match).
+hipError_t launch_rotate_rows(const void* k, void* krot, const DecodeParams& p, int64_t r0, int64_t r1,
+                              hipStream_t stream);
 
 // Decode split plan.  A workgroup has 8 waves that cover up to 4 KV heads
 // (wave w -> head w % WH, key sub-range w / WH) over one key range, so each
