@@ -32,6 +32,7 @@ CASES = [  # (B, L, Hq, Hkv, D, w_pre, w0, alpha, beta)
     (1, 1537, 16, 2, 128, 512, 200, 0.5, 8.0),     # GQA 8
     (1, 600, 4, 2, 128, 256, 0, 50.0, 100.0),      # every pair divided by s (position interpolation)
     (1, 900, 8, 2, 128, 100, 30, -2.0, -1.0),      # every pair kept: plain attention
+    (1, 300, 16, 2, 128, 100, 400, 1.0, 32.0),     # w0 >= L: every pair local, s = 3
 ]
 
 
@@ -108,6 +109,8 @@ DCASES = [  # (B, L, Lmax, Hq, Hkv, D, w_pre, w0, alpha, beta)
     (1, 20000, 20050, 32, 8, 128, 4096, 1000, 1.0, 32.0),   # many splits, s = 4.88
     (1, 600, 700, 8, 8, 128, 256, 0, 50.0, 100.0),
     (1, 131328, 131328, 32, 8, 128, 32768, 4096, 1.0, 32.0),  # the 128K cache, angles up to ~1e5 rad
+    (2, 300, 320, 16, 2, 128, 100, 400, 1.0, 32.0),          # w0 >= L: no remote key
+    (1, 65, 70, 4, 2, 64, 1, 3, 1.0, 32.0),                  # w_pretrained = 1: s = L
 ]
 
 
