@@ -329,7 +329,8 @@ typedef struct jl_rotated_keys {
  * w_pretrained tokens) the rotation covers every remote row (one pass over
  * the keys).  After a step with remote keys, state = {G, L-w0}.  `state` is
  * updated at enqueue time, so calls that share a cache must be ordered on
- * one stream.  The result equals jl_bifocal_decode's up to bf16 rounding
+ * one stream, and a call captured into a HIP graph does not stand for later
+ * steps (its rotation range was decided when it was enqueued).  The result equals jl_bifocal_decode's up to bf16 rounding
  * (the remote view of each key is rounded once, in the cache).  Everything
  * else as for jl_bifocal_decode.
  *
