@@ -156,3 +156,20 @@ def test_decode_fi_steps_and_s1():
     jl.jl_bifocal_decode(q, kc, vc, plain, None, 390, w0, w_pre, base, scale, jl.alloc_table(Lmax, D, base), ws)
     torch.cuda.synchronize()
     assert torch.equal(out, plain)
+
+
+def test_device_fi_table_equals_host_fi_table():
+    """The device fill and the host fill of the interpolation table agree:
+    header bit for bit, entries within one fp32 ulp (device and host float64
+    cos/sin may round differently)."""
+    require_gpu()
+    for (L, w_pre, D, base, alpha, beta) in [(1000, 300, 64, 1e4, 1.0, 32.0),
+                                             (131328, 32768, 128, 1e6, 1.0, 32.0)]:
+        t = jl.alloc_fi_table(L, w_pre, D, base, alpha, beta)
+        torch.cuda.synchronize()
+        dev = t.cpu().numpy()
+        host = jl.jl_fi_table_fill_host(L, w_pre, D, base, alpha, beta)
+        assert np.array_equal(dev[:64], host[:64])
+        a = dev[64:].view(np.float32).astype(np.float64)
+        b = host[64:].view(np.float32)
+        assert np.all(np.abs(a - b) <= np.spacing(np.abs(b)).astype(np.float64) + 1e-10)
