@@ -1,7 +1,18 @@
-"""GPU parity at the full workload sizes (the benchmark's launch
-configuration): every output row is computed by the GPU, and the oracle
-recomputes a sample of rows -- the structural rows at the window and
-schedule edges plus seeded uniform rows -- for every head."""
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.  The GPU computes every output row; the float64 oracle
+(Jet-Long §3 Eq. 1 over every causal key of a row) recomputes:
+
+  * the 32K identity workload: every query row of every head;
+  * the 64K and 128K extension workloads: the structural rows (window and
+    schedule edges, first and last rows, and the 64-row tile edges next to
+    each) plus 2048 seeded uniform rows, every head;
+  * the 128K-cache decode workload: all 256 steps, every head.
+
+bf16 outputs are held to max-abs 2e-2 (elements with |ref| >= 4 may add the
+half-ulp rounding of the exact value); fp32 outputs and log-sum-exps to
+2e-2."""
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -9,12 +20,15 @@ import torch
 import oracle
 import synth_inputs as si
 import zero_shot_rope_jl_amd as jl
-from gpu_common import TOL_BF16, assert_bf16_out_close, max_err, prefill, require_gpu, to_dev
+from gpu_common import (TOL_BF16, assert_bf16_out_close, max_err, oracle_decode_parallel, oracle_rows_parallel,
+                        prefill, require_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
 
+N_RANDOM_ROWS = 2048
 
-def f64_rows(bits, rows, L):
+
+def f64_rows(bits, rows):
     """Float64 copy of a [B, L, H, D] bf16 array holding only ``rows``."""
     out = np.zeros(bits.shape, dtype=np.float64)
     out[:, rows] = si.f32_from_bf16_bits(bits[:, rows])
@@ -23,37 +37,46 @@ def f64_rows(bits, rows, L):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["identity32k", "ext64k", "ext128k"])
-def test_fullsize_prefill_sampled_rows(name):
+def test_fullsize_prefill(name):
     require_gpu()
     w = si.WORKLOADS[name]
     print(f"[fullsize] {name}: generating inputs", flush=True)
     x = si.make_prefill_inputs(w, want_f64=False)
     q, k, v = (to_dev(x[n], w.dtype) for n in "qkv")
     table = jl.alloc_table(w.L, w.D, w.rope_base)
-    rows = si.sampled_rows(w.L, w.w0, w.w_pretrained, n_random=40, seed=w.seed)
+    if w.L <= w.w_pretrained:
+        rows = np.arange(w.L, dtype=np.int64)
+        what = "every row"
+    else:
+        rows = si.sampled_rows(w.L, w.w0, w.w_pretrained, n_random=N_RANDOM_ROWS, seed=w.seed)
+        what = f"{len(rows)} rows ({N_RANDOM_ROWS} seeded + structural)"
     got = {}
     for od in (torch.bfloat16, torch.float32):
         out, lse = prefill(q, k, v, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, od, table)
         assert torch.isfinite(out).all()
         got[od] = (out[:, rows].float().cpu().numpy(), lse[:, :, rows].cpu().numpy())
         del out, lse
-    print(f"[fullsize] {name}: oracle on {len(rows)} rows x {w.Hq} heads", flush=True)
-    q64 = f64_rows(x["q"], rows, w.L)
+    print(f"[fullsize] {name}: oracle on {what} x {w.Hq} heads", flush=True)
+    t0 = time.perf_counter()
+    q64 = f64_rows(x["q"], rows)
     k64 = si.f32_from_bf16_bits(x["k"]).astype(np.float64)
     v64 = si.f32_from_bf16_bits(x["v"]).astype(np.float64)
-    ref, ref_lse = oracle.bifocal_attention(q64, k64, v64, w.w0, w.w_pretrained, w.rope_base,
-                                            w.sm_scale, rows=rows)
+    ref, ref_lse = oracle_rows_parallel(q64, k64, v64, rows, w.w0, w.w_pretrained, w.rope_base, w.sm_scale)
     o32, l32 = got[torch.float32]
     o16, _ = got[torch.bfloat16]
-    e32, e16, el = max_err(o32, ref), max_err(o16, ref), max_err(l32, ref_lse)
-    print(f"[fullsize] {name}: fp32-out err {e32:.3e}, bf16-out err {e16:.3e}, lse err {el:.3e}", flush=True)
+    e32, el = max_err(o32, ref), max_err(l32, ref_lse)
+    e16, n_big = assert_bf16_out_close(o16, ref, label=name)
+    print(f"[fullsize] {name}: {len(rows)} rows x {w.Hq} heads compared ({time.perf_counter() - t0:.0f} s): "
+          f"fp32-out err {e32:.3e}, bf16-out err {e16:.3e} ({n_big} elements with |ref| >= 4), "
+          f"lse err {el:.3e}", flush=True)
     assert e32 <= TOL_BF16
     assert el <= TOL_BF16
-    assert_bf16_out_close(o16, ref)
     if w.L <= w.w_pretrained:
         # identity regime: the oracle's bifocal result is plain causal attention
-        plain, _ = oracle.plain_causal_attention(q64, k64, v64, w.sm_scale, rows=rows)
-        assert np.array_equal(plain, ref)
+        sub = rows[:: max(1, len(rows) // 512)]
+        plain, _ = oracle.plain_causal_attention(q64, k64, v64, w.sm_scale, rows=sub)
+        bif, _ = oracle.bifocal_attention(q64, k64, v64, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, rows=sub)
+        assert np.array_equal(plain, bif)
         # and the GPU output does not depend on w0 (here vs the pages' default 2048)
         a, _ = prefill(q, k, v, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, torch.bfloat16, table)
         b, _ = prefill(q, k, v, 2048, w.w_pretrained, w.rope_base, w.sm_scale, torch.bfloat16, table)
@@ -69,8 +92,7 @@ def test_fullsize_decode_256_steps():
     kc, vc = to_dev(kc_np, "bf16"), to_dev(vc_np, "bf16")
     table = jl.alloc_table(dw.Lmax, dw.D, dw.rope_base)
     ws = jl.alloc_decode_workspace(dw.B, dw.Hq, dw.D, dw.Lmax)
-    check = {1, 2, 128, 255, 256}
-    outs, lses, qs = {}, {}, {}
+    outs32, outs16, lses, qs = [], [], [], []
     for s in range(1, dw.steps + 1):
         qb, kb, vb = si.make_decode_step(dw, s)
         L = dw.prompt_len + s
@@ -78,22 +100,38 @@ def test_fullsize_decode_256_steps():
         vc[:, L - 1:L].copy_(to_dev(vb, "bf16"))
         kc_np[:, L - 1:L] = kb
         vc_np[:, L - 1:L] = vb
-        out = torch.empty((dw.B, 1, dw.Hq, dw.D), dtype=torch.float32, device="cuda")
+        qd = to_dev(qb, "bf16")
+        o32 = torch.empty((dw.B, 1, dw.Hq, dw.D), dtype=torch.float32, device="cuda")
+        o16 = torch.empty((dw.B, 1, dw.Hq, dw.D), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((dw.B, dw.Hq), dtype=torch.float32, device="cuda")
-        jl.jl_bifocal_decode(to_dev(qb, "bf16"), kc, vc, out, lse, L, dw.w0, dw.w_pretrained, dw.rope_base,
-                             dw.sm_scale, table, ws)
-        assert torch.isfinite(out).all() and torch.isfinite(lse).all(), s
-        if s in check:
-            outs[s], lses[s], qs[s] = out.cpu().numpy()[:, 0], lse.cpu().numpy(), qb
+        jl.jl_bifocal_decode(qd, kc, vc, o32, lse, L, dw.w0, dw.w_pretrained, dw.rope_base, dw.sm_scale, table, ws)
+        jl.jl_bifocal_decode(qd, kc, vc, o16, None, L, dw.w0, dw.w_pretrained, dw.rope_base, dw.sm_scale, table, ws)
+        outs32.append(o32)
+        outs16.append(o16)
+        lses.append(lse)
+        qs.append(qb)
     torch.cuda.synchronize()
+    o32 = torch.stack(outs32)[:, :, 0].cpu().numpy()           # [S, B, Hq, D]
+    o16 = torch.stack(outs16)[:, :, 0].float().cpu().numpy()
+    l32 = torch.stack(lses).cpu().numpy()                       # [S, B, Hq]
+    assert np.isfinite(o32).all() and np.isfinite(o16).all() and np.isfinite(l32).all()
+    print(f"[fullsize] decode128k: oracle on all {dw.steps} steps x {dw.Hq} heads", flush=True)
+    t0 = time.perf_counter()
     k64 = si.f32_from_bf16_bits(kc_np).astype(np.float64)
     v64 = si.f32_from_bf16_bits(vc_np).astype(np.float64)
-    for s in sorted(check):
+    del kc_np, vc_np
+    steps = []
+    for s in range(1, dw.steps + 1):
         L = dw.prompt_len + s
         assert oracle.group_size(L, dw.w_pretrained) == 5
-        q64 = si.f32_from_bf16_bits(qs[s]).astype(np.float64)[:, 0]
-        ref, ref_lse = oracle.decode_attention(q64, k64, v64, L, dw.w0, dw.w_pretrained, dw.rope_base,
-                                               dw.sm_scale)
-        e, el = max_err(outs[s], ref), max_err(lses[s], ref_lse)
-        print(f"[fullsize] decode step {s} (L={L}): err {e:.3e}, lse err {el:.3e}", flush=True)
-        assert e <= TOL_BF16 and el <= TOL_BF16
+        steps.append((si.f32_from_bf16_bits(qs[s - 1]).astype(np.float64)[:, 0], L))
+    res = oracle_decode_parallel(steps, k64, v64, dw.w0, dw.w_pretrained, dw.rope_base, dw.sm_scale)
+    ref = np.stack([r[0] for r in res])
+    ref_lse = np.stack([r[1] for r in res])
+    e32, el = max_err(o32, ref), max_err(l32, ref_lse)
+    per_step = np.abs(o32 - ref).reshape(dw.steps, -1).max(axis=1)
+    e16, n_big = assert_bf16_out_close(o16, ref, label="decode128k")
+    print(f"[fullsize] decode128k: {dw.steps} steps x {dw.Hq} heads compared ({time.perf_counter() - t0:.0f} s): "
+          f"fp32-out err {e32:.3e} (worst step {int(per_step.argmax()) + 1}), bf16-out err {e16:.3e}, "
+          f"lse err {el:.3e}", flush=True)
+    assert e32 <= TOL_BF16 and el <= TOL_BF16
