@@ -28,7 +28,7 @@ import time
 import numpy as np
 
 METRIC = "bifocal prefill TFLOP/s @128K (% MFMA peak); decode µs/step @128K (% HBM BW)"
-PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published (the device-derived peak rides beside it)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
@@ -258,13 +258,14 @@ def bench_reorder(torch, jl, w, x):
     return ms, gbs
 
 
-def bench_chunk(torch, jl, args, w, x, Lq=4096, page_size=256):
-    """The last Lq-token chunk of the workload over its cache, contiguous and
-    held in shuffled pages (jl_bifocal_prefill_chunk / _chunk_paged)."""
+CHUNK_LQ = (1, 16, 256, 4096)
+
+
+def bench_chunk(torch, jl, args, w, x, page_size=256):
+    """The last Lq tokens of the workload as one chunk over the cache of all L
+    keys (jl_bifocal_prefill_chunk), for several chunk lengths; the longest
+    also over the cache held in shuffled pages (jl_bifocal_prefill_chunk_paged)."""
     q, k, v = (to_dev(torch, x[n], w.dtype) for n in "qkv")
-    qc = q[:, w.L - Lq:].contiguous()
-    del q
-    out = torch.empty((w.B, Lq, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
     table = jl.alloc_table(w.L, w.D, w.rope_base)
     ws = jl.alloc_prefill_workspace(k, w.w_pretrained)
     max_pages = (w.L + page_size - 1) // page_size
@@ -278,24 +279,28 @@ def bench_chunk(torch, jl, args, w, x, Lq=4096, page_size=256):
     bt = torch.from_numpy(perm.reshape(w.B, max_pages).astype(np.int32)).cuda()
     stream = torch.cuda.current_stream()
     res = {}
-    for name, call in (("contiguous", lambda: jl.jl_bifocal_prefill_chunk(
-                            qc, k, v, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table,
-                            workspace=ws)),
-                       ("paged_256", lambda: jl.jl_bifocal_prefill_chunk_paged(
-                            qc, kp, vp, bt, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table,
-                            workspace=ws))):
-        call()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(args.chunk_steps):
+    for Lq in CHUNK_LQ:
+        qc = q[:, w.L - Lq:].contiguous()
+        out = torch.empty((w.B, Lq, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+        calls = [(f"lq{Lq}_ms", lambda: jl.jl_bifocal_prefill_chunk(
+            qc, k, v, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table, workspace=ws))]
+        if Lq == CHUNK_LQ[-1]:
+            calls.append((f"lq{Lq}_paged_256_ms", lambda: jl.jl_bifocal_prefill_chunk_paged(
+                qc, kp, vp, bt, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table,
+                workspace=ws)))
+        for name, call in calls:
             call()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        res[name + "_ms"] = round(ev0.elapsed_time(ev1) / args.chunk_steps, 4)
-    log(f"[bench] last {Lq}-token chunk: {res['contiguous_ms']:.3f} ms contiguous, "
-        f"{res['paged_256_ms']:.3f} ms over 256-key pages")
-    del k, v, qc, out, kp, vp, ws
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(args.chunk_steps):
+                call()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = round(ev0.elapsed_time(ev1) / args.chunk_steps, 4)
+        del qc, out
+    log("[bench] chunks over the 128K cache: " + ", ".join(f"{k} {v:.3f}" for k, v in res.items()))
+    del q, k, v, kp, vp, ws
     torch.cuda.empty_cache()
     return res
 
@@ -346,6 +351,44 @@ def bench_decode(torch, jl, si, args):
         evs[s + 1].record(stream)
     torch.cuda.synchronize()
     us_median = float(np.median([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(dw.steps)]))
+
+    # the matched control: the same kernel and steps with w_pretrained = Lmax,
+    # so G = 1 and every key is read in its stored view
+    def control_pass():
+        for s in range(dw.steps):
+            L = dw.prompt_len + s + 1
+            jl.jl_bifocal_decode(qs[s], kc, vc, out, None, L, dw.w0, dw.Lmax, dw.rope_base, dw.sm_scale, table, ws)
+
+    control_pass()
+    ev0.record(stream)
+    for _ in range(args.decode_passes):
+        control_pass()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_control = ev0.elapsed_time(ev1) * 1e3 / (args.decode_passes * dw.steps)
+
+    # the unfused step: three decode passes (window in the stored view, every
+    # key in the corrected view, window in the corrected view) and the §3.3
+    # Eq. 6 merge
+    uws = jl.alloc_decode_unfused_workspace(dw.B, dw.Hq, dw.D, dw.Lmax)
+    uout = torch.empty_like(out)
+
+    def unfused_pass():
+        for s in range(dw.steps):
+            L = dw.prompt_len + s + 1
+            jl.jl_bifocal_decode_unfused(qs[s], kc, vc, uout, None, L, dw.w0, dw.w_pretrained, dw.rope_base,
+                                         dw.sm_scale, table, uws)
+
+    unfused_pass()
+    ev0.record(stream)
+    unfused_pass()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_unfused = ev0.elapsed_time(ev1) * 1e3 / dw.steps
+    one_pass()
+    torch.cuda.synchronize()
+    unfused_ok = bool((uout.float() - out.float()).abs().max().item() <= 2e-2)
+    del uws, uout
 
     # the same steps over the cache held in shuffled 256-key pages
     ps = 256
@@ -429,6 +472,8 @@ def bench_decode(torch, jl, si, args):
     mean_L = dw.prompt_len + (dw.steps + 1) / 2.0
     bytes_step = 2.0 * dw.B * mean_L * dw.Hkv * dw.D * 2
     gbs = bytes_step / (us * 1e-6) / 1e9
+    log(f"[bench] decode matched control (G=1) {us_control:.2f} us/step, unfused (three passes + merge) "
+        f"{us_unfused:.2f} us/step{'' if unfused_ok else ' MISMATCH'}")
     log(f"[bench] decode {us:.2f} us/step (per-step median {us_median:.2f}, paged cache {us_paged:.2f}, "
         f"graph {us_graph:.2f}{'' if graph_ok else ' MISMATCH'}, rotated-key cache {us_rkc:.2f}, "
         f"frequency interpolation {us_fi:.2f}"
@@ -440,18 +485,49 @@ def bench_decode(torch, jl, si, args):
                                                "graph_matches_eager": graph_ok,
                                                "us_per_step_rotated_keys": round(us_rkc, 3),
                                                "us_per_step_frequency_interpolation": round(us_fi, 3),
-                                               "rotated_keys_match": rkc_ok}
+                                               "rotated_keys_match": rkc_ok,
+                                               "matched_control": {
+                                                   "what": "same kernel and steps with w_pretrained = Lmax "
+                                                           "(G = 1, every key in its stored view)",
+                                                   "us_per_step": round(us_control, 3),
+                                                   "bifocal_over_control": round(us_control / us, 4)},
+                                               "unfused": {
+                                                   "what": "three decode passes (stored view over the window, "
+                                                           "corrected view over all keys and over the window) and "
+                                                           "their inclusion-exclusion merge",
+                                                   "us_per_step": round(us_unfused, 3),
+                                                   "fused_speedup": round(us_unfused / us, 4),
+                                                   "matches_fused": unfused_ok}}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads():
+    """BLAS threads for the oracle: every core this process may run on."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        return n, threadpool_limits(limits=n)
+    except ImportError:  # pragma: no cover
+        import contextlib
+        return n, contextlib.nullcontext()
 
 
 def cpu_baseline(si, w, x, n_rows):
     """The float64 oracle on a bounded sample of the same workload: all 32
-    heads at n_rows seeded uniform query rows (all keys of each row)."""
+    heads at n_rows seeded uniform query rows (all keys of each row), with
+    the time for all L rows extrapolated by algorithmic FLOPs."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    cores, limit = oracle_threads()
     f64 = (lambda a: si.f32_from_bf16_bits(a).astype(np.float64)) if w.dtype == "bf16" else \
         (lambda a: a.astype(np.float64))
     rng = np.random.Generator(np.random.PCG64([w.seed, 99]))
@@ -459,13 +535,17 @@ def cpu_baseline(si, w, x, n_rows):
     q64 = np.zeros((w.B, w.L, w.Hq, w.D))
     q64[:, rows] = f64(x["q"][:, rows])
     k64, v64 = f64(x["k"]), f64(x["v"])
-    t0 = time.perf_counter()
-    oracle.bifocal_attention(q64, k64, v64, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, rows=rows)
-    sec = time.perf_counter() - t0
+    with limit:
+        t0 = time.perf_counter()
+        oracle.bifocal_attention(q64, k64, v64, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, rows=rows)
+        sec = time.perf_counter() - t0
     flops = float(sum(4.0 * w.B * w.Hq * w.D * (r + 1) for r in rows))
     return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(), "rows_sampled": int(n_rows), "rows_total": int(w.L),
+            "sample_s": round(sec, 2), "extrapolated_full_s": round(sec * prefill_flops(w) / flops, 1),
             "sample": f"{w.name}: {n_rows} seeded uniform query rows x all {w.Hq} heads over their causal keys "
-                      f"(float64 NumPy oracle incl. the remote view of all {w.L} keys), {sec:.1f} s"}
+                      f"(float64 NumPy oracle incl. the remote view of all {w.L} keys), {sec:.1f} s; the full "
+                      f"{w.L}-row call extrapolated by algorithmic FLOPs"}
 
 
 def cpu_baseline_decode(si, n_steps=2):
@@ -473,23 +553,27 @@ def cpu_baseline_decode(si, n_steps=2):
     workload (one query token over every cached key per step)."""
     import oracle
     dw = si.DECODE_WORKLOAD
+    cores, limit = oracle_threads()
     kc_np, vc_np = si.make_decode_prompt(dw)
     kc = si.f32_from_bf16_bits(kc_np).astype(np.float64)
     vc = si.f32_from_bf16_bits(vc_np).astype(np.float64)
     del kc_np, vc_np
     sec = 0.0
-    for s in range(1, n_steps + 1):
-        q, kn, vn = si.make_decode_step(dw, s)
-        row = dw.prompt_len + s - 1
-        kc[:, row] = si.f32_from_bf16_bits(kn[:, 0])
-        vc[:, row] = si.f32_from_bf16_bits(vn[:, 0])
-        q64 = si.f32_from_bf16_bits(q[:, 0]).astype(np.float64)
-        t0 = time.perf_counter()
-        oracle.decode_attention(q64, kc, vc, row + 1, dw.w0, dw.w_pretrained, dw.rope_base, dw.sm_scale)
-        sec += time.perf_counter() - t0
-    return {"value": sec / n_steps * 1e6, "unit": "µs/step", "kind": "oracle",
+    with limit:
+        for s in range(1, n_steps + 1):
+            q, kn, vn = si.make_decode_step(dw, s)
+            row = dw.prompt_len + s - 1
+            kc[:, row] = si.f32_from_bf16_bits(kn[:, 0])
+            vc[:, row] = si.f32_from_bf16_bits(vn[:, 0])
+            q64 = si.f32_from_bf16_bits(q[:, 0]).astype(np.float64)
+            t0 = time.perf_counter()
+            oracle.decode_attention(q64, kc, vc, row + 1, dw.w0, dw.w_pretrained, dw.rope_base, dw.sm_scale)
+            sec += time.perf_counter() - t0
+    return {"value": sec / n_steps * 1e6, "unit": "µs/step", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(), "steps_sampled": n_steps, "steps_total": dw.steps,
+            "extrapolated_full_s": round(sec / n_steps * dw.steps, 1),
             "sample": f"{dw.name}: the first {n_steps} of its {dw.steps} steps (float64 NumPy oracle, every "
-                      f"cached key incl. its remote view), {sec:.1f} s"}
+                      f"cached key incl. its remote view), {sec:.1f} s; all {dw.steps} steps extrapolated"}
 
 
 def main():
@@ -512,6 +596,9 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {n} bytes done")
         del src, dst
+    n_cu, clk_khz = jl.jl_device_info(torch.cuda.current_device())
+    peak_dev = n_cu * clk_khz * 1e3 * 4096 / 1e12
+    log(f"[bench] device: {n_cu} CUs at {clk_khz / 1e6:.2f} GHz peak clock -> {peak_dev:.1f} TFLOP/s dense bf16")
     w = si.WORKLOADS["ext128k"]
     log(f"[bench] generating {w.name} inputs")
     x = si.make_prefill_inputs(w, want_f64=False)
@@ -528,7 +615,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": pick(traffic, PREFILL_KERNEL),
-                     "flops_per_launch": flops},
+                     "flops_per_launch": flops,
+                     "peak_device": round(peak_dev, 1), "frac_device": round(tflops / peak_dev, 4),
+                     "peak_device_from": f"{n_cu} CUs x {clk_khz / 1e6:.2f} GHz x 4096 bf16 FLOP/clock/CU"},
         "prefill_ms_per_call": pstats,
     }
     if args.control_steps > 0:
@@ -555,7 +644,8 @@ def main():
         result["interleaved_reorder"] = {"what": "channel reorder of q and k for interleaved RoPE pairs",
                                          "ms_per_call": round(rms, 4), "gb_per_s": round(rgbs, 1)}
     if args.chunk_steps > 0:
-        result["chunk"] = {"what": "last 4096 tokens of the workload as one chunk over the other 126976 keys",
+        result["chunk"] = {"what": "the last Lq tokens of the workload as one chunk over all 131072 keys "
+                                   f"(Lq = {', '.join(map(str, CHUNK_LQ))}); the longest also over 256-key pages",
                            **bench_chunk(torch, jl, args, w, x)}
     if not args.skip_decode:
         dw, us, gbs, bytes_step, us_median, extra = bench_decode(torch, jl, si, args)

@@ -66,6 +66,14 @@ JL_API const char* jl_last_error(void);
 JL_API int jl_version(void);
 
 /*
+ * jl_device_info -- compute units and peak shader clock (kHz) of HIP device
+ * `device`, as the runtime reports them (for rooflines: the dense bf16
+ * MFMA peak of a CDNA4 device is n_cu * 4096 FLOP per clock).  Makes HIP
+ * calls.  Errors: NULL outputs -> JL_EINVAL, a runtime error -> JL_EHIP.
+ */
+JL_API int jl_device_info(int device, int* n_cu, int* max_clock_khz);
+
+/*
  * jl_schedule -- §3.1 Eq. (2) and the correction-angle table for §3.2 Eq. (5).
  *
  *   *G_out = max(1, ceil(L / w_pretrained)).
@@ -245,7 +253,11 @@ JL_API int jl_bifocal_prefill_chunk_paged(const void* q, const void* k_pages, co
 
 /*
  * jl_bifocal_decode_workspace -- bytes of fp32 scratch that jl_bifocal_decode
- * needs for a step that attends L keys (split-KV partials).  Pure host call.
+ * (and its paged, rotated-key and interpolation forms) needs for steps that
+ * attend up to L keys: the split-KV partials (acc[D], max, sum) of every
+ * query head, B * Hq * min(ceil(L/32), 256) * (D + 2) floats.  Pure host call.
+ * Calls that share a workspace must not overlap in time (keep them on one
+ * stream).
  */
 JL_API int jl_bifocal_decode_workspace(int64_t B, int64_t Hq, int64_t D, int64_t L, size_t* bytes);
 
@@ -271,6 +283,34 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
                       int64_t w_pretrained, double rope_base, float sm_scale,
                       const void* table, size_t table_bytes, void* workspace,
                       size_t workspace_bytes, void* hip_stream);
+
+/*
+ * jl_bifocal_decode_unfused_workspace -- bytes of scratch for
+ * jl_bifocal_decode_unfused: the decode partials above (rounded up to 256
+ * bytes), then three fp32 pass outputs [B, Hq, D] and three log-sum-exps
+ * [B, Hq], each rounded up to 256 bytes.  Pure host call.
+ */
+JL_API int jl_bifocal_decode_unfused_workspace(int64_t B, int64_t Hq, int64_t D, int64_t L, size_t* bytes);
+
+/*
+ * jl_bifocal_decode_unfused -- the same step as jl_bifocal_decode (same
+ * arguments and result up to rounding), computed as §3.3 Eq. (6) writes it:
+ * three separate attention passes over the cache, each a full decode launch,
+ *   A: stored view, keys with (L-1) - k <= w0,
+ *   B: remote view, every key k <= L-1,
+ *   C: remote view, keys with (L-1) - k <= w0,
+ * then O = (W_A O_A + W_B O_B - W_C O_C) / (W_A + W_B - W_C) with W_X the
+ * passes' softmax denominators.  It is the unfused baseline that the fused
+ * step is measured against (§4.8, Tab. 7).  `workspace` must hold
+ * jl_bifocal_decode_unfused_workspace(B, Hq, D, L) bytes.  Errors as for
+ * jl_bifocal_decode.
+ */
+JL_API int jl_bifocal_decode_unfused(const void* q, const void* k_cache, const void* v_cache, void* out,
+                                     float* lse, int in_dtype, int out_dtype, int64_t B, int64_t L,
+                                     int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                                     int64_t w_pretrained, double rope_base, float sm_scale,
+                                     const void* table, size_t table_bytes, void* workspace,
+                                     size_t workspace_bytes, void* hip_stream);
 
 /*
  * jl_bifocal_decode_paged -- jl_bifocal_decode over a paged cache (a block

@@ -29,10 +29,11 @@ def test_exports_every_declared_symbol():
                            "jl_bifocal_prefill_unfused_workspace", "jl_bifocal_prefill_unfused",
                            "jl_bifocal_prefill_chunk_paged", "jl_bifocal_decode_rkc", "jl_fi_table",
                            "jl_fi_table_fill_host", "jl_bifocal_prefill_fi", "jl_bifocal_decode_fi",
-                           "jl_rope_interleaved_to_half"])
+                           "jl_rope_interleaved_to_half", "jl_bifocal_decode_unfused_workspace",
+                           "jl_bifocal_decode_unfused", "jl_device_info"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 8
+    assert jl.jl_version() == 9
 
 
 def test_schedule_golden_and_table_size():
@@ -260,12 +261,52 @@ def test_decode_paged_validation(over, code):
     assert jl.jl_last_error()
 
 
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+def _dec_ws(B, Hq, D, splits):
+    """Split partials [B, Hq, splits, D + 2] fp32."""
+    return B * Hq * splits * (D + 2) * 4
+
+
 def test_decode_workspace_size():
-    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 131328) == 32 * 256 * 130 * 4
-    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 1000) == 32 * 32 * 130 * 4
-    assert jl.jl_bifocal_decode_workspace(2, 4, 64, 1) == 2 * 4 * 1 * 66 * 4
+    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 131328) == _dec_ws(1, 32, 128, 256)
+    assert jl.jl_bifocal_decode_workspace(1, 32, 128, 1000) == _dec_ws(1, 32, 128, 32)
+    assert jl.jl_bifocal_decode_workspace(2, 4, 64, 1) == _dec_ws(2, 4, 64, 1)
     with pytest.raises(jl.JetLongError):
         jl.jl_bifocal_decode_workspace(1, 4, 96, 10)
+
+
+def test_decode_unfused_workspace_size():
+    base = _up(_dec_ws(1, 32, 128, 256))
+    assert jl.jl_bifocal_decode_unfused_workspace(1, 32, 128, 131328) == \
+        base + 3 * _up(32 * 128 * 4) + 3 * _up(32 * 4)
+    with pytest.raises(jl.JetLongError):
+        jl.jl_bifocal_decode_unfused_workspace(0, 4, 128, 10)
+
+
+def _unfused_dec(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, i=jl.JL_BF16, o=jl.JL_BF16, B=1, L=600, Lmax=700,
+             Hq=8, Hkv=2, D=128, w0=16, wp=64, base=1e4, sc=0.125, table=FAKE, tb=1 << 30, ws=FAKE,
+             wsb=1 << 30)
+    a.update(over)
+    return jl.lib.jl_bifocal_decode_unfused(a["q"], a["k"], a["v"], a["out"], a["lse"], a["i"], a["o"], a["B"],
+                                            a["L"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"],
+                                            a["base"], a["sc"], a["table"], a["tb"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ws=None), jl.JL_EINVAL), (dict(Lmax=599), jl.JL_EINVAL), (dict(i=jl.JL_F32, o=jl.JL_F32),
+                                                                    jl.JL_EUNSUPPORTED),
+    (dict(wsb=jl.jl_bifocal_decode_workspace(1, 8, 128, 600)), jl.JL_ESPACE), (dict(tb=64), jl.JL_ESPACE),
+    (dict(w0=-1), jl.JL_EINVAL), (dict(table=None), jl.JL_EINVAL),
+])
+def test_decode_unfused_validation(over, code):
+    """The unfused step needs room for the fused step's workspace and its
+    three pass results; anything less is refused before any HIP call."""
+    assert _unfused_dec(**over) == code
+    assert jl.jl_last_error()
 
 
 @pytest.mark.parametrize("D,base,L", [(64, 1e4, 512), (128, 1e6, 131328), (128, 5e5, 1)])
@@ -389,3 +430,35 @@ def test_decode_fi_validation(over, code):
 ])
 def test_interleaved_to_half_validation(args, code):
     assert jl.lib.jl_rope_interleaved_to_half(*args, None) == code
+
+
+def test_call_scratch_is_allocated_on_the_call_stream(monkeypatch):
+    """A wrapper that allocates its own workspace does so on the stream its
+    kernels run on, so the caching allocator cannot reuse the block for work
+    on another stream while those kernels still use it."""
+    import types
+    from zero_shot_rope_jl_amd import binding
+    log = []
+
+    class Ctx:
+        def __init__(self, s):
+            self.s = s
+
+        def __enter__(self):
+            log.append(("enter", self.s))
+
+        def __exit__(self, *a):
+            log.append(("exit", self.s))
+
+    fake = types.SimpleNamespace(
+        uint8="u8",
+        empty=lambda n, dtype, device: log.append(("alloc", n)) or ("buf", n),
+        cuda=types.SimpleNamespace(ExternalStream=lambda ptr, device=None: ("ext", ptr),
+                                   stream=lambda s: Ctx(s)))
+    monkeypatch.setattr(binding, "_torch", lambda: fake)
+    assert binding._scratch(64, "cuda:0", 0x1234) == ("buf", 64)
+    assert log == [("enter", ("ext", 0x1234)), ("alloc", 64), ("exit", ("ext", 0x1234))]
+    log.clear()
+    binding._scratch(32, "cuda:0", None)   # torch's current stream: the call runs there too
+    assert log == [("alloc", 32)]
+

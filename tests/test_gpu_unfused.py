@@ -78,3 +78,55 @@ def test_unfused_agrees_with_fused():
     print("unfused vs fused", d, dl)
     # each side is within 2e-2 of the exact result; in practice they agree far closer
     assert d <= TOL_BF16 and dl <= TOL_BF16
+
+
+# ---- the unfused decode step: three decode launches (A, B, C) and the merge
+DEC_CASES = [  # (B, L, Lmax, Hq, Hkv, D, w_pre, w0)
+    (1, 1500, 1600, 8, 2, 128, 400, 100),      # G = 4, window inside the cache
+    (2, 777, 800, 4, 4, 64, 256, 33),          # G = 4, D = 64, no GQA, B = 2
+    (1, 20000, 20000, 32, 8, 128, 4096, 1000), # many splits in every pass (two merge levels in B)
+    (1, 600, 700, 8, 2, 128, 256, 0),          # w0 = 0: the window is the newest key
+    (1, 400, 400, 8, 2, 128, 1000, 50),        # G = 1: the views coincide
+    (1, 300, 310, 8, 2, 128, 100, 400),        # w0 >= L: the window holds every key
+]
+
+
+@pytest.mark.parametrize("case", DEC_CASES, ids=[f"B{c[0]}_L{c[1]}_H{c[3]}x{c[4]}_D{c[5]}_wp{c[6]}_w0{c[7]}"
+                                                  for c in DEC_CASES])
+def test_unfused_decode_matches_oracle(case):
+    require_gpu()
+    B, L, Lmax, Hq, Hkv, D, w_pre, w0 = case
+    base, scale = 1e4, D ** -0.5
+    rng = np.random.default_rng(L + 31 * Hq)
+    bits = lambda shape: si.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32))
+    qb, kb, vb = bits((B, 1, Hq, D)), bits((B, Lmax, Hkv, D)), bits((B, Lmax, Hkv, D))
+    q, kc, vc = to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16")
+    table = jl.alloc_table(Lmax, D, base)
+    ws = jl.alloc_decode_unfused_workspace(B, Hq, D, Lmax)
+    fws = jl.alloc_decode_workspace(B, Hq, D, Lmax)
+    f64 = lambda a: si.f32_from_bf16_bits(a).astype(np.float64)
+    q64, k64, v64 = f64(qb)[:, 0], f64(kb), f64(vb)
+    ref, ref_lse = oracle.decode_attention(q64, k64, v64, L, w0, w_pre, base, scale)
+    # the oracle's literal three-softmax merge for the same row (query at L-1)
+    qfull = np.zeros((B, L, Hq, D))
+    qfull[:, L - 1] = q64
+    ie = oracle.inclusion_exclusion_attention(qfull, k64[:, :L], v64[:, :L], w0, w_pre, base, scale,
+                                              rows=np.array([L - 1]))[:, 0]
+    outs = {}
+    for od in (torch.float32, torch.bfloat16):
+        out = torch.empty((B, 1, Hq, D), dtype=od, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        jl.jl_bifocal_decode_unfused(q, kc, vc, out, lse, L, w0, w_pre, base, scale, table, ws)
+        torch.cuda.synchronize()
+        outs[od] = (out.float().cpu().numpy()[:, 0], lse.cpu().numpy())
+    fused = torch.empty((B, 1, Hq, D), dtype=torch.float32, device="cuda")
+    jl.jl_bifocal_decode(q, kc, vc, fused, None, L, w0, w_pre, base, scale, table, fws)
+    torch.cuda.synchronize()
+    o32, l32 = outs[torch.float32]
+    print(case, "G", oracle.group_size(L, w_pre), "unfused decode err", max_err(o32, ref), "vs IE",
+          max_err(o32, ie), "lse", max_err(l32, ref_lse), "vs fused", max_err(o32, fused.cpu().numpy()[:, 0]))
+    assert np.all(np.isfinite(o32))
+    assert max_err(o32, ref) <= TOL_BF16 and max_err(o32, ie) <= TOL_BF16
+    assert max_err(l32, ref_lse) <= TOL_BF16
+    assert_bf16_out_close(outs[torch.bfloat16][0], ref, label=f"unfused decode {case}")
+    assert max_err(o32, fused.cpu().numpy()[:, 0]) <= TOL_BF16

@@ -41,6 +41,8 @@ def _load():
     L.jl_last_error.restype = cp
     L.jl_last_error.argtypes = []
     L.jl_version.restype = ctypes.c_int
+    L.jl_device_info.restype = ctypes.c_int
+    L.jl_device_info.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     L.jl_schedule.restype = ctypes.c_int
     L.jl_schedule.argtypes = [i64, i64, i64, ctypes.c_double, ctypes.POINTER(i64), vp, sz,
                               ctypes.POINTER(sz), vp]
@@ -70,6 +72,11 @@ def _load():
     L.jl_bifocal_decode.restype = ctypes.c_int
     L.jl_bifocal_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                     i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
+    L.jl_bifocal_decode_unfused_workspace.restype = ctypes.c_int
+    L.jl_bifocal_decode_unfused_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(sz)]
+    L.jl_bifocal_decode_unfused.restype = ctypes.c_int
+    L.jl_bifocal_decode_unfused.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                            i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
     L.jl_bifocal_decode_rkc.restype = ctypes.c_int
     L.jl_bifocal_decode_rkc.argtypes = [vp, vp, vp, vp, ctypes.POINTER(JLRotatedKeys), vp, vp, ctypes.c_int,
                                         ctypes.c_int, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
@@ -105,6 +112,13 @@ def jl_version() -> int:
     return lib.jl_version()
 
 
+def jl_device_info(device: int = 0):
+    """(compute units, peak shader clock in kHz) of a HIP device."""
+    n, c = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib.jl_device_info(device, ctypes.byref(n), ctypes.byref(c)))
+    return n.value, c.value
+
+
 def _check(rc: int) -> None:
     if rc != JL_OK:
         raise JetLongError(rc, jl_last_error())
@@ -134,6 +148,20 @@ def _stream(stream):
         return ctypes.c_void_p(stream)
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _scratch(nbytes: int, device, stream):
+    """Device scratch for one call that allocates it itself.  The caching
+    allocator may hand a freed block to the next allocation on the stream it
+    was allocated on, so the block is allocated on the stream the call's
+    kernels run on: then any reuse is ordered after those kernels.  (Allocated
+    on torch's current stream while the kernels run on another, it could be
+    reused while they still read or write it.)"""
+    torch = _torch()
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device)):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def _need_device(*ts):
@@ -206,7 +234,7 @@ def jl_bifocal_prefill(q, k, v, out, lse, w0: int, w_pretrained: int, rope_base:
 
     `workspace`: device scratch of jl_bifocal_prefill_workspace bytes (see
     alloc_prefill_workspace); when None and some is needed, one is allocated
-    through torch for this call.
+    through torch for this call, on the stream the call runs on.
     """
     _need_device(q, k, v, out, lse, table, workspace)
     B, L, Hq, D = q.shape
@@ -220,7 +248,8 @@ def jl_bifocal_prefill(q, k, v, out, lse, w0: int, w_pretrained: int, rope_base:
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
     if workspace is None:
-        workspace = alloc_prefill_workspace(k, w_pretrained, device=q.device)
+        n = jl_bifocal_prefill_workspace(_dtype_code(k), B, L, Hkv, D, w_pretrained)
+        workspace = _scratch(n, q.device, stream) if n else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.jl_bifocal_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
                                   _dtype_code(out), B, L, Hq, Hkv, D, w0, w_pretrained, rope_base,
@@ -260,7 +289,8 @@ def jl_bifocal_prefill_unfused(q, k, v, out, lse, w0: int, w_pretrained: int, ro
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share a dtype")
     if workspace is None:
-        workspace = alloc_prefill_unfused_workspace(q, k, w_pretrained, device=q.device)
+        workspace = _scratch(jl_bifocal_prefill_unfused_workspace(_dtype_code(q), B, L, Hq, Hkv, D, w_pretrained),
+                             q.device, stream)
     _check(lib.jl_bifocal_prefill_unfused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
                                           _dtype_code(out), B, L, Hq, Hkv, D, w0, w_pretrained, rope_base,
                                           sm_scale, _ptr(table), table.numel() * table.element_size(),
@@ -287,7 +317,7 @@ def jl_bifocal_prefill_chunk(q, k_cache, v_cache, out, lse, L: int, w0: int, w_p
         raise TypeError("q and the caches must share a dtype")
     if workspace is None:
         n = jl_bifocal_prefill_workspace(_dtype_code(q), B, L, Hkv, D, w_pretrained)
-        workspace = _torch().empty(n, dtype=_torch().uint8, device=q.device) if n else None
+        workspace = _scratch(n, q.device, stream) if n else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.jl_bifocal_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
                                         _dtype_code(q), _dtype_code(out), B, Lq, L, Lmax, Hq, Hkv, D, w0,
@@ -316,7 +346,7 @@ def jl_bifocal_prefill_chunk_paged(q, k_pages, v_pages, block_table, out, lse, L
         raise ValueError("lse must be float32 [B, Hq, Lq]")
     if workspace is None:
         n = jl_bifocal_prefill_workspace(_dtype_code(q), B, L, Hkv, D, w_pretrained)
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+        workspace = _scratch(n, q.device, stream) if n else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.jl_bifocal_prefill_chunk_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(out),
                                               _ptr(lse), _dtype_code(q), _dtype_code(out), B, Lq, L, n_pages,
@@ -333,8 +363,22 @@ def jl_bifocal_decode_workspace(B: int, Hq: int, D: int, L: int) -> int:
 
 
 def alloc_decode_workspace(B: int, Hq: int, D: int, Lmax: int, device="cuda"):
+    """Decode workspace (split partials) for steps of up to Lmax keys."""
     torch = _torch()
     n = jl_bifocal_decode_workspace(B, Hq, D, Lmax)
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def jl_bifocal_decode_unfused_workspace(B: int, Hq: int, D: int, L: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.jl_bifocal_decode_unfused_workspace(B, Hq, D, L, ctypes.byref(n)))
+    return n.value
+
+
+def alloc_decode_unfused_workspace(B: int, Hq: int, D: int, Lmax: int, device="cuda"):
+    """Workspace of jl_bifocal_decode_unfused for steps of up to Lmax keys."""
+    torch = _torch()
+    n = jl_bifocal_decode_unfused_workspace(B, Hq, D, Lmax)
     return torch.empty(n // 4, dtype=torch.float32, device=device)
 
 
@@ -355,6 +399,27 @@ def jl_bifocal_decode(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrain
                                  w_pretrained, rope_base, sm_scale, _ptr(table),
                                  table.numel() * table.element_size(), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def jl_bifocal_decode_unfused(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrained: int,
+                              rope_base: float, sm_scale: float, table, workspace, stream=None):
+    """jl_bifocal_decode computed as three passes and their §3.3 Eq. 6 merge;
+    `workspace` from alloc_decode_unfused_workspace."""
+    _need_device(q, k_cache, v_cache, out, lse, table, workspace)
+    B, one, Hq, D = q.shape
+    _, Lmax, Hkv, Dk = k_cache.shape
+    if one != 1 or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B:
+        raise ValueError("q must be [B,1,Hq,D] and the caches [B,Lmax,Hkv,D]")
+    if tuple(out.shape) != (B, 1, Hq, D):
+        raise ValueError("out must be [B, 1, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq]")
+    _check(lib.jl_bifocal_decode_unfused(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                         _dtype_code(q), _dtype_code(out), B, L, Lmax, Hq, Hkv, D, w0,
+                                         w_pretrained, rope_base, sm_scale, _ptr(table),
+                                         table.numel() * table.element_size(), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 
@@ -472,7 +537,8 @@ def jl_bifocal_prefill_fi(q, k, v, out, lse, w0: int, w_pretrained: int, rope_ba
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
     if workspace is None:
-        workspace = alloc_prefill_workspace(k, w_pretrained, device=q.device)
+        n = jl_bifocal_prefill_workspace(_dtype_code(k), B, L, Hkv, D, w_pretrained)
+        workspace = _scratch(n, q.device, stream) if n else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.jl_bifocal_prefill_fi(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
                                      _dtype_code(out), B, L, Hq, Hkv, D, w0, w_pretrained, rope_base, fi_alpha,

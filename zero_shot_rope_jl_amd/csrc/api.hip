@@ -86,7 +86,16 @@ extern "C" {
 
 JL_API const char* jl_last_error(void) { return g_err.c_str(); }
 
-JL_API int jl_version(void) { return 8; }
+JL_API int jl_device_info(int device, int* n_cu, int* max_clock_khz) {
+    g_err.clear();
+    if (!n_cu || !max_clock_khz) return fail(JL_EINVAL, "n_cu and max_clock_khz must be non-NULL");
+    hipError_t e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(max_clock_khz, hipDeviceAttributeClockRate, device);
+    if (e != hipSuccess) return fail(JL_EHIP, "device %d attributes: %s", device, hipGetErrorString(e));
+    return JL_OK;
+}
+
+JL_API int jl_version(void) { return 9; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -447,13 +456,53 @@ JL_API int jl_bifocal_decode_workspace(int64_t B, int64_t Hq, int64_t D, int64_t
     if (!bytes) return fail(JL_EINVAL, "bytes is NULL");
     if (B < 1 || Hq < 1 || L < 1 || L > kMaxLen) return fail(JL_EINVAL, "B, Hq, L must be >= 1 and L <= 2^30");
     if (D != 64 && D != 128) return fail(JL_EUNSUPPORTED, "head_dim %lld not supported", (long long)D);
-    *bytes = (size_t)B * (size_t)Hq * (size_t)jl::decode_max_splits(L) * (size_t)(D + 2) * sizeof(float);
+    *bytes = jl::decode_partial_bytes(B, Hq, D, L);
     return JL_OK;
 }
 
 }  // extern "C"
 
 namespace {
+
+// Workspace of the unfused decode step: the split partials of the fused
+// step (the passes run one after another and share them), then the three
+// passes' fp32 outputs [B, Hq, D] and log-sum-exps [B, Hq].
+struct UnfusedDecodeLayout {
+    size_t o[3], l[3], total;
+};
+
+UnfusedDecodeLayout unfused_decode_layout(int64_t B, int64_t Hq, int64_t D, int64_t L) {
+    UnfusedDecodeLayout u{};
+    size_t off = jl::decode_align(jl::decode_partial_bytes(B, Hq, D, L));
+    for (int i = 0; i < 3; ++i) {
+        u.o[i] = off;
+        off = jl::decode_align(off + (size_t)B * (size_t)Hq * (size_t)D * sizeof(float));
+    }
+    for (int i = 0; i < 3; ++i) {
+        u.l[i] = off;
+        off = jl::decode_align(off + (size_t)B * (size_t)Hq * sizeof(float));
+    }
+    u.total = off;
+    return u;
+}
+
+// The keys a decode launch reads and how it scores them (p.G and p.w0 set):
+// the fused step reads every key, the passes of the unfused step (§3.3
+// Eq. 6) read the window's keys in the stored view (A), every key in the
+// corrected view (B) or the window's keys in the corrected view (C).  With
+// G = 1 the corrected view is the stored one.  The split plan covers the
+// keys read.
+void set_decode_range(jl::DecodeParams& p, int64_t L, int mode) {
+    const int64_t kwin = L - 1 - p.w0 > 0 ? L - 1 - p.w0 : 0;   // first key of the window
+    const int64_t all_stored = 0, none_stored = p.G == 1 ? 0 : L;
+    switch (mode) {
+    case jl::kLocalWindow: p.k_lo = kwin; p.kloc = all_stored; break;
+    case jl::kRemoteAll: p.k_lo = 0; p.kloc = none_stored; break;
+    case jl::kRemoteWindow: p.k_lo = kwin; p.kloc = none_stored; break;
+    default: p.k_lo = 0; p.kloc = p.G == 1 ? 0 : kwin; break;
+    }
+    jl::decode_split_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk);
+}
 
 // Both decode entry points.  Contiguous cache: block_table == NULL, k/v
 // [B, Lmax, Hkv, D].  Paged cache: k/v [n_pages, page_size, Hkv, D] and
@@ -463,7 +512,7 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
                 int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
                 int64_t w_pretrained, double rope_base, float sm_scale, const void* table, size_t table_bytes,
                 void* workspace, size_t workspace_bytes, void* hip_stream, void* krot = nullptr,
-                jl_rotated_keys* rk_state = nullptr, const FiArgs* fi = nullptr) {
+                jl_rotated_keys* rk_state = nullptr, const FiArgs* fi = nullptr, bool unfused = false) {
     g_err.clear();
     if (!q || !k_cache || !v_cache || !out || (!table && !fi) || !workspace)
         return fail(JL_EINVAL, "%s: q, the caches, out, table and workspace must be non-NULL", who);
@@ -496,8 +545,8 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
         if (table_bytes < need)
             return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
     }
-    size_t ws_need = 0;
-    jl_bifocal_decode_workspace(B, Hq, D, L, &ws_need);
+    const UnfusedDecodeLayout ul = unfused_decode_layout(B, Hq, D, L);
+    const size_t ws_need = unfused ? ul.total : jl::decode_partial_bytes(B, Hq, D, L);
     if (workspace_bytes < ws_need)
         return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace_bytes, ws_need);
     if (Hkv > 65535) return fail(JL_EINVAL, "Hkv exceeds 65535");
@@ -516,7 +565,6 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     p.v = v_cache;
     p.out = out;
     p.lse = lse;
-    p.ws = static_cast<float*>(workspace);
     p.table = static_cast<const jl::TableHeader*>(table);
     p.TF = table ? reinterpret_cast<const float2*>(static_cast<const char*>(table) + jl::kTableHeaderBytes) : nullptr;
     p.table_key = jl::TableKey{jl::kTableMagic, 0, 0, 0.0, 0.0};
@@ -530,7 +578,6 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.R = (int)R;
-    jl::decode_split_plan(B, Hkv, L, &p.n_split, &p.wave_chunk);
     p.heads_per_wg = jl::decode_heads_per_wg(Hkv);
     p.w0 = w0 < L ? w0 : L;
     p.G = group_size(L, w_pretrained);
@@ -545,6 +592,8 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
         for (int i = 0; i < (int)D / 2; ++i)
             p.fi_phi[i] = jl::fi_phi(rope_base, (int)D, L, w_pretrained, fi->alpha, fi->beta, i);
     }
+    set_decode_range(p, L, jl::kFused);
+    p.ws = static_cast<float*>(workspace);
     (void)hipGetLastError();
     if (krot) {
         // bring the rotated-key cache up to date for this step: every key with
@@ -564,8 +613,40 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
             if (rk_state->rows < kloc + 1) rk_state->rows = kloc + 1;
         }
     }
-    hipError_t e = jl::launch_decode(p, out_dtype, static_cast<hipStream_t>(hip_stream));
-    if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
+    const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (!unfused) {
+        hipError_t e = jl::launch_decode(p, out_dtype, stream);
+        if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
+        return JL_OK;
+    }
+    // the unfused step: passes A, B and C one after the other (they share the
+    // split partials), each writing fp32 output and log-sum-exp, then
+    // the inclusion-exclusion merge (§3.3 Eq. 6)
+    char* w = static_cast<char*>(workspace);
+    const int modes[3] = {jl::kLocalWindow, jl::kRemoteAll, jl::kRemoteWindow};
+    for (int i = 0; i < 3; ++i) {
+        jl::DecodeParams pi = p;
+        set_decode_range(pi, L, modes[i]);
+        pi.out = w + ul.o[i];
+        pi.lse = reinterpret_cast<float*>(w + ul.l[i]);
+        hipError_t e = jl::launch_decode(pi, JL_F32, stream);
+        if (e != hipSuccess) return fail(JL_EHIP, "%s pass %d launch failed: %s", who, i, hipGetErrorString(e));
+    }
+    jl::MergeParams m{};
+    m.o_a = reinterpret_cast<const float*>(w + ul.o[0]);
+    m.o_b = reinterpret_cast<const float*>(w + ul.o[1]);
+    m.o_c = reinterpret_cast<const float*>(w + ul.o[2]);
+    m.lse_a = reinterpret_cast<const float*>(w + ul.l[0]);
+    m.lse_b = reinterpret_cast<const float*>(w + ul.l[1]);
+    m.lse_c = reinterpret_cast<const float*>(w + ul.l[2]);
+    m.out = out;
+    m.lse = lse;
+    m.B = B;
+    m.Lq = 1;
+    m.Hq = Hq;
+    m.D = D;
+    hipError_t e = jl::launch_ie_merge(m, out_dtype, stream);
+    if (e != hipSuccess) return fail(JL_EHIP, "%s merge launch failed: %s", who, hipGetErrorString(e));
     return JL_OK;
 }
 
@@ -581,6 +662,25 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
     return decode_impl("decode", q, k_cache, v_cache, nullptr, 0, 0, 0, out, lse, in_dtype, out_dtype, B, L, Lmax,
                        Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
                        workspace_bytes, hip_stream);
+}
+
+JL_API int jl_bifocal_decode_unfused_workspace(int64_t B, int64_t Hq, int64_t D, int64_t L, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(JL_EINVAL, "bytes is NULL");
+    if (B < 1 || Hq < 1 || L < 1 || L > kMaxLen) return fail(JL_EINVAL, "B, Hq, L must be >= 1 and L <= 2^30");
+    if (D != 64 && D != 128) return fail(JL_EUNSUPPORTED, "head_dim %lld not supported", (long long)D);
+    *bytes = unfused_decode_layout(B, Hq, D, L).total;
+    return JL_OK;
+}
+
+JL_API int jl_bifocal_decode_unfused(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                     int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq,
+                                     int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained, double rope_base,
+                                     float sm_scale, const void* table, size_t table_bytes, void* workspace,
+                                     size_t workspace_bytes, void* hip_stream) {
+    return decode_impl("decode_unfused", q, k_cache, v_cache, nullptr, 0, 0, 0, out, lse, in_dtype, out_dtype, B, L,
+                       Lmax, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
+                       workspace_bytes, hip_stream, nullptr, nullptr, nullptr, true);
 }
 
 JL_API int jl_bifocal_decode_rkc(const void* q, const void* k_cache, const void* v_cache, void* krot_cache,

@@ -29,6 +29,11 @@
 // combine kernel merges a head's partials with the log-sum-exp rule (§3.3
 // Eq. 6 with disjoint key sets).
 //
+// Pass modes (the unfused step): the same kernels read only the window's
+// keys in the stored view (pass A), every key in the corrected view (B), or
+// the window's keys in the corrected view (C); the merge kernel of the
+// unfused prefill then applies Eq. 6 to the three results.
+//
 // Variants of the split kernel (template flags): PAGED reads the cache
 // through a block table; RKC reads remote keys already rotated from a
 // second cache (and writes ahead the row the next step needs); FI uses the
@@ -149,8 +154,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const int R = p.R;
     const int G = (int)p.G;
     const int qpos = L - 1;
-    // keys >= kloc are local (q - k <= w0); G == 1 makes every key local
-    const int kloc = (G == 1) ? 0 : (int)max<int64_t>(0, (int64_t)qpos - p.w0);
+    // keys >= kloc score in the stored view (q - k <= w0 in the fused step;
+    // G == 1 makes every key local)
+    const int kloc = (int)p.kloc;
     const float scale2 = p.sm_scale_log2;
     const __bf16* __restrict__ kc = static_cast<const __bf16*>(p.k);
     // rotated-key cache (RKC): remote keys are read in their corrected view
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     // the first step's K and V go out before anything else (the set-up below
     // waits on the table and q); they stay within the cache whatever the
     // table check decides
-    const int wstart = (split * NW + sub) * p.wave_chunk;
+    const int wstart = (int)p.k_lo + (split * NW + sub) * p.wave_chunk;
     const int wend0 = min(L, wstart + p.wave_chunk);
     DecodeTile<D> cur;
     int64_t r_next = 0;   // cache row of the next step's first key

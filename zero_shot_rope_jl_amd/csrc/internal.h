@@ -65,7 +65,7 @@ struct DecodeParams {
     const void* v;
     void* out;
     float* lse;
-    float* ws;
+    float* ws;          // split partials (acc[D], max, sum) [B, Hq, n_split, D + 2]
     const TableHeader* table;
     const float2* TF;   // (cos, sin)(n theta_i) rows, n < coverage
     int64_t B, L, Lmax, Hq, Hkv;
@@ -80,6 +80,13 @@ struct DecodeParams {
     int heads_per_wg;   // KV heads per workgroup (waves per head = 8 / heads_per_wg)
     int64_t w0;
     int64_t G;
+    // keys k_lo .. L-1 are read; those >= kloc score in the stored view, the
+    // rest in the corrected view.  The fused step reads every key with
+    // kloc = L-1-w0 (0 when G = 1); the passes of the unfused step restrict
+    // the keys to the window and put kloc at its start (pass A) or at L
+    // (passes B and C: every key corrected).
+    int64_t k_lo;
+    int64_t kloc;
     float sm_scale_log2;
     double rope_base;
     int head_dim;
@@ -116,10 +123,16 @@ constexpr int kDecodeWaves = 8;
 constexpr int kDecodeMaxHeadsPerWG = 4;
 constexpr int kDecodeTargetWGs = 256;
 constexpr int kDecodeMaxSplits = 256;
-
 inline int64_t decode_max_splits(int64_t L) {
     const int64_t n = (L + 31) / 32;
     return n < kDecodeMaxSplits ? n : kDecodeMaxSplits;
+}
+
+inline size_t decode_align(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+// Bytes of split partials for steps of up to L keys.
+inline size_t decode_partial_bytes(int64_t B, int64_t Hq, int64_t D, int64_t L) {
+    return (size_t)B * (size_t)Hq * (size_t)decode_max_splits(L) * (size_t)(D + 2) * sizeof(float);
 }
 
 inline int decode_heads_per_wg(int64_t Hkv) {

@@ -48,11 +48,16 @@ def short_name(name: str) -> str:
     return n.replace("jl::(anonymous namespace)::", "jl::")
 
 
-def stats_markdown(path: str, title: str, cmd: str, top: int = 8) -> str:
+def stats_markdown(path: str, title: str, cmd: str, other: int = 3) -> str:
+    """Every library kernel (names starting with jl::) of the trace, and the
+    `other` longest-running kernels that are not the library's."""
     rows = list(csv.DictReader(open(path)))
+    ours = [r for r in rows if "jl::" in r["Name"]]
+    rest = [r for r in rows if "jl::" not in r["Name"]][:other]
+    keep = sorted(ours + rest, key=lambda r: -float(r["Percentage"]))
     out = [f"# {title}", "", "Command (repository root on one MI355X):", "", "```", cmd, "```", "",
            "| kernel | calls | average (us) | min (us) | max (us) | % GPU time |", "|---|---|---|---|---|---|"]
-    for r in rows[:top]:
+    for r in keep:
         n = short_name(r["Name"])
         n = n if len(n) < 80 else n[:77] + "..."
         out.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
