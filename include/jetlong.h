@@ -285,6 +285,30 @@ JL_API int jl_bifocal_decode(const void* q, const void* k_cache, const void* v_c
                       size_t workspace_bytes, void* hip_stream);
 
 /*
+ * jl_bifocal_decode_noalloc -- jl_bifocal_decode with no workspace argument
+ * and no allocation, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments (minus workspace) and the same result, bit for
+ * bit, as jl_bifocal_decode on a contiguous cache.
+ *
+ * The split partials go to a fixed 16 MiB device array inside the library
+ * (one per device, held until the process ends; its address is looked up
+ * on the first call on each device).  A step needs
+ * B * Hq * n_split * (D + 2) * 4 bytes, n_split <= min(ceil(L/32), 256) from
+ * the split plan (2 MiB for B = 1, Hq = 32, D = 128 at L = 128K); a step
+ * that needs more than 16 MiB returns JL_ESPACE.  Every call on a device
+ * shares that device's array: calls that overlap in time on one device
+ * (other streams, other threads) race and must not be issued.  Nothing in
+ * the array needs clearing between calls.  Errors otherwise as for
+ * jl_bifocal_decode.
+ */
+JL_API int jl_bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out,
+                                     float* lse, int in_dtype, int out_dtype, int64_t B, int64_t L,
+                                     int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
+                                     int64_t w_pretrained, double rope_base, float sm_scale,
+                                     const void* table, size_t table_bytes, void* hip_stream);
+
+/*
  * jl_bifocal_decode_unfused_workspace -- bytes of scratch for
  * jl_bifocal_decode_unfused: the decode partials above (rounded up to 256
  * bytes), then three fp32 pass outputs [B, Hq, D] and three log-sum-exps

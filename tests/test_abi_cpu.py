@@ -30,10 +30,10 @@ def test_exports_every_declared_symbol():
                            "jl_bifocal_prefill_chunk_paged", "jl_bifocal_decode_rkc", "jl_fi_table",
                            "jl_fi_table_fill_host", "jl_bifocal_prefill_fi", "jl_bifocal_decode_fi",
                            "jl_rope_interleaved_to_half", "jl_bifocal_decode_unfused_workspace",
-                           "jl_bifocal_decode_unfused", "jl_device_info"])
+                           "jl_bifocal_decode_unfused", "jl_device_info", "jl_bifocal_decode_noalloc"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 9
+    assert jl.jl_version() == 10
 
 
 def test_schedule_golden_and_table_size():
@@ -462,3 +462,19 @@ def test_call_scratch_is_allocated_on_the_call_stream(monkeypatch):
     binding._scratch(32, "cuda:0", None)   # torch's current stream: the call runs there too
     assert log == [("alloc", 32)]
 
+
+def test_decode_noalloc_validation_and_scratch_limit():
+    """The no-allocation decode validates like jl_bifocal_decode and refuses,
+    before any HIP call, a step whose partials exceed its fixed 16 MiB
+    scratch (1024 sequences x 64 heads x one split x 130 floats)."""
+    args = lambda **o: dict(dict(B=1, L=600, Lmax=700, Hq=8, Hkv=2, D=128, tab=FAKE), **o)
+
+    def call(a):
+        return jl.lib.jl_bifocal_decode_noalloc(FAKE, FAKE, FAKE, FAKE, None, jl.JL_BF16, jl.JL_BF16, a["B"],
+                                                a["L"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], 16, 64, 1e4, 0.125,
+                                                a["tab"], 1 << 40, None)
+    assert call(args(Lmax=599)) == jl.JL_EINVAL
+    assert call(args(tab=None)) == jl.JL_EINVAL
+    assert call(args(D=96)) == jl.JL_EUNSUPPORTED
+    assert call(args(B=1024, L=64, Lmax=64, Hq=64, Hkv=8)) == jl.JL_ESPACE
+    assert "scratch" in jl.jl_last_error()

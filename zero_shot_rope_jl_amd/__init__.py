@@ -18,5 +18,5 @@ from .binding import (  # noqa: F401
     jl_bifocal_decode_fi, jl_rope_interleaved_to_half,
     jl_bifocal_decode_workspace, jl_table_fill_host, alloc_table, alloc_prefill_workspace,
     alloc_decode_workspace, jl_bifocal_decode_unfused, jl_bifocal_decode_unfused_workspace,
-    alloc_decode_unfused_workspace, jl_device_info,
+    alloc_decode_unfused_workspace, jl_device_info, jl_bifocal_decode_noalloc,
 )

@@ -72,6 +72,9 @@ def _load():
     L.jl_bifocal_decode.restype = ctypes.c_int
     L.jl_bifocal_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                     i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
+    L.jl_bifocal_decode_noalloc.restype = ctypes.c_int
+    L.jl_bifocal_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                            i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp]
     L.jl_bifocal_decode_unfused_workspace.restype = ctypes.c_int
     L.jl_bifocal_decode_unfused_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(sz)]
     L.jl_bifocal_decode_unfused.restype = ctypes.c_int
@@ -399,6 +402,26 @@ def jl_bifocal_decode(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrain
                                  w_pretrained, rope_base, sm_scale, _ptr(table),
                                  table.numel() * table.element_size(), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def jl_bifocal_decode_noalloc(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrained: int,
+                              rope_base: float, sm_scale: float, table, stream=None):
+    """jl_bifocal_decode with the library's fixed scratch instead of a
+    workspace (no allocation anywhere in the call)."""
+    _need_device(q, k_cache, v_cache, out, lse, table)
+    B, one, Hq, D = q.shape
+    _, Lmax, Hkv, Dk = k_cache.shape
+    if one != 1 or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B:
+        raise ValueError("q must be [B,1,Hq,D] and the caches [B,Lmax,Hkv,D]")
+    if tuple(out.shape) != (B, 1, Hq, D):
+        raise ValueError("out must be [B, 1, Hq, D]")
+    if lse is not None and (tuple(lse.shape) != (B, Hq) or _dtype_code(lse) != JL_F32):
+        raise ValueError("lse must be float32 [B, Hq]")
+    _check(lib.jl_bifocal_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                         _dtype_code(q), _dtype_code(out), B, L, Lmax, Hq, Hkv, D, w0,
+                                         w_pretrained, rope_base, sm_scale, _ptr(table),
+                                         table.numel() * table.element_size(), _stream(stream)))
     return out, lse
 
 

@@ -95,7 +95,7 @@ JL_API int jl_device_info(int device, int* n_cu, int* max_clock_khz) {
     return JL_OK;
 }
 
-JL_API int jl_version(void) { return 9; }
+JL_API int jl_version(void) { return 10; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -512,9 +512,10 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
                 int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D, int64_t w0,
                 int64_t w_pretrained, double rope_base, float sm_scale, const void* table, size_t table_bytes,
                 void* workspace, size_t workspace_bytes, void* hip_stream, void* krot = nullptr,
-                jl_rotated_keys* rk_state = nullptr, const FiArgs* fi = nullptr, bool unfused = false) {
+                jl_rotated_keys* rk_state = nullptr, const FiArgs* fi = nullptr, bool unfused = false,
+                bool noalloc = false) {
     g_err.clear();
-    if (!q || !k_cache || !v_cache || !out || (!table && !fi) || !workspace)
+    if (!q || !k_cache || !v_cache || !out || (!table && !fi) || (!workspace && !noalloc))
         return fail(JL_EINVAL, "%s: q, the caches, out, table and workspace must be non-NULL", who);
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(table) ||
         !aligned16(workspace) || !aligned16(lse))
@@ -547,7 +548,7 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     }
     const UnfusedDecodeLayout ul = unfused_decode_layout(B, Hq, D, L);
     const size_t ws_need = unfused ? ul.total : jl::decode_partial_bytes(B, Hq, D, L);
-    if (workspace_bytes < ws_need)
+    if (!noalloc && workspace_bytes < ws_need)
         return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace_bytes, ws_need);
     if (Hkv > 65535) return fail(JL_EINVAL, "Hkv exceeds 65535");
     if (Hkv % 8 != 0 && 8 % Hkv != 0)
@@ -593,6 +594,16 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
             p.fi_phi[i] = jl::fi_phi(rope_base, (int)D, L, w_pretrained, fi->alpha, fi->beta, i);
     }
     set_decode_range(p, L, jl::kFused);
+    if (noalloc) {
+        // the partials of this step's split plan must fit the fixed scratch
+        const size_t need = (size_t)B * (size_t)Hq * (size_t)p.n_split * (size_t)(D + 2) * sizeof(float);
+        if (need > jl::kNoAllocScratchBytes)
+            return fail(JL_ESPACE, "%s: the step needs %zu bytes of scratch, the library's fixed scratch holds %zu",
+                        who, need, jl::kNoAllocScratchBytes);
+        (void)hipGetLastError();
+        const hipError_t es = jl::noalloc_scratch(&workspace);
+        if (es != hipSuccess) return fail(JL_EHIP, "%s: scratch lookup failed: %s", who, hipGetErrorString(es));
+    }
     p.ws = static_cast<float*>(workspace);
     (void)hipGetLastError();
     if (krot) {
@@ -681,6 +692,15 @@ JL_API int jl_bifocal_decode_unfused(const void* q, const void* k_cache, const v
     return decode_impl("decode_unfused", q, k_cache, v_cache, nullptr, 0, 0, 0, out, lse, in_dtype, out_dtype, B, L,
                        Lmax, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
                        workspace_bytes, hip_stream, nullptr, nullptr, nullptr, true);
+}
+
+JL_API int jl_bifocal_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                     int in_dtype, int out_dtype, int64_t B, int64_t L, int64_t Lmax, int64_t Hq,
+                                     int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained, double rope_base,
+                                     float sm_scale, const void* table, size_t table_bytes, void* hip_stream) {
+    return decode_impl("decode_noalloc", q, k_cache, v_cache, nullptr, 0, 0, 0, out, lse, in_dtype, out_dtype, B, L,
+                       Lmax, Hq, Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, nullptr, 0,
+                       hip_stream, nullptr, nullptr, nullptr, false, true);
 }
 
 JL_API int jl_bifocal_decode_rkc(const void* q, const void* k_cache, const void* v_cache, void* krot_cache,

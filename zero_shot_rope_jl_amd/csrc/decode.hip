@@ -41,6 +41,8 @@
 // rows (cos, sin)(n * phi_i) the kernel forms itself.
 #include <math.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace jl {
@@ -637,6 +639,31 @@ hipError_t launch_rotate_rows(const void* k, void* krot, const DecodeParams& p, 
                            static_cast<const __bf16*>(k), static_cast<__bf16*>(krot), p.TF, n_items, p.Lmax,
                            (int)p.Hkv, r0, r1 - r0, p.G, p.table, p.table_key, p.rope_base, p.L);
     return hipGetLastError();
+}
+
+// Scratch of jl_bifocal_decode_noalloc, for callers that cannot allocate
+// (graph capture, serving loops): the split partials live in this fixed
+// device array, one copy per device, held until the process ends.  Host code
+// uses only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* per_device[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        per_device[dev] = a;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int out_dtype, hipStream_t stream) {

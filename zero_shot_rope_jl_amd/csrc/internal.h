@@ -181,4 +181,9 @@ hipError_t launch_ie_merge(const MergeParams& p, int out_dtype, hipStream_t stre
 hipError_t launch_prefill_bf16(const PrefillParams& p, int out_dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int out_dtype, hipStream_t stream);
 
+// The fixed device scratch of jl_bifocal_decode_noalloc: its size, and its
+// address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace jl
