@@ -77,20 +77,28 @@ JL_API int jl_device_info(int device, int* n_cu, int* max_clock_khz);
  * jl_schedule -- §3.1 Eq. (2) and the correction-angle table for §3.2 Eq. (5).
  *
  *   *G_out = max(1, ceil(L / w_pretrained)).
- *   *table_bytes_needed = bytes of a table covering correction offsets
- *       n = p - f(p) for every position p < L, for this head_dim.
+ *   *table_bytes_needed = bytes of a table covering the correction offsets
+ *       n = p - f(p) of every position p < L under this G, i.e. n < n_cover
+ *       with n_cover = n(L-1) + 1, for this head_dim.
  *
  * If `table` is non-NULL, the call also enqueues on `hip_stream` a float64
- * kernel that fills the table for (head_dim, rope_base) covering p < L.  The
- * table does not depend on G or w_pretrained, so one table built for the
- * largest length serves every later call with L no larger and the same
- * head_dim and rope_base (decode steps that cross a G change included).
+ * kernel that fills the table for (head_dim, rope_base) covering n < n_cover.
+ * The entries do not depend on G, and the offsets of a call grow with its L
+ * and its G, so one table built for the largest length serves every later
+ * call with L no larger, w_pretrained no smaller and the same head_dim and
+ * rope_base (decode steps that cross a G change included).  w_pretrained = 1
+ * sizes it for any window (n_cover = L).  A call whose offsets the table does
+ * not cover, or whose head_dim or rope_base differ, writes NaN outputs.
  *
  * Table layout (opaque to callers; documented for completeness): a 64-byte
- * header {magic, head_dim, n_cover, rope_base}, then fp32 (cos, sin) pairs
- * TF[n][i] = (cos, sin)(n * theta_i) for n < L, i < D/2, each angle formed in
- * float64 and rounded once to fp32 (L * D * 4 bytes: 64 MiB for L = 128K,
- * D = 128).
+ * header {magic, head_dim, n_cover, rope_base}, then two levels of fp32
+ * (cos, sin) pairs, each angle formed in float64 and rounded once to fp32:
+ * 1024 rows TL[l][i] = (cos, sin)(l * theta_i), then ceil(n_cover / 1024)
+ * rows TH[h][i] = (cos, sin)(1024 h * theta_i), i < D/2.  The entry of offset
+ * n is the complex product TL[n mod 1024] * TH[n / 1024] (within a few fp32
+ * ulp).  Size: (1024 + ceil(n_cover / 1024)) * D * 4 bytes + 64: 0.57 MB for
+ * L = 128K at any window, 0.92 MB for L = 2^20 with w_pretrained = 2^18,
+ * D = 128.
  *
  * With table == NULL no HIP call is made.  Errors: L < 1, w_pretrained < 1,
  * head_dim not in {64, 128} (JL_EUNSUPPORTED), rope_base <= 1 or not finite,
@@ -414,10 +422,10 @@ JL_API int jl_bifocal_decode_rkc(const void* q, const void* k_cache, const void*
                                  size_t workspace_bytes, void* hip_stream);
 
 /*
- * jl_table_fill_host -- fill a HOST buffer with the same table jl_schedule
- * writes on the device (same layout, same float64 formulas compiled for the
- * host).  Lets the table builder be checked without a GPU.  Errors as for
- * jl_schedule.
+ * jl_table_fill_host -- fill a HOST buffer with the table jl_schedule writes
+ * on the device for w_pretrained = 1 (covering every offset n < L; same
+ * layout, same float64 formulas compiled for the host).  Lets the table
+ * builder be checked without a GPU.  Errors as for jl_schedule.
  */
 JL_API int jl_table_fill_host(int64_t L, int64_t head_dim, double rope_base, void* table,
                        size_t table_bytes);
@@ -464,10 +472,12 @@ JL_API int jl_rope_interleaved_to_half(const void* x, void* out, int dtype, int6
 
 /*
  * jl_fi_table -- the table of the frequency-interpolation view for one call:
- * rows p < L of (cos, sin)(p * phi_i), angles formed in float64 and stored
- * fp32, after a header recording (L, w_pretrained, fi_alpha, fi_beta,
- * head_dim, rope_base).  Same size as jl_schedule's table for L
- * (*table_bytes_needed); table may be NULL to query the size only.  The
+ * (cos, sin)(p * phi_i) for positions p < L in jl_schedule's two-level
+ * layout (1024 rows of l * phi_i, then ceil(L / 1024) rows of 1024 h * phi_i;
+ * angles formed in float64 and stored fp32), after a header recording (L,
+ * w_pretrained, fi_alpha, fi_beta, head_dim, rope_base).  Same size as
+ * jl_schedule's table for L with w_pretrained = 1 (*table_bytes_needed);
+ * table may be NULL to query the size only.  The
  * fill is enqueued on hip_stream.  jl_bifocal_prefill_fi checks the header
  * and writes NaN outputs when it was built for anything else.
  *

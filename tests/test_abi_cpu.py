@@ -41,7 +41,20 @@ def test_schedule_golden_and_table_size():
         for e in json.load(fh)["examples"]:
             G, need = jl.jl_schedule(e["L"], e["w_pretrained"], 128, 1e6)
             assert G == e["G"], e["cite"]
-            assert need == 64 + e["L"] * 64 * 8
+            # two levels: 1024 low rows, then one high row per 1024 offsets below
+            # n(L-1) + 1, where n(p) = p - floor(p/G) (the largest offset a call reads)
+            n_cover = (e["L"] - 1) - (e["L"] - 1) // G + 1
+            assert need == 64 + (1024 + -(-n_cover // 1024)) * 64 * 8
+
+
+def test_table_is_small_at_one_million_tokens():
+    """A 1M-token call extended 4x (w_pretrained 256K, G = 4) reads offsets below
+    786433: the table is under 1 MB at D = 128."""
+    G, need = jl.jl_schedule(1 << 20, 1 << 18, 128, 1e6)
+    assert G == 4 and need == 64 + (1024 + 769) * 512 and need < 1_000_000
+    # without the pretrained window (w_pretrained = 1: G = L, offsets up to L - 1)
+    _, worst = jl.jl_schedule(1 << 20, 1, 128, 1e6)
+    assert worst == 64 + 2048 * 512
 
 
 def _sched(L=100, w=10, D=128, base=1e4, G=True, table=None, tbytes=0):
@@ -317,13 +330,25 @@ def test_host_table_matches_numpy_float64(D, base, L):
     assert hdr[4:8].view(np.int32)[0] == D
     assert hdr[8:16].view(np.int64)[0] == L
     assert hdr[16:24].view(np.float64)[0] == base
-    ent = buf[64:].view(np.float32).reshape(L, D // 2, 2)
+    n_hi = -(-L // 1024)
+    ent = buf[64:].view(np.float32).reshape(1024 + n_hi, D // 2, 2)
     theta = base ** (-(2.0 * np.arange(D // 2)) / D)          # independent float64 definition
-    ang = np.arange(L, dtype=np.float64)[:, None] * theta[None, :]
+    # the rows: angles l * theta (l < 1024), then 1024 h * theta (h < ceil(L / 1024))
+    mult = np.concatenate([np.arange(1024), 1024 * np.arange(n_hi)]).astype(np.float64)
+    ang = mult[:, None] * theta[None, :]
     want = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
     # one fp32 ulp of rounding plus the float64 angle error (|n * d(theta)| < 1e-10)
     ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
     assert np.all(np.abs(ent.astype(np.float64) - want) <= ulp + 1e-10)
+    # the entry of offset n is TL[n mod 1024] * TH[n / 1024]: within a few fp32
+    # ulp of (cos, sin)(n theta) for every n the table covers
+    n = np.unique(np.concatenate([np.arange(min(L, 2100)), np.random.default_rng(L).integers(0, L, 2000)]))
+    n = n[n < L]
+    lo, hi = ent[n % 1024].astype(np.float64), ent[1024 + n // 1024].astype(np.float64)
+    c = lo[..., 0] * hi[..., 0] - lo[..., 1] * hi[..., 1]
+    s_ = lo[..., 0] * hi[..., 1] + lo[..., 1] * hi[..., 0]
+    a = n[:, None].astype(np.float64) * theta[None, :]
+    assert np.max(np.abs(c - np.cos(a))) <= 4e-7 and np.max(np.abs(s_ - np.sin(a))) <= 4e-7
 
 
 def test_binding_has_no_cpu_fallback():
@@ -354,12 +379,20 @@ def test_host_fi_table_matches_oracle(D, base, L, w_pre, alpha, beta):
     assert hdr[16:24].view(np.float64)[0] == base
     assert hdr[24:32].view(np.int64)[0] == L and hdr[32:40].view(np.int64)[0] == w_pre
     assert hdr[40:48].view(np.float64)[0] == alpha and hdr[48:56].view(np.float64)[0] == beta
-    ent = buf[64:].view(np.float32).reshape(L, D // 2, 2)
+    n_hi = -(-L // 1024)
+    ent = buf[64:].view(np.float32).reshape(1024 + n_hi, D // 2, 2)
     phi = oracle.inv_freq(D, base) - oracle.fi_inv_freq(D, base, L, w_pre, alpha, beta)
-    ang = np.arange(L, dtype=np.float64)[:, None] * phi[None, :]
+    mult = np.concatenate([np.arange(1024), 1024 * np.arange(n_hi)]).astype(np.float64)
+    ang = mult[:, None] * phi[None, :]
     want = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
     ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
     assert np.all(np.abs(ent.astype(np.float64) - want) <= ulp + 1e-10)
+    # position p: TL[p mod 1024] * TH[p / 1024] within a few fp32 ulp of (cos, sin)(p phi)
+    p = np.arange(L)
+    lo, hi = ent[p % 1024].astype(np.float64), ent[1024 + p // 1024].astype(np.float64)
+    a = p[:, None].astype(np.float64) * phi[None, :]
+    assert np.max(np.abs(lo[..., 0] * hi[..., 0] - lo[..., 1] * hi[..., 1] - np.cos(a))) <= 4e-7
+    assert np.max(np.abs(lo[..., 0] * hi[..., 1] + lo[..., 1] * hi[..., 0] - np.sin(a))) <= 4e-7
     if L <= w_pre or alpha < 0:   # s = 1, or every pair kept: the identity
         assert np.all(ent[..., 0] == 1.0) and np.all(ent[..., 1] == 0.0)
 
@@ -376,7 +409,7 @@ def test_fi_ramp_validation(alpha, beta):
 def test_fi_table_size_and_space():
     need = ctypes.c_size_t(0)
     assert jl.lib.jl_fi_table(1000, 100, 128, 1e4, 1.0, 32.0, None, 0, ctypes.byref(need), None) == jl.JL_OK
-    assert need.value == 64 + 1000 * 64 * 8
+    assert need.value == 64 + (1024 + 1) * 64 * 8
     assert jl.lib.jl_fi_table(1000, 100, 128, 1e4, 1.0, 32.0, FAKE, need.value - 1, None, None) == jl.JL_ESPACE
     assert jl.lib.jl_fi_table(1000, 0, 128, 1e4, 1.0, 32.0, None, 0, None, None) == jl.JL_EINVAL
     assert jl.lib.jl_fi_table(1000, 100, 96, 1e4, 1.0, 32.0, None, 0, None, None) == jl.JL_EUNSUPPORTED

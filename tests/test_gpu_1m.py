@@ -27,7 +27,10 @@ def test_1m_prefill_sampled_rows_and_decode_across_g():
     x = si.make_prefill_inputs(w, want_f64=False)
     q, k, v = (to_dev(x[n], w.dtype) for n in "qkv")
     Lmax = w.L + 2
-    table = jl.alloc_table(Lmax, w.D, w.rope_base)
+    # sized for the pretrained window: offsets below n(Lmax - 1) + 1 under G(Lmax) = 5
+    table = jl.alloc_table(Lmax, w.D, w.rope_base, w_pretrained=w.w_pretrained)
+    print(f"[1m] correction table {table.numel()} bytes", flush=True)
+    assert table.numel() < 1_100_000
 
     print("[1m] GPU prefill", flush=True)
     out, lse = prefill(q, k, v, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, torch.float32, table)

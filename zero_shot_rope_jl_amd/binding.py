@@ -208,12 +208,15 @@ def jl_table_fill_host(L: int, head_dim: int, rope_base: float):
     return buf
 
 
-def alloc_table(L: int, head_dim: int, rope_base: float, device="cuda", stream=None):
-    """Allocate a device table with torch and fill it through jl_schedule."""
+def alloc_table(L: int, head_dim: int, rope_base: float, device="cuda", stream=None, w_pretrained: int = 1):
+    """Allocate a device table with torch and fill it through jl_schedule.
+
+    It serves every call with up to L tokens and pretrained window >=
+    ``w_pretrained``; the default 1 covers every window (offsets up to L - 1)."""
     torch = _torch()
-    _, need = jl_schedule(L, 1, head_dim, rope_base)
+    _, need = jl_schedule(L, w_pretrained, head_dim, rope_base)
     t = torch.empty(need, dtype=torch.uint8, device=device)
-    jl_schedule(L, 1, head_dim, rope_base, table=t, stream=stream)
+    jl_schedule(L, w_pretrained, head_dim, rope_base, table=t, stream=stream)
     return t
 
 

@@ -104,7 +104,10 @@ JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double
     if (L < 1 || L > kMaxLen) return fail(JL_EINVAL, "L must be in [1, 2^30] (got %lld)", (long long)L);
     if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1 (got %lld)", (long long)w_pretrained);
     if (int rc = check_rope(head_dim, rope_base)) return rc;
-    const size_t need = jl::table_bytes_for(L, (int)head_dim);
+    // the offsets of every call with L' <= L and this w_pretrained are below
+    // n(L-1) + 1 (they grow with L' and with G)
+    const int64_t n_cover = jl::table_need(L, group_size(L, w_pretrained));
+    const size_t need = jl::table_bytes_for(n_cover, (int)head_dim);
     if (table_bytes_needed) *table_bytes_needed = need;
     if (table) {
         if (!aligned16(table)) return fail(JL_EINVAL, "table must be 16-byte aligned");
@@ -114,7 +117,8 @@ JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double
     *G_out = group_size(L, w_pretrained);
     if (!table) return JL_OK;
     (void)hipGetLastError();
-    hipError_t e = jl::launch_table_fill(table, L, (int)head_dim, rope_base, static_cast<hipStream_t>(hip_stream));
+    hipError_t e = jl::launch_table_fill(table, n_cover, (int)head_dim, rope_base,
+                                         static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(JL_EHIP, "table fill launch failed: %s", hipGetErrorString(e));
     return JL_OK;
 }
@@ -207,7 +211,7 @@ namespace {
 int check_prefill(const char* who, const void* q, const void* k, const void* v, const void* out, const float* lse,
                   int in_dtype, int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Lkv, int64_t Hq,
                   int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale,
-                  const void* table, size_t table_bytes, const void* workspace) {
+                  const void* table, size_t table_bytes, const void* workspace, bool fi = false) {
     if (!q || !k || !v || !out || !table) return fail(JL_EINVAL, "%s: q, k, v, out and table must be non-NULL", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(table) ||
         !aligned16(lse) || !aligned16(workspace))
@@ -221,7 +225,8 @@ int check_prefill(const char* who, const void* q, const void* k, const void* v, 
     const int64_t R = Hq / Hkv;
     if (R != 1 && R != 2 && R != 4 && R != 8)
         return fail(JL_EUNSUPPORTED, "GQA ratio Hq/Hkv = %lld not supported (1, 2, 4, 8)", (long long)R);
-    const size_t need = jl::table_bytes_for(L, (int)D);
+    // the table rows the call reads (the interpolation view indexes by position)
+    const size_t need = jl::table_bytes_for(fi ? L : jl::table_need(L, group_size(L, w_pretrained)), (int)D);
     if (table_bytes < need)
         return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
     const int64_t n_qtiles = (Lq + 256 / R - 1) / (256 / R);
@@ -272,7 +277,7 @@ int prefill_impl(const char* who, const void* q, const void* k, const void* v, v
                  const FiArgs* fi = nullptr) {
     g_err.clear();
     if (int rc = check_prefill(who, q, k, v, out, lse, in_dtype, out_dtype, B, Lq, L, Lkv, Hq, Hkv, D, w0,
-                               w_pretrained, rope_base, sm_scale, table, table_bytes, workspace))
+                               w_pretrained, rope_base, sm_scale, table, table_bytes, workspace, fi != nullptr))
         return rc;
     if (fi)
         if (int rc = check_fi_ramp(fi->alpha, fi->beta)) return rc;
@@ -542,7 +547,7 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     if (fi) {
         if (int rc = check_fi_ramp(fi->alpha, fi->beta)) return rc;
     } else {
-        const size_t need = jl::table_bytes_for(L, (int)D);
+        const size_t need = jl::table_bytes_for(jl::table_need(L, group_size(L, w_pretrained)), (int)D);
         if (table_bytes < need)
             return fail(JL_ESPACE, "table holds %zu bytes, %zu needed for L=%lld", table_bytes, need, (long long)L);
     }

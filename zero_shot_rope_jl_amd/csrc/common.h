@@ -17,13 +17,18 @@ constexpr uint32_t kTableMagic = 0x324C544Au;    // "JTL2": offset table
 constexpr uint32_t kTableMagicFI = 0x3146544Au;  // "JTF1": interpolation table
 constexpr int kTableHeaderBytes = 64;
 
-// Device/host view of the correction-angle table header.  The header is
-// followed by rows TF[n][i] = (cos, sin)(n * phi_i), n < n_cover, i < D/2,
-// each angle formed in float64 and rounded once to fp32.  Offset tables
-// (the aliasing correction) have phi_i = theta_i and are indexed by the
-// offset n = p - floor(p/G); interpolation tables have
-// phi_i = theta_i - theta'_i (the frequency-interpolation remote view) and
-// are indexed by the position p.
+// Device/host view of the correction-angle table header.  The table holds
+// (cos, sin)(n * phi_i) for every n < n_cover and i < D/2 in two levels: the
+// header is followed by kTableLoRows rows TL[l] = (cos, sin)(l * phi_i) and
+// then ceil(n_cover / kTableLoRows) rows TH[h] = (cos, sin)(kTableLoRows * h
+// * phi_i), each angle formed in float64 and rounded once to fp32; the entry
+// for n is the complex product TL[n mod 1024] * TH[n / 1024] (table_cs), a
+// few fp32 ulp from the rounded exact value.  So the table grows by one
+// 512-byte row (D = 128) per 1024 offsets: 0.9 MB covers the offsets of a
+// 1M-token call at G = 4.  Offset tables (the aliasing correction) have
+// phi_i = theta_i and are indexed by the offset n = p - floor(p/G);
+// interpolation tables have phi_i = theta_i - theta'_i (the frequency-
+// interpolation remote view) and are indexed by the position p.
 struct TableHeader {
     uint32_t magic;
     int32_t head_dim;
@@ -49,9 +54,14 @@ struct TableKey {
     double fi_beta;
 };
 
+// The offsets a call over positions 0..L-1 reads: n(p) = p - floor(p/G)
+// grows with p, so every n is below n(L-1) + 1.  (The interpolation view runs
+// with G = max(2, L), where n(p) = p.)
+__host__ __device__ inline int64_t table_need(int64_t L, int64_t G) { return (L - 1) - (L - 1) / G + 1; }
+
 __host__ __device__ inline bool table_matches(const TableHeader* th, const TableKey& key, int D, double base,
-                                              int64_t L) {
-    return th->magic == key.magic && th->head_dim == D && th->rope_base == base && th->n_cover >= L &&
+                                              int64_t n_need) {
+    return th->magic == key.magic && th->head_dim == D && th->rope_base == base && th->n_cover >= n_need &&
            th->fi_L == key.fi_L && th->fi_w_pretrained == key.fi_w_pretrained && th->fi_alpha == key.fi_alpha &&
            th->fi_beta == key.fi_beta;
 }
@@ -71,8 +81,31 @@ __host__ __device__ inline double fi_phi(double base, int D, int64_t L, int64_t 
     return theta * (1.0 - g) * (1.0 - 1.0 / s);
 }
 
+constexpr int kTableLoShift = 10;
+constexpr int64_t kTableLoRows = int64_t(1) << kTableLoShift;
+
+__host__ __device__ inline int64_t table_rows_for(int64_t n_cover) {
+    return kTableLoRows + (n_cover + kTableLoRows - 1) / kTableLoRows;
+}
+
 __host__ __device__ inline size_t table_bytes_for(int64_t n_cover, int head_dim) {
-    return (size_t)kTableHeaderBytes + (size_t)n_cover * (size_t)(head_dim / 2) * 8u;
+    return (size_t)kTableHeaderBytes + (size_t)table_rows_for(n_cover) * (size_t)(head_dim / 2) * 8u;
+}
+
+// (cos, sin)(n * phi_i) from the two levels of the table rows TF (after the
+// header): TL[n mod 1024] * TH[n / 1024] as complex numbers.
+__device__ inline float2 table_cs(const float2* __restrict__ TF, int half, int64_t n, int i) {
+    const float2 lo = TF[(n & (kTableLoRows - 1)) * half + i];
+    const float2 hi = TF[(kTableLoRows + (n >> kTableLoShift)) * half + i];
+    return make_float2(lo.x * hi.x - lo.y * hi.y, lo.x * hi.y + lo.y * hi.x);
+}
+
+// Pairs i and i + 1 of row n (i even): (cos_i, sin_i, cos_i+1, sin_i+1).
+__device__ inline float4 table_cs2(const float2* __restrict__ TF, int half, int64_t n, int i) {
+    const float4 lo = *reinterpret_cast<const float4*>(TF + (n & (kTableLoRows - 1)) * half + i);
+    const float4 hi = *reinterpret_cast<const float4*>(TF + (kTableLoRows + (n >> kTableLoShift)) * half + i);
+    return make_float4(lo.x * hi.x - lo.y * hi.y, lo.x * hi.y + lo.y * hi.x, lo.z * hi.z - lo.w * hi.w,
+                       lo.z * hi.w + lo.w * hi.z);
 }
 
 // Rotate the pair (x, y) by the angle -n*theta (cs = cos, sn = sin of +n*theta).

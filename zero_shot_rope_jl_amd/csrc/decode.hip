@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     // frequency-interpolation view, which has no table)
     auto tf = [&](int64_t n, int i) -> float2 {
         if constexpr (FI) return fi_cs(p.fi_phi[i], n);
-        else return TF[n * HALF + i];
+        else return table_cs(TF, HALF, n, i);
     };
     const int64_t row = p.Hkv * D;
     const int64_t cache_b = PAGED ? (int64_t)g * D : (int64_t)b * p.Lmax * row + (int64_t)g * D;
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         wa_cs = tf(p.rot_row - p.rot_row / G, lane);
     }
 
-    if (tid == 0) s_bad = FI ? 0 : !table_matches(p.table, p.table_key, D, p.rope_base, p.L);
+    if (tid == 0) s_bad = FI ? 0 : !table_matches(p.table, p.table_key, D, p.rope_base, table_need(p.L, p.G));
     // rows 0..32 of the table are cos/sin(dn * theta_i); only rows < L are
     // guaranteed to exist and dn <= L-1, so copy no further
     if (!RKC)
@@ -601,11 +601,10 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const __bf16* __restri
     const int64_t o = ((b * Lmax + pos) * Hkv + h) * D + 8 * c;
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(k + o);
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(k + o + HALF);
-    const float4* cs = reinterpret_cast<const float4*>(TF + n * HALF + 8 * c);
     bf16x8 xo, yo;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float4 c4 = cs[e];
+        const float4 c4 = table_cs2(TF, HALF, n, 8 * c + 2 * e);
         float x0 = (float)x[2 * e], y0 = (float)y[2 * e];
         float x1 = (float)x[2 * e + 1], y1 = (float)y[2 * e + 1];
         rotate_back(x0, y0, make_float2(c4.x, c4.y));
@@ -615,7 +614,7 @@ __global__ __launch_bounds__(256) void rotate_rows_kernel(const __bf16* __restri
         xo[2 * e + 1] = (__bf16)x1;
         yo[2 * e + 1] = (__bf16)y1;
     }
-    if (!table_matches(table, key, D, rope_base, L)) {
+    if (!table_matches(table, key, D, rope_base, table_need(L, G))) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xo[e] = yo[e] = (__bf16)NAN;
     }

@@ -104,7 +104,7 @@ __device__ __forceinline__ void load_q_frags(QF* qv, const T* __restrict__ qrow,
             for (int j = 0; j < W; ++j) {
                 float x = (float)qv[c][j];
                 float y = (float)qv[c + NQ / 2][j];
-                rotate_back(x, y, TF[nq * Lay::HALF + c * 2 * W + W * hh + j]);
+                rotate_back(x, y, table_cs(TF, Lay::HALF, nq, c * 2 * W + W * hh + j));
                 qv[c][j] = (T)x;
                 qv[c + NQ / 2][j] = (T)y;
             }
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     }
     if (tid == 0) {
         const TableHeader* th = p.table;
-        s_bad = !table_matches(th, p.table_key, D, p.rope_base, p.L);
+        s_bad = !table_matches(th, p.table_key, D, p.rope_base, table_need(p.L, p.G));
     }
     __syncthreads();
     if (s_bad) {
@@ -419,9 +419,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         st.y = ok ? *reinterpret_cast<const typename St::KV*>(krow + HALF + f0) : typename St::KV{};
         st.v = ok ? *reinterpret_cast<const typename St::VV*>(vrow + v0) : typename St::VV{};
         if (pi < nR) {
-            const float4* t4 = reinterpret_cast<const float4*>(TF + (int64_t)(ok ? kpos - kpos / G : 0) * HALF + f0);
+            const int64_t n = ok ? kpos - kpos / G : 0;
 #pragma unroll
-            for (int j = 0; j < PPT / 2; ++j) st.cs[j] = t4[j];
+            for (int j = 0; j < PPT / 2; ++j) st.cs[j] = table_cs2(TF, HALF, n, f0 + 2 * j);
         }
     };
     auto stage_store = [&](int pi, int buf) {

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 
     if (tid == 0) {
         const TableHeader* th = p.table;
-        s_bad = !table_matches(th, p.table_key, D, p.rope_base, p.L);
+        s_bad = !table_matches(th, p.table_key, D, p.rope_base, table_need(p.L, p.G));
     }
     __syncthreads();
     if (s_bad) {
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         float x = (float)raw[c][e], y = (float)raw[c + NC / 2][e];
-                        rotate_back(x, y, TF[nq * HALF + 16 * c + 8 * hh + e]);
+                        rotate_back(x, y, table_cs(TF, HALF, nq, 16 * c + 8 * hh + e));
                         qv[j][c][e] = (__bf16)(x * scale2);
                         qv[j][c + NC / 2][e] = (__bf16)(y * scale2);
                     }
@@ -641,11 +641,10 @@ __global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restri
     const __bf16* src = k + (crow * Hkv + row % Hkv) * D + 8 * c;
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(src);
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(src + HALF);
-    const float4* cs = reinterpret_cast<const float4*>(TF + n * HALF + 8 * c);
     bf16x8 xo, yo;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float4 c4 = cs[e];
+        const float4 c4 = table_cs2(TF, HALF, n, 8 * c + 2 * e);
         float x0 = (float)x[2 * e], y0 = (float)y[2 * e];
         float x1 = (float)x[2 * e + 1], y1 = (float)y[2 * e + 1];
         rotate_back(x0, y0, make_float2(c4.x, c4.y));

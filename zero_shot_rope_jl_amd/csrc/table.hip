@@ -1,8 +1,9 @@
 // Correction-angle table for the on-the-fly RoPE correction (Jet-Long §3.2,
 // Eq. 5): (cos, sin)(n * theta_i) for every offset n = p - floor(p/G) below
-// the coverage.  Angles are formed in float64 and rounded once to fp32; the
-// table does not depend on G, so one table serves every G and every L up to
-// its coverage.
+// the coverage, held in two levels (rows TL[l] for l < 1024 and TH[h] for the
+// multiples 1024 h; see TableHeader).  Angles are formed in float64 and
+// rounded once to fp32; the table does not depend on G, so one table serves
+// every G and every L whose offsets it covers.
 #include <math.h>
 #include <string.h>
 
@@ -10,9 +11,15 @@
 
 namespace jl {
 
-__host__ __device__ inline float2 table_entry(double base, int D, int64_t n, int i) {
+// The multiple of the angle that table row r holds: r for the low level,
+// 1024 (r - 1024) for the high level.
+__host__ __device__ inline double row_multiple(int64_t r) {
+    return r < kTableLoRows ? (double)r : (double)(kTableLoRows * (r - kTableLoRows));
+}
+
+__host__ __device__ inline float2 table_entry(double base, int D, int64_t r, int i) {
     const double theta = pow(base, -(2.0 * (double)i) / (double)D);
-    const double a = (double)n * theta;
+    const double a = row_multiple(r) * theta;
     return make_float2((float)cos(a), (float)sin(a));
 }
 
@@ -30,7 +37,7 @@ __global__ void table_fill_kernel(char* table, int64_t n_cover, int D, double ba
     const int half = D / 2;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     float2* ent = reinterpret_cast<float2*>(table + kTableHeaderBytes);
-    if (idx < n_cover * half) ent[idx] = table_entry(base, D, idx / half, (int)(idx % half));
+    if (idx < table_rows_for(n_cover) * half) ent[idx] = table_entry(base, D, idx / half, (int)(idx % half));
     if (idx == 0) {
         *reinterpret_cast<TableHeader*>(table) = make_header(n_cover, D, base);
     }
@@ -50,8 +57,8 @@ __host__ __device__ inline TableHeader make_fi_header(int64_t L, int D, double b
     return h;
 }
 
-__host__ __device__ inline float2 fi_entry(double phi, int64_t p) {
-    const double a = (double)p * phi;
+__host__ __device__ inline float2 fi_entry(double phi, int64_t r) {
+    const double a = row_multiple(r) * phi;
     return make_float2((float)cos(a), (float)sin(a));
 }
 
@@ -60,7 +67,7 @@ __global__ void table_fill_fi_kernel(char* table, int64_t L, int D, double base,
     const int half = D / 2;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     float2* ent = reinterpret_cast<float2*>(table + kTableHeaderBytes);
-    if (idx < L * half) {
+    if (idx < table_rows_for(L) * half) {
         const int i = (int)(idx % half);
         ent[idx] = fi_entry(fi_phi(base, D, L, w_pre, alpha, beta, i), idx / half);
     }
@@ -69,7 +76,7 @@ __global__ void table_fill_fi_kernel(char* table, int64_t L, int D, double base,
 
 hipError_t launch_table_fill_fi(void* table, int64_t L, int head_dim, double rope_base, int64_t w_pretrained,
                                 double alpha, double beta, hipStream_t stream) {
-    const int64_t total = L * (head_dim / 2);
+    const int64_t total = table_rows_for(L) * (head_dim / 2);
     const int threads = 256;
     const int blocks = (int)((total + threads - 1) / threads);
     hipLaunchKernelGGL(table_fill_fi_kernel, dim3(blocks), dim3(threads), 0, stream, static_cast<char*>(table), L,
@@ -85,13 +92,13 @@ void table_fill_fi_host(void* table, int64_t L, int head_dim, double rope_base, 
     float2* ent = reinterpret_cast<float2*>(static_cast<char*>(table) + kTableHeaderBytes);
     for (int i = 0; i < half; ++i) {
         const double phi = fi_phi(rope_base, head_dim, L, w_pretrained, alpha, beta, i);
-        for (int64_t p = 0; p < L; ++p) ent[p * half + i] = fi_entry(phi, p);
+        for (int64_t r = 0; r < table_rows_for(L); ++r) ent[r * half + i] = fi_entry(phi, r);
     }
 }
 
 hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double rope_base,
                              hipStream_t stream) {
-    const int64_t total = n_cover * (head_dim / 2);
+    const int64_t total = table_rows_for(n_cover) * (head_dim / 2);
     const int threads = 256;
     const int blocks = (int)((total + threads - 1) / threads);
     hipLaunchKernelGGL(table_fill_kernel, dim3(blocks), dim3(threads), 0, stream,
@@ -104,8 +111,8 @@ void table_fill_host(void* table, int64_t n_cover, int head_dim, double rope_bas
     TableHeader h = make_header(n_cover, head_dim, rope_base);
     memcpy(table, &h, sizeof(h));
     float2* ent = reinterpret_cast<float2*>(static_cast<char*>(table) + kTableHeaderBytes);
-    for (int64_t n = 0; n < n_cover; ++n)
-        for (int i = 0; i < half; ++i) ent[n * half + i] = table_entry(rope_base, head_dim, n, i);
+    for (int64_t r = 0; r < table_rows_for(n_cover); ++r)
+        for (int i = 0; i < half; ++i) ent[r * half + i] = table_entry(rope_base, head_dim, r, i);
 }
 
 }  // namespace jl
