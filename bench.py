@@ -263,11 +263,15 @@ CHUNK_LQ = (1, 16, 256, 4096)
 
 def bench_chunk(torch, jl, args, w, x, page_size=256):
     """The last Lq tokens of the workload as one chunk over the cache of all L
-    keys (jl_bifocal_prefill_chunk), for several chunk lengths; the longest
-    also over the cache held in shuffled pages (jl_bifocal_prefill_chunk_paged)."""
+    keys (jl_bifocal_prefill_chunk), for several chunk lengths.  Each length
+    is timed as a chunk of a sequence prefilled chunk by chunk: the call's
+    rotated-key state covers the rows before the chunk, so it rotates its own
+    Lq new keys (the state is set back before every timed call).  The
+    longest chunk is also timed without a state (every key rotated) and over
+    the cache held in shuffled pages (jl_bifocal_prefill_chunk_paged)."""
     q, k, v = (to_dev(torch, x[n], w.dtype) for n in "qkv")
-    table = jl.alloc_table(w.L, w.D, w.rope_base)
-    ws = jl.alloc_prefill_workspace(k, w.w_pretrained)
+    table = jl.alloc_table(w.L, w.D, w.rope_base, w_pretrained=w.w_pretrained)
+    G = (w.L + w.w_pretrained - 1) // w.w_pretrained
     max_pages = (w.L + page_size - 1) // page_size
     perm = np.random.Generator(np.random.PCG64([w.seed, 23])).permutation(w.B * max_pages)
     kp = torch.empty((w.B * max_pages, page_size, w.Hkv, w.D), dtype=k.dtype, device="cuda")
@@ -277,17 +281,28 @@ def bench_chunk(torch, jl, args, w, x, page_size=256):
         kp[idx] = k[b].view(max_pages, page_size, w.Hkv, w.D)
         vp[idx] = v[b].view(max_pages, page_size, w.Hkv, w.D)
     bt = torch.from_numpy(perm.reshape(w.B, max_pages).astype(np.int32)).cuda()
+    st = jl.alloc_chunk_state(q[:, :CHUNK_LQ[-1]], k, w.w_pretrained)
+    # the state's rotated keys: every row, as the chunks before would have left them
+    jl.jl_bifocal_prefill_chunk(q[:, -1:].contiguous(), k, v, torch.empty((w.B, 1, w.Hq, w.D), dtype=torch.bfloat16,
+                                device="cuda"), None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table,
+                                workspace=st)
+    assert (st.state.G, st.state.rows) == (G, w.L)
     stream = torch.cuda.current_stream()
     res = {}
     for Lq in CHUNK_LQ:
         qc = q[:, w.L - Lq:].contiguous()
         out = torch.empty((w.B, Lq, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
-        calls = [(f"lq{Lq}_ms", lambda: jl.jl_bifocal_prefill_chunk(
-            qc, k, v, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table, workspace=ws))]
+
+        def with_state():
+            st.state.G, st.state.rows = G, w.L - Lq   # the earlier chunks rotated rows < L - Lq
+            jl.jl_bifocal_prefill_chunk(qc, k, v, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale,
+                                        table, workspace=st)
+        calls = [(f"lq{Lq}_ms", with_state)]
         if Lq == CHUNK_LQ[-1]:
+            calls.append((f"lq{Lq}_every_key_rotated_ms", lambda: jl.jl_bifocal_prefill_chunk(
+                qc, k, v, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table)))
             calls.append((f"lq{Lq}_paged_256_ms", lambda: jl.jl_bifocal_prefill_chunk_paged(
-                qc, kp, vp, bt, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table,
-                workspace=ws)))
+                qc, kp, vp, bt, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table)))
         for name, call in calls:
             call()
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -300,7 +315,7 @@ def bench_chunk(torch, jl, args, w, x, page_size=256):
             res[name] = round(ev0.elapsed_time(ev1) / args.chunk_steps, 4)
         del qc, out
     log("[bench] chunks over the 128K cache: " + ", ".join(f"{k} {v:.3f}" for k, v in res.items()))
-    del q, k, v, kp, vp, ws
+    del q, k, v, kp, vp, st
     torch.cuda.empty_cache()
     return res
 
@@ -645,7 +660,9 @@ def main():
                                          "ms_per_call": round(rms, 4), "gb_per_s": round(rgbs, 1)}
     if args.chunk_steps > 0:
         result["chunk"] = {"what": "the last Lq tokens of the workload as one chunk over all 131072 keys "
-                                   f"(Lq = {', '.join(map(str, CHUNK_LQ))}); the longest also over 256-key pages",
+                                   f"(Lq = {', '.join(map(str, CHUNK_LQ))}), rotating its own Lq new keys (the "
+                                   "rotated-key state covers the earlier rows); the longest also with every key "
+                                   "rotated and over 256-key pages",
                            **bench_chunk(torch, jl, args, w, x)}
     if not args.skip_decode:
         dw, us, gbs, bytes_step, us_median, extra = bench_decode(torch, jl, si, args)

@@ -74,6 +74,16 @@ JL_API int jl_version(void);
 JL_API int jl_device_info(int device, int* n_cu, int* max_clock_khz);
 
 /*
+ * jl_rotated_keys -- host-side state of keys kept in their remote view (a
+ * rotated-key cache, or a chunk workspace): rows 0 .. rows-1 hold their keys in the remote view under group
+ * size G.  Start from {0, 0}; the library updates it on each call.
+ */
+typedef struct jl_rotated_keys {
+    int64_t G;
+    int64_t rows;
+} jl_rotated_keys;
+
+/*
  * jl_schedule -- §3.1 Eq. (2) and the correction-angle table for §3.2 Eq. (5).
  *
  *   *G_out = max(1, ceil(L / w_pretrained)).
@@ -207,21 +217,45 @@ JL_API int jl_bifocal_prefill_unfused(const void* q, const void* k, const void* 
  *   out     [B, Lq,   Hq,  D]  out_dtype
  *   lse     [B, Hq,   Lq]      fp32, or NULL
  *
- * dtypes, D, GQA ratios, table and workspace as for jl_bifocal_prefill
- * (workspace: jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D,
- * w_pretrained) bytes).  Every key row 0..L-1 is rotated into the workspace
- * on each call, so a chunk costs one pass over the cache's keys besides its
- * attention.
+ * dtypes, D, GQA ratios and table as for jl_bifocal_prefill.  `workspace`
+ * must hold jl_bifocal_prefill_chunk_workspace(in_dtype, B, Lq, Lmax, Hq, Hkv,
+ * D, w_pretrained) bytes (NULL when that is 0).  It holds the keys in their
+ * remote view, [B, Lmax, Hkv, D] bf16 by position, and the partials of the
+ * key splits: when the chunk's query tiles are few (short chunks), each
+ * tile's keys are split over several workgroups and merged with the
+ * log-sum-exp rule (§3.3 Eq. 6 with disjoint key sets).
+ *
+ * `state` (host, may be NULL) describes the workspace's rotated keys: with
+ * state->G equal to this call's G, rows below state->rows are not rotated
+ * again, only rows state->rows .. L-1; the call then sets state to {G, L}.
+ * Pass the same workspace and state to the chunks of one sequence (start
+ * from {0, 0}, and reset to {0, 0} after rewriting cached keys below
+ * state->rows); a chunk then rotates only its own new keys, except when G
+ * changes.  With state NULL every key row 0..L-1 is rotated on each call.
+ * The cache itself is never written.
  *
  * Errors: as for jl_bifocal_prefill, plus JL_EINVAL unless
- * 1 <= Lq <= L <= Lmax <= 2^30.
+ * 1 <= Lq <= L <= Lmax <= 2^30 or if state->rows is outside [0, Lmax].
  */
 JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* out,
                              float* lse, int in_dtype, int out_dtype, int64_t B, int64_t Lq,
                              int64_t L, int64_t Lmax, int64_t Hq, int64_t Hkv, int64_t D,
                              int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale,
                              const void* table, size_t table_bytes, void* workspace,
-                             size_t workspace_bytes, void* hip_stream);
+                             size_t workspace_bytes, jl_rotated_keys* state, void* hip_stream);
+
+/*
+ * jl_bifocal_prefill_chunk_workspace -- bytes of scratch for a chunk of Lq
+ * tokens over a cache of Lcap rows per sequence (Lmax for
+ * jl_bifocal_prefill_chunk, max_pages * page_size for the paged form): the
+ * keys' remote view when G can exceed 1 (bf16 inputs, Lcap > w_pretrained),
+ * B * Lcap * Hkv * D * 2 bytes rounded up to 256, then room for the split
+ * partials of any chunk of up to Lq tokens, max(splits * Lq') * B * Hq *
+ * (D + 4) fp32 over Lq' <= Lq (none when no such chunk is split).  The same
+ * size serves every Lq' <= Lq and L <= Lcap.  Pure host call.
+ */
+JL_API int jl_bifocal_prefill_chunk_workspace(int in_dtype, int64_t B, int64_t Lq, int64_t Lcap, int64_t Hq,
+                                              int64_t Hkv, int64_t D, int64_t w_pretrained, size_t* bytes);
 
 /*
  * jl_bifocal_prefill_chunk_paged -- jl_bifocal_prefill_chunk over a paged
@@ -236,10 +270,11 @@ JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const vo
  *   out, lse         as for jl_bifocal_prefill_chunk
  *
  * page_size must be a positive multiple of 128 (a 128-key tile never
- * crosses a page) and max_pages * page_size >= L.  The workspace is the
- * prefill's (jl_bifocal_prefill_workspace(JL_BF16, B, L, Hkv, D,
- * w_pretrained) bytes); the keys in their remote view go there laid out by
- * position, not by page.  Results are bit-identical to
+ * crosses a page) and L <= max_pages * page_size <= 2^30.  The workspace
+ * holds jl_bifocal_prefill_chunk_workspace(JL_BF16, B, Lq, max_pages *
+ * page_size, Hq, Hkv, D, w_pretrained) bytes; the keys in their remote view
+ * go there laid out by position, not by page, and `state` works as for
+ * jl_bifocal_prefill_chunk.  Results are bit-identical to
  * jl_bifocal_prefill_chunk over the same keys held contiguously.  A block
  * table entry outside [0, n_pages) is never followed: every output row whose
  * workgroup needs that page (at least every row at or after the page's first
@@ -247,8 +282,8 @@ JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const vo
  *
  * Errors: as for jl_bifocal_prefill_chunk, plus JL_EINVAL for a NULL or
  * misaligned block_table, a page_size that is not a positive multiple of 128,
- * n_pages < 1 or max_pages * page_size < L; in_dtype other than JL_BF16 ->
- * JL_EUNSUPPORTED.
+ * n_pages < 1 or max_pages * page_size outside [L, 2^30]; in_dtype other
+ * than JL_BF16 -> JL_EUNSUPPORTED.
  */
 JL_API int jl_bifocal_prefill_chunk_paged(const void* q, const void* k_pages, const void* v_pages,
                                           const int32_t* block_table, void* out, float* lse,
@@ -257,7 +292,8 @@ JL_API int jl_bifocal_prefill_chunk_paged(const void* q, const void* k_pages, co
                                           int64_t max_pages, int64_t Hq, int64_t Hkv, int64_t D,
                                           int64_t w0, int64_t w_pretrained, double rope_base,
                                           float sm_scale, const void* table, size_t table_bytes,
-                                          void* workspace, size_t workspace_bytes, void* hip_stream);
+                                          void* workspace, size_t workspace_bytes, jl_rotated_keys* state,
+                                          void* hip_stream);
 
 /*
  * jl_bifocal_decode_workspace -- bytes of fp32 scratch that jl_bifocal_decode
@@ -372,16 +408,6 @@ JL_API int jl_bifocal_decode_paged(const void* q, const void* k_pages, const voi
                             int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
                             size_t table_bytes, void* workspace, size_t workspace_bytes,
                             void* hip_stream);
-
-/*
- * jl_rotated_keys -- host-side state of a rotated-key cache: the rows
- * 0 .. rows-1 of the cache hold their keys in the remote view under group
- * size G.  Start from {0, 0}; the library updates it on each call.
- */
-typedef struct jl_rotated_keys {
-    int64_t G;
-    int64_t rows;
-} jl_rotated_keys;
 
 /*
  * jl_bifocal_decode_rkc -- jl_bifocal_decode with a rotated-key cache: the

@@ -30,10 +30,11 @@ def test_exports_every_declared_symbol():
                            "jl_bifocal_prefill_chunk_paged", "jl_bifocal_decode_rkc", "jl_fi_table",
                            "jl_fi_table_fill_host", "jl_bifocal_prefill_fi", "jl_bifocal_decode_fi",
                            "jl_rope_interleaved_to_half", "jl_bifocal_decode_unfused_workspace",
-                           "jl_bifocal_decode_unfused", "jl_device_info", "jl_bifocal_decode_noalloc"])
+                           "jl_bifocal_decode_unfused", "jl_device_info", "jl_bifocal_decode_noalloc",
+                           "jl_bifocal_prefill_chunk_workspace"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 10
+    assert jl.jl_version() == 11
 
 
 def test_schedule_golden_and_table_size():
@@ -166,15 +167,17 @@ def _chunk(**over):
     return jl.lib.jl_bifocal_prefill_chunk(a["q"], a["k"], a["v"], a["out"], a["lse"], a["i"], a["o"], a["B"],
                                            a["Lq"], a["L"], a["Lmax"], a["Hq"], a["Hkv"], a["D"], a["w0"],
                                            a["wp"], a["base"], a["sc"], a["table"], a["tb"], a["ws"], a["wsb"],
-                                           None)
+                                           a.get("state"), None)
 
 
 @pytest.mark.parametrize("over,code", [
     (dict(Lq=0), jl.JL_EINVAL), (dict(Lq=601), jl.JL_EINVAL), (dict(Lmax=599), jl.JL_EINVAL),
     (dict(L=0), jl.JL_EINVAL), (dict(q=None), jl.JL_EINVAL), (dict(out=FAKE + 2), jl.JL_EINVAL),
     (dict(D=96), jl.JL_EUNSUPPORTED), (dict(Hq=32, Hkv=2), jl.JL_EUNSUPPORTED), (dict(tb=100), jl.JL_ESPACE),
-    (dict(ws=None), jl.JL_ESPACE), (dict(wsb=600 * 2 * 128 * 2 - 1), jl.JL_ESPACE),
+    (dict(ws=None), jl.JL_ESPACE), (dict(wsb=700 * 2 * 128 * 2 - 1), jl.JL_ESPACE),
     (dict(i=jl.JL_F32, o=jl.JL_BF16), jl.JL_EUNSUPPORTED), (dict(Lmax=(1 << 30) + 1), jl.JL_EINVAL),
+    (dict(state=ctypes.pointer(jl.JLRotatedKeys(4, 701))), jl.JL_EINVAL),
+    (dict(state=ctypes.pointer(jl.JLRotatedKeys(4, -1))), jl.JL_EINVAL),
 ])
 def test_prefill_chunk_validation(over, code):
     assert _chunk(**over) == code
@@ -189,7 +192,7 @@ def _chunk_paged(**over):
     return jl.lib.jl_bifocal_prefill_chunk_paged(a["q"], a["k"], a["v"], a["bt"], a["out"], a["lse"], a["i"],
                                                  a["o"], a["B"], a["Lq"], a["L"], a["npg"], a["ps"], a["mp"],
                                                  a["Hq"], a["Hkv"], a["D"], a["w0"], a["wp"], a["base"], a["sc"],
-                                                 a["table"], a["tb"], a["ws"], a["wsb"], None)
+                                                 a["table"], a["tb"], a["ws"], a["wsb"], a.get("state"), None)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -198,7 +201,8 @@ def _chunk_paged(**over):
     (dict(mp=4), jl.JL_EINVAL), (dict(mp=0), jl.JL_EINVAL), (dict(Lq=0), jl.JL_EINVAL),
     (dict(Lq=601), jl.JL_EINVAL), (dict(q=None), jl.JL_EINVAL), (dict(D=96), jl.JL_EUNSUPPORTED),
     (dict(i=jl.JL_F32, o=jl.JL_F32), jl.JL_EUNSUPPORTED), (dict(tb=100), jl.JL_ESPACE),
-    (dict(ws=None), jl.JL_ESPACE), (dict(wsb=600 * 2 * 128 * 2 - 1), jl.JL_ESPACE),
+    (dict(ws=None), jl.JL_ESPACE), (dict(wsb=640 * 2 * 128 * 2 - 1), jl.JL_ESPACE),
+    (dict(mp=(1 << 23) + 1), jl.JL_EINVAL),
 ])
 def test_prefill_chunk_paged_validation(over, code):
     assert _chunk_paged(**over) == code
@@ -511,3 +515,45 @@ def test_decode_noalloc_validation_and_scratch_limit():
     assert call(args(D=96)) == jl.JL_EUNSUPPORTED
     assert call(args(B=1024, L=64, Lmax=64, Hq=64, Hkv=8)) == jl.JL_ESPACE
     assert "scratch" in jl.jl_last_error()
+
+
+def test_prefill_chunk_workspace_size():
+    """Rotated keys [B, Lcap, Hkv, D] bf16 (when G can exceed 1), rounded up to
+    256 bytes, then the partials of the key splits: a chunk whose query tiles
+    give under 128 workgroups is split over ~512 (>= 4 key tiles each, <= 64)."""
+    up = lambda x: (x + 255) // 256 * 256
+    # 131072-row cache, 16-token chunk, 32/8 heads: 8 workgroups -> 64 splits
+    n = jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 16, 131072, 32, 8, 128, 32768)
+    assert n == up(131072 * 8 * 128 * 2) + 64 * 16 * 32 * 132 * 4
+    # a 4096-token chunk fills 512 workgroups and is not split, but a workspace for
+    # chunks of up to 4096 tokens has room for the splits of shorter ones: the
+    # largest need is 5 splits x 960 rows (120 workgroups)
+    def need_rows(lq_max, keys, R=4, Hkv=8):
+        best = 0
+        for lq in range(1, lq_max + 1):
+            wgs = -(-lq // (256 // R)) * Hkv
+            tiles = -(-keys // 128)
+            if wgs >= 128 or tiles < 8:
+                continue
+            s = min(-(-512 // wgs), tiles // 4, 64)
+            best = max(best, s * lq if s > 1 else 0)
+        return best
+    n = jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 4096, 131072, 32, 8, 128, 32768)
+    assert need_rows(4096, 131072) == 5 * 960
+    assert n == up(131072 * 8 * 128 * 2) + 5 * 960 * 32 * 132 * 4
+    # up to 256 tokens: room for the largest need, 22 splits x 192 rows (24 workgroups
+    # at 129..192 tokens; 64 tokens need 64 x 64, 256 tokens 16 x 256)
+    n = jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 256, 131072, 32, 8, 128, 32768)
+    assert n == up(131072 * 8 * 128 * 2) + 22 * 192 * 32 * 132 * 4
+    # the size never shrinks as the chunk bound grows
+    sizes = [jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, lq, 1500, 8, 2, 128, 400) for lq in range(1, 300)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+    # a cache within the pretrained window needs no rotated keys: 9 key tiles, 2 splits
+    assert jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 16, 1100, 32, 8, 128, 32768) == \
+        2 * 16 * 32 * 132 * 4
+    # fewer than 8 key tiles: no split
+    assert jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 16, 896, 32, 8, 128, 32768) == 0
+    # fp32 inputs: the generic kernel rotates its keys itself and does not split
+    assert jl.jl_bifocal_prefill_chunk_workspace(jl.JL_F32, 1, 16, 131072, 32, 8, 128, 32768) == 0
+    with pytest.raises(jl.JetLongError):
+        jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 17, 16, 32, 8, 128, 32768)

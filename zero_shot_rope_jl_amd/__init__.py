@@ -19,4 +19,5 @@ from .binding import (  # noqa: F401
     jl_bifocal_decode_workspace, jl_table_fill_host, alloc_table, alloc_prefill_workspace,
     alloc_decode_workspace, jl_bifocal_decode_unfused, jl_bifocal_decode_unfused_workspace,
     alloc_decode_unfused_workspace, jl_device_info, jl_bifocal_decode_noalloc,
+    jl_bifocal_prefill_chunk_workspace, ChunkState, alloc_chunk_state,
 )

@@ -59,14 +59,18 @@ def _load():
     L.jl_bifocal_prefill_unfused.restype = ctypes.c_int
     L.jl_bifocal_prefill_unfused.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                              i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp, sz, vp]
+    rk = ctypes.POINTER(JLRotatedKeys)
     L.jl_bifocal_prefill_chunk_paged.restype = ctypes.c_int
     L.jl_bifocal_prefill_chunk_paged.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64,
                                                  i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double,
-                                                 ctypes.c_float, vp, sz, vp, sz, vp]
+                                                 ctypes.c_float, vp, sz, vp, sz, rk, vp]
     L.jl_bifocal_prefill_chunk.restype = ctypes.c_int
     L.jl_bifocal_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                            i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_float, vp, sz, vp,
-                                           sz, vp]
+                                           sz, rk, vp]
+    L.jl_bifocal_prefill_chunk_workspace.restype = ctypes.c_int
+    L.jl_bifocal_prefill_chunk_workspace.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
+                                                     ctypes.POINTER(sz)]
     L.jl_bifocal_decode_workspace.restype = ctypes.c_int
     L.jl_bifocal_decode_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(sz)]
     L.jl_bifocal_decode.restype = ctypes.c_int
@@ -305,14 +309,58 @@ def jl_bifocal_prefill_unfused(q, k, v, out, lse, w0: int, w_pretrained: int, ro
     return out, lse
 
 
+def jl_bifocal_prefill_chunk_workspace(in_dtype: int, B: int, Lq: int, Lcap: int, Hq: int, Hkv: int, D: int,
+                                       w_pretrained: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.jl_bifocal_prefill_chunk_workspace(in_dtype, B, Lq, Lcap, Hq, Hkv, D, w_pretrained, ctypes.byref(n)))
+    return n.value
+
+
+class ChunkState:
+    """A chunk workspace with its rotated-key state (jl_rotated_keys): pass
+    the same one to the chunks of one sequence so that each chunk rotates
+    only its new keys.  Call reset() after rewriting cached keys."""
+
+    def __init__(self, nbytes: int, device="cuda"):
+        torch = _torch()
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+        self.state = JLRotatedKeys(0, 0)
+
+    def reset(self):
+        self.state.G = 0
+        self.state.rows = 0
+
+
+def alloc_chunk_state(q, k_cache, w_pretrained: int, Lq_max: int | None = None, device="cuda"):
+    """ChunkState for chunks of up to Lq_max tokens (default: q's) over k_cache [B, Lcap, Hkv, D]."""
+    B, Lq, Hq, D = q.shape
+    Lcap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    n = jl_bifocal_prefill_chunk_workspace(_dtype_code(q), B, Lq_max or Lq, Lcap, Hq, Hkv, D, w_pretrained)
+    return ChunkState(n, device)
+
+
+def _chunk_ws(workspace, nbytes, device, stream):
+    """(device buffer, state pointer) of a chunk call's workspace argument: a
+    ChunkState, a plain tensor (no state: every key row rotated), or None (a
+    buffer for this call on its stream)."""
+    if isinstance(workspace, ChunkState):
+        return workspace.buf, ctypes.byref(workspace.state)
+    if workspace is None and nbytes:
+        workspace = _scratch(nbytes, device, stream)
+    return workspace, None
+
+
 def jl_bifocal_prefill_chunk(q, k_cache, v_cache, out, lse, L: int, w0: int, w_pretrained: int,
                              rope_base: float, sm_scale: float, table, workspace=None, stream=None):
     """q [B,Lq,Hq,D] at positions L-Lq..L-1, caches [B,Lmax,Hkv,D] with rows < L valid,
-    out [B,Lq,Hq,D], lse [B,Hq,Lq] fp32 or None.  `workspace` as for jl_bifocal_prefill
-    (sized for L keys); when None and some is needed, one is allocated through torch."""
-    _need_device(q, k_cache, v_cache, out, lse, table, workspace)
+    out [B,Lq,Hq,D], lse [B,Hq,Lq] fp32 or None.  `workspace`: a ChunkState (see
+    alloc_chunk_state; keeps the rotated keys across the chunks of a sequence), a
+    device tensor of jl_bifocal_prefill_chunk_workspace bytes, or None (allocated
+    through torch for this call)."""
     B, Lq, Hq, D = q.shape
     Bk, Lmax, Hkv, Dk = k_cache.shape
+    buf0 = workspace.buf if isinstance(workspace, ChunkState) else workspace
+    _need_device(q, k_cache, v_cache, out, lse, table, buf0)
     if Bk != B or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("caches must be [B, Lmax, Hkv, D] matching q")
     if tuple(out.shape) != (B, Lq, Hq, D):
@@ -321,14 +369,13 @@ def jl_bifocal_prefill_chunk(q, k_cache, v_cache, out, lse, L: int, w0: int, w_p
         raise ValueError("lse must be float32 [B, Hq, Lq]")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q and the caches must share a dtype")
-    if workspace is None:
-        n = jl_bifocal_prefill_workspace(_dtype_code(q), B, L, Hkv, D, w_pretrained)
-        workspace = _scratch(n, q.device, stream) if n else None
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    n = jl_bifocal_prefill_chunk_workspace(_dtype_code(q), B, Lq, Lmax, Hq, Hkv, D, w_pretrained)
+    buf, st = _chunk_ws(workspace, n, q.device, stream)
+    ws_bytes = 0 if buf is None else buf.numel() * buf.element_size()
     _check(lib.jl_bifocal_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
                                         _dtype_code(q), _dtype_code(out), B, Lq, L, Lmax, Hq, Hkv, D, w0,
                                         w_pretrained, rope_base, sm_scale, _ptr(table),
-                                        table.numel() * table.element_size(), _ptr(workspace), ws_bytes,
+                                        table.numel() * table.element_size(), _ptr(buf), ws_bytes, st,
                                         _stream(stream)))
     return out, lse
 
@@ -336,12 +383,13 @@ def jl_bifocal_prefill_chunk(q, k_cache, v_cache, out, lse, L: int, w0: int, w_p
 def jl_bifocal_prefill_chunk_paged(q, k_pages, v_pages, block_table, out, lse, L: int, w0: int, w_pretrained: int,
                                    rope_base: float, sm_scale: float, table, workspace=None, stream=None):
     """q [B,Lq,Hq,D] bf16 at positions L-Lq..L-1; pages [n_pages, page_size, Hkv, D] bf16;
-    block_table [B, max_pages] int32; out [B,Lq,Hq,D]; lse [B,Hq,Lq] fp32 or None.  `workspace`
-    as for jl_bifocal_prefill (sized for L keys); allocated through torch when None and needed."""
+    block_table [B, max_pages] int32; out [B,Lq,Hq,D]; lse [B,Hq,Lq] fp32 or None.
+    `workspace` as for jl_bifocal_prefill_chunk, sized for max_pages * page_size rows."""
     torch = _torch()
-    _need_device(q, k_pages, v_pages, block_table, out, lse, table, workspace)
     B, Lq, Hq, D = q.shape
     n_pages, page_size, Hkv, Dk = k_pages.shape
+    buf0 = workspace.buf if isinstance(workspace, ChunkState) else workspace
+    _need_device(q, k_pages, v_pages, block_table, out, lse, table, buf0)
     if Dk != D or tuple(v_pages.shape) != tuple(k_pages.shape):
         raise ValueError("the pages must be [n_pages, page_size, Hkv, D] matching q")
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
@@ -350,15 +398,15 @@ def jl_bifocal_prefill_chunk_paged(q, k_pages, v_pages, block_table, out, lse, L
         raise ValueError("out must be [B, Lq, Hq, D]")
     if lse is not None and (tuple(lse.shape) != (B, Hq, Lq) or _dtype_code(lse) != JL_F32):
         raise ValueError("lse must be float32 [B, Hq, Lq]")
-    if workspace is None:
-        n = jl_bifocal_prefill_workspace(_dtype_code(q), B, L, Hkv, D, w_pretrained)
-        workspace = _scratch(n, q.device, stream) if n else None
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    max_pages = block_table.shape[1]
+    n = jl_bifocal_prefill_chunk_workspace(_dtype_code(q), B, Lq, max_pages * page_size, Hq, Hkv, D, w_pretrained)
+    buf, st = _chunk_ws(workspace, n, q.device, stream)
+    ws_bytes = 0 if buf is None else buf.numel() * buf.element_size()
     _check(lib.jl_bifocal_prefill_chunk_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(out),
                                               _ptr(lse), _dtype_code(q), _dtype_code(out), B, Lq, L, n_pages,
-                                              page_size, block_table.shape[1], Hq, Hkv, D, w0, w_pretrained,
-                                              rope_base, sm_scale, _ptr(table), table.numel() * table.element_size(),
-                                              _ptr(workspace), ws_bytes, _stream(stream)))
+                                              page_size, max_pages, Hq, Hkv, D, w0, w_pretrained, rope_base,
+                                              sm_scale, _ptr(table), table.numel() * table.element_size(),
+                                              _ptr(buf), ws_bytes, st, _stream(stream)))
     return out, lse
 
 

@@ -95,7 +95,7 @@ JL_API int jl_device_info(int device, int* n_cu, int* max_clock_khz) {
     return JL_OK;
 }
 
-JL_API int jl_version(void) { return 10; }
+JL_API int jl_version(void) { return 11; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -264,9 +264,95 @@ jl::PrefillParams make_prefill_params(const void* q, const void* k, const void* 
     p.rope_base = rope_base;
     p.head_dim = (int)D;
     p.krot = krot;
+    p.krot_rows = L;
+    p.rot_lo = 0;
+    p.n_ksplit = 1;
+    p.part = nullptr;
     p.mode = jl::kFused;
     p.table_key = jl::TableKey{jl::kTableMagic, 0, 0, 0.0, 0.0};
     return p;
+}
+
+// Key splits of a chunk's query tiles: when the query tiles of a chunk give
+// fewer than 128 workgroups, each one's key tiles are split over several
+// workgroups (about 512 in all, at least 4 key tiles each, at most 64
+// splits), whose partials a combine kernel merges.  bf16 inputs only.  The
+// split count grows with L, so a plan for a larger L bounds it.
+int64_t chunk_ksplit(int in_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Hq, int64_t Hkv) {
+    if (in_dtype != JL_BF16) return 1;
+    const int64_t R = Hq / Hkv, BQ = 256 / R;
+    const int64_t wgs = (Lq + BQ - 1) / BQ * Hkv * B;
+    const int64_t tiles = (L + 127) / 128;
+    if (wgs >= 128 || tiles < 8) return 1;
+    int64_t s = (512 + wgs - 1) / wgs;
+    if (s > tiles / 4) s = tiles / 4;
+    if (s > jl::kMaxKSplit) s = jl::kMaxKSplit;
+    return s < 1 ? 1 : s;
+}
+
+// Workspace of chunk calls of up to Lq tokens over a cache of Lcap rows per
+// sequence: the keys' remote view [B, Lcap, Hkv, D] bf16 by position (bf16
+// inputs, when a G > 1 is possible), then room for the split partials of any
+// such call.
+struct ChunkLayout {
+    size_t krot, part, total;
+};
+
+// The partial rows (split x query row) of the largest need among chunks of
+// up to Lq tokens over up to Lcap keys.  The split count falls as the query
+// tiles grow, so the need peaks at the end of a run of Lq with the same tile
+// count; past 128 workgroups nothing is split.
+int64_t chunk_part_rows(int in_dtype, int64_t B, int64_t Lq, int64_t Lcap, int64_t Hq, int64_t Hkv) {
+    const int64_t BQ = 256 / (Hq / Hkv);
+    int64_t best = 0;
+    for (int64_t t = 1; (t - 1) * BQ < Lq; ++t) {
+        const int64_t lq = t * BQ < Lq ? t * BQ : Lq;
+        if (t * Hkv * B >= 128) break;
+        const int64_t s = chunk_ksplit(in_dtype, B, lq, Lcap, Hq, Hkv);
+        if (s > 1 && s * lq > best) best = s * lq;
+    }
+    return best;
+}
+
+ChunkLayout chunk_layout(int in_dtype, int64_t B, int64_t Lq, int64_t Lcap, int64_t Hq, int64_t Hkv, int64_t D,
+                         int64_t w_pretrained) {
+    ChunkLayout c{};
+    const bool rotated = in_dtype == JL_BF16 && group_size(Lcap, w_pretrained) > 1;
+    c.krot = 0;
+    c.part = jl::decode_align(rotated ? (size_t)B * (size_t)Lcap * (size_t)Hkv * (size_t)D * 2u : 0u);
+    const int64_t rows = chunk_part_rows(in_dtype, B, Lq, Lcap, Hq, Hkv);
+    c.total = c.part + (size_t)rows * (size_t)B * (size_t)Hq * (size_t)(D + 4) * sizeof(float);
+    return c;
+}
+
+// Chunk set-up shared by the contiguous and paged forms: workspace checks,
+// the rotated keys (only the rows the state does not cover are rotated) and
+// the key splits.  Updates *state when given.
+int setup_chunk(const char* who, jl::PrefillParams& p, int in_dtype, int64_t Lcap, int64_t D, int64_t w_pretrained,
+                void* workspace, size_t workspace_bytes, jl_rotated_keys* state) {
+    const ChunkLayout c = chunk_layout(in_dtype, p.B, p.Lq, Lcap, p.Hq, p.Hkv, D, w_pretrained);
+    if (c.total > 0 && (!workspace || workspace_bytes < c.total))
+        return fail(JL_ESPACE, "%s: workspace holds %zu bytes, %zu needed", who,
+                    workspace ? workspace_bytes : (size_t)0, c.total);
+    if (state && (state->rows < 0 || state->rows > Lcap))
+        return fail(JL_EINVAL, "%s: state.rows must be in [0, %lld] (got %lld)", who, (long long)Lcap,
+                    (long long)state->rows);
+    char* w = static_cast<char*>(workspace);
+    p.krot = c.part > 0 ? w + c.krot : nullptr;
+    p.krot_rows = Lcap;
+    p.n_ksplit = (int)chunk_ksplit(in_dtype, p.B, p.Lq, p.L, p.Hq, p.Hkv);
+    p.part = p.n_ksplit > 1 ? reinterpret_cast<float*>(w + c.part) : nullptr;
+    p.rot_lo = 0;
+    if (state && p.G > 1) {
+        // rows below state->rows already hold their remote view under this G
+        if (state->G == p.G && state->rows <= p.L) p.rot_lo = state->rows;
+        state->G = p.G;
+        state->rows = p.L;
+    } else if (state) {
+        state->G = p.G;
+        state->rows = 0;   // G = 1: nothing rotated
+    }
+    return JL_OK;
 }
 
 // Both fused prefill entry points.
@@ -274,20 +360,24 @@ int prefill_impl(const char* who, const void* q, const void* k, const void* v, v
                  int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Lkv, int64_t Hq, int64_t Hkv, int64_t D,
                  int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale, const void* table,
                  size_t table_bytes, void* workspace, size_t workspace_bytes, void* hip_stream,
-                 const FiArgs* fi = nullptr) {
+                 const FiArgs* fi = nullptr, bool chunk = false, jl_rotated_keys* state = nullptr) {
     g_err.clear();
     if (int rc = check_prefill(who, q, k, v, out, lse, in_dtype, out_dtype, B, Lq, L, Lkv, Hq, Hkv, D, w0,
                                w_pretrained, rope_base, sm_scale, table, table_bytes, workspace, fi != nullptr))
         return rc;
     if (fi)
         if (int rc = check_fi_ramp(fi->alpha, fi->beta)) return rc;
-    size_t ws_need = 0;
-    jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D, w_pretrained, &ws_need);
-    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
-        return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : (size_t)0,
-                    ws_need);
+    if (!chunk) {
+        size_t ws_need = 0;
+        jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D, w_pretrained, &ws_need);
+        if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
+            return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                        ws_need);
+    }
     jl::PrefillParams p = make_prefill_params(q, k, v, out, lse, B, Lq, L, Lkv, Hq, Hkv, D, w0, w_pretrained,
                                               rope_base, sm_scale, table, workspace);
+    if (chunk)
+        if (int rc = setup_chunk(who, p, in_dtype, Lkv, D, w_pretrained, workspace, workspace_bytes, state)) return rc;
     if (fi) {
         p.G = fi_group(L, w_pretrained);
         p.table_key = jl::TableKey{jl::kTableMagicFI, L, w_pretrained, fi->alpha, fi->beta};
@@ -348,14 +438,29 @@ JL_API int jl_bifocal_prefill_fi(const void* q, const void* k, const void* v, vo
                         &fi);
 }
 
+JL_API int jl_bifocal_prefill_chunk_workspace(int in_dtype, int64_t B, int64_t Lq, int64_t Lcap, int64_t Hq,
+                                              int64_t Hkv, int64_t D, int64_t w_pretrained, size_t* bytes) {
+    g_err.clear();
+    if (!bytes) return fail(JL_EINVAL, "bytes is NULL");
+    if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lq > Lcap || Lcap > kMaxLen)
+        return fail(JL_EINVAL, "need B, Hq, Hkv >= 1 and 1 <= Lq <= Lcap <= 2^30");
+    if (Hq % Hkv != 0) return fail(JL_EINVAL, "Hq %% Hkv != 0 (%lld, %lld)", (long long)Hq, (long long)Hkv);
+    if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1 (got %lld)", (long long)w_pretrained);
+    if (D != 64 && D != 128) return fail(JL_EUNSUPPORTED, "head_dim %lld not supported", (long long)D);
+    if (in_dtype != JL_F32 && in_dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "unknown in_dtype %d", in_dtype);
+    *bytes = chunk_layout(in_dtype, B, Lq, Lcap, Hq, Hkv, D, w_pretrained).total;
+    return JL_OK;
+}
+
 JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
                                     int in_dtype, int out_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Lmax,
                                     int64_t Hq, int64_t Hkv, int64_t D, int64_t w0, int64_t w_pretrained,
                                     double rope_base, float sm_scale, const void* table, size_t table_bytes,
-                                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+                                    void* workspace, size_t workspace_bytes, jl_rotated_keys* state,
+                                    void* hip_stream) {
     return prefill_impl("prefill_chunk", q, k_cache, v_cache, out, lse, in_dtype, out_dtype, B, Lq, L, Lmax, Hq,
                         Hkv, D, w0, w_pretrained, rope_base, sm_scale, table, table_bytes, workspace,
-                        workspace_bytes, hip_stream);
+                        workspace_bytes, hip_stream, nullptr, true, state);
 }
 
 JL_API int jl_bifocal_prefill_unfused_workspace(int in_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv,
@@ -423,7 +528,7 @@ JL_API int jl_bifocal_prefill_chunk_paged(const void* q, const void* k_pages, co
                                           int64_t page_size, int64_t max_pages, int64_t Hq, int64_t Hkv, int64_t D,
                                           int64_t w0, int64_t w_pretrained, double rope_base, float sm_scale,
                                           const void* table, size_t table_bytes, void* workspace,
-                                          size_t workspace_bytes, void* hip_stream) {
+                                          size_t workspace_bytes, jl_rotated_keys* state, void* hip_stream) {
     const char* who = "prefill_chunk_paged";
     g_err.clear();
     if (!block_table) return fail(JL_EINVAL, "%s: block_table must be non-NULL", who);
@@ -435,17 +540,17 @@ JL_API int jl_bifocal_prefill_chunk_paged(const void* q, const void* k_pages, co
     if (page_size < 128 || page_size % 128 != 0 || page_size > kMaxLen)
         return fail(JL_EINVAL, "%s: page_size must be a positive multiple of 128 (got %lld)", who,
                     (long long)page_size);
-    if (n_pages < 1 || max_pages < 1 || max_pages > kMaxLen || max_pages * page_size < L)
-        return fail(JL_EINVAL, "%s: need n_pages >= 1 and max_pages * page_size >= L (%lld, %lld, L=%lld)", who,
+    if (n_pages < 1 || max_pages < 1 || max_pages > kMaxLen || max_pages * page_size < L ||
+        max_pages * page_size > kMaxLen)
+        return fail(JL_EINVAL, "%s: need n_pages >= 1 and L <= max_pages * page_size <= 2^30 (%lld, %lld, L=%lld)", who,
                     (long long)n_pages, (long long)max_pages, (long long)L);
     if (in_dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "%s reads a bf16 cache only", who);
-    size_t ws_need = 0;
-    jl_bifocal_prefill_workspace(in_dtype, B, L, Hkv, D, w_pretrained, &ws_need);
-    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
-        return fail(JL_ESPACE, "workspace holds %zu bytes, %zu needed", workspace ? workspace_bytes : (size_t)0,
-                    ws_need);
     jl::PrefillParams p = make_prefill_params(q, k_pages, v_pages, out, lse, B, Lq, L, L, Hq, Hkv, D, w0,
                                               w_pretrained, rope_base, sm_scale, table, workspace);
+    // the rotated keys are kept by position for max_pages * page_size rows
+    if (int rc = setup_chunk(who, p, in_dtype, max_pages * page_size, D, w_pretrained, workspace, workspace_bytes,
+                             state))
+        return rc;
     p.block_table = block_table;
     p.page_size = page_size;
     p.max_pages = max_pages;

@@ -31,9 +31,19 @@ struct PrefillParams {
     // 0: compute every row.  1: recompute only the workgroups whose rows carry
     // the non-finite-row mark left by the bf16 kernel (NaN in element 0).
     int fixup;
-    // bf16 kernel only: B*L*Hkv*D bf16 workspace that receives the keys in
-    // their corrected view when G > 1 (laid out like k)
+    // bf16 kernel only: workspace that receives the keys in their corrected
+    // view when G > 1, [B, krot_rows, Hkv, D] bf16 by position (krot_rows >=
+    // L); rows [rot_lo, L) are rotated by the call, rows below rot_lo are
+    // already there (a caller-kept state, chunked calls only)
     void* krot;
+    int64_t krot_rows;
+    int64_t rot_lo;
+    // bf16 kernel only: the key tiles of each query tile are split over
+    // n_ksplit workgroups (1: no split), which leave fp32 partials (acc[D],
+    // max in log2 units, sum, 2 pad) [n_ksplit, B, Lq, Hq, D + 4] in `part`
+    // for the combine kernel (rows 16-byte aligned)
+    int n_ksplit;
+    float* part;
     // which pairs and which view (Jet-Long §3.3 Eq. 6): kFused is the bifocal
     // rule in one softmax; the other three are the separate passes of the
     // inclusion-exclusion merge, each one plain masked attention in one view
@@ -175,6 +185,9 @@ struct MergeParams {
     float* lse;           // [B, Hq, Lq] or null
     int64_t B, Lq, Hq, D;
 };
+
+// Most key splits of one query tile in a chunked prefill.
+constexpr int kMaxKSplit = 64;
 
 hipError_t launch_prefill(const PrefillParams& p, int in_dtype, int out_dtype, hipStream_t stream);
 hipError_t launch_ie_merge(const MergeParams& p, int out_dtype, hipStream_t stream);

@@ -122,6 +122,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     bid /= (int)p.Hkv;
     const int b = (int)(bid % p.B);
     bid /= (int)p.B;
+    const int ks = bid % p.n_ksplit;   // key split of this query tile (0 when unsplit)
+    bid /= p.n_ksplit;
     const int qt = p.n_qtiles - 1 - bid;
 
     // positions: keys 0..L-1; queries q_off..L-1, stored as rows 0..Lq-1
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // keys in their corrected view (only read by remote tiles, which exist only
     // when G > 1), laid out like k with L rows per batch entry
     const __bf16* __restrict__ krbase =
-        G > 1 ? static_cast<const __bf16*>(p.krot) + (int64_t)b * L * kv_row + (int64_t)g * D : kbase;
+        G > 1 ? static_cast<const __bf16*>(p.krot) + (int64_t)b * p.krot_rows * kv_row + (int64_t)g * D : kbase;
 
     if (tid == 0) {
         const TableHeader* th = p.table;
@@ -170,10 +172,17 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     }
     __syncthreads();
     if (s_bad) {
-        // The table does not belong to this (D, rope_base, L): poison the output.
+        // The table does not belong to this (D, rope_base, L): poison the output
+        // (a split marks its partials; the combine and fixup passes then poison
+        // the rows).
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             if (!qok[j]) continue;
+            if (p.n_ksplit > 1) {
+                if (hh == 0)
+                    p.part[((((int64_t)ks * p.B + b) * Lq + (my_q[j] - q_off)) * Hq + head[j]) * (D + 4) + D] = NAN;
+                continue;
+            }
             const int64_t o = (((int64_t)b * Lq + (my_q[j] - q_off)) * Hq + head[j]) * D;
             for (int d = hh; d < D; d += 2) {
                 if constexpr (OUT_BF16) static_cast<__bf16*>(p.out)[o + d] = (__bf16)NAN;
@@ -211,6 +220,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         }
     }
     const int NP = nR + (nkt - nL0);
+    // this workgroup's share of the tile list: a contiguous run, so a split
+    // walks its tiles in the unsplit order
+    const int pi_lo = (int)((int64_t)NP * ks / p.n_ksplit);
+    const int pi_hi = (int)((int64_t)NP * (ks + 1) / p.n_ksplit);
 
     // ---- query fragments ---------------------------------------------------------
     // B operand, fragment c = dims 16c + 8hh + [0, 8), multiplied by
@@ -527,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // tile pi computes from buffer pi & 1 (= buf) and stages tile pi + 1 into the other
     auto tile = [&](int pi, auto buf) __attribute__((always_inline)) {
         using Other = std::integral_constant<int, 1 - decltype(buf)::value>;
-        if (pi == nR && nR > 0) load_q(false);   // the local phase starts: stored Q
+        if (pi == nR && pi > pi_lo) load_q(false);   // the local phase starts: stored Q
         // the first score MFMAs go out right after the barrier, ahead of the
         // tile's scalar set-up: a region with S(0) only
         f32x16 s0[NJ];
@@ -537,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
             region(std::false_type{}, std::true_type{}, std::false_type{}, decltype(buf)::value ? sK1 : sK0,
                    decltype(buf)::value ? sV1 : sV0, 0, 0, noP, s0, noS, noP);
         }
-        const int pn = pi + 1 < NP ? pi + 1 : pi;   // the last tile refills the idle buffer
+        const int pn = pi + 1 < pi_hi ? pi + 1 : pi;   // the last tile refills the idle buffer
         stage_load_k(pn, Other{});
         const bool rem = pi < nR;
         const int k0 = tile_k0(pi);
@@ -555,23 +568,55 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         __syncthreads();
     };
 
-    stage_load_k(0, Buf0{});
-    stage_load_v(0, Buf0{});
+    if (pi_lo < pi_hi) {
+        stage_load_k(pi_lo, Buf0{});
+        stage_load_v(pi_lo, Buf0{});
+    }
     wait_vmem();
     __syncthreads();
-    load_q(nR > 0);
-    int pi = 0;
-    for (; pi + 1 < NP; pi += 2) {
+    load_q(pi_lo < nR);
+    int pi = pi_lo;
+    for (; pi + 1 < pi_hi; pi += 2) {
         tile(pi, Buf0{});
         tile(pi + 1, Buf1{});
     }
-    if (pi < NP) tile(pi, Buf0{});
+    if (pi < pi_hi) tile(pi, Buf0{});
 
     // ---- epilogue ---------------------------------------------------------------
     // A row whose probabilities overflowed (a later score above its fixed
     // reference by more than the fp32 exponent range) comes out non-finite;
     // it is marked with NaN in element 0 for the fixup pass, which recomputes
     // its workgroup with a running max.
+    if (p.n_ksplit > 1) {
+        // a split leaves its unnormalised partial (acc, max, sum) per row; a
+        // row whose values overflowed (or that read a bad page) carries NaN
+        // as its max, which the combine kernel turns into the fixup mark
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const float l_tot = l_run[j] + __shfl_xor(l_run[j], 32);
+            bool finite = l_tot < INFINITY;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) finite = finite && fabsf(acc[j][db][i]) < INFINITY;
+            const bool row_ok = finite && __shfl_xor((int)finite, 32) && !bad_page;
+            if (!qok[j]) continue;
+            float* o = p.part + ((((int64_t)ks * p.B + b) * Lq + (my_q[j] - q_off)) * Hq + head[j]) * (D + 4);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d0 = db * 32 + a4 * 8 + hh * 4;
+                    *reinterpret_cast<f32x4*>(o + d0) = f32x4{acc[j][db][4 * a4], acc[j][db][4 * a4 + 1],
+                                                              acc[j][db][4 * a4 + 2], acc[j][db][4 * a4 + 3]};
+                }
+            if (hh == 0) {
+                o[D] = row_ok ? m_ref[j] : NAN;
+                o[D + 1] = l_tot;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const float l_tot = l_run[j] + __shfl_xor(l_run[j], 32);
@@ -609,36 +654,41 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     }
 }
 
-// The keys in their corrected view (§3.2 Eq. 5 applied to K): row k of every
-// (batch, KV head) rotated by its correction offset, table row n(k) = k -
-// floor(k/G), rounded to bf16.  One thread per 8 rotation pairs of a row;
-// HBM-bound (one read and one write of K, table rows shared by the KV heads
-// of a position through L2).
+// The keys in their corrected view (§3.2 Eq. 5 applied to K): rows
+// rot_lo .. rot_lo + nrows - 1 of every (batch, KV head) rotated by their
+// correction offset, table row n(k) = k - floor(k/G), rounded to bf16, into
+// [B, krot_rows, Hkv, D] by position.  One thread per 8 rotation pairs of a
+// row; HBM-bound (one read and one write of K, table rows shared by the KV
+// heads of a position through L2).
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kr,
-                                                          const float2* __restrict__ TF, int64_t n_items, int64_t L,
-                                                          int64_t Lkv, int Hkv, int64_t G, PrefillParams pp) {
+                                                          const float2* __restrict__ TF, int64_t n_items,
+                                                          int64_t nrows, int64_t Lkv, int Hkv, int64_t G,
+                                                          PrefillParams pp) {
     constexpr int HALF = D / 2;
     constexpr int CPR = HALF / 8;   // 8-pair items per row
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= n_items) return;
-    const int64_t row = t / CPR;    // (b, position, head) of the output, head fastest
+    const int64_t item = t / CPR;   // (b, position - rot_lo, head), head fastest
     const int c = (int)(t % CPR);
-    const int64_t bp = row / Hkv;
-    const int64_t pos = bp % L;
+    const int64_t bp = item / Hkv;
+    const int64_t pos = pp.rot_lo + bp % nrows;
     const int64_t n = pos - pos / G;
+    const int64_t bb = bp / nrows;
+    // the output: row pos of batch entry bb, [B, krot_rows, Hkv, D]
+    const int64_t row = (bb * pp.krot_rows + pos) * Hkv + item % Hkv;
     // k holds Lkv rows per batch entry (or pages), the output L
     int64_t crow;
     if constexpr (PAGED) {
         // an entry outside [0, n_pages) reads page 0; the attention kernel
         // marks the rows that use it
-        int64_t pg = pp.block_table[(bp / L) * pp.max_pages + pos / pp.page_size];
+        int64_t pg = pp.block_table[bb * pp.max_pages + pos / pp.page_size];
         pg = (pg < 0 || pg >= pp.n_pages) ? 0 : pg;
         crow = pg * pp.page_size + pos % pp.page_size;
     } else {
-        crow = (bp / L) * Lkv + pos;
+        crow = bb * Lkv + pos;
     }
-    const __bf16* src = k + (crow * Hkv + row % Hkv) * D + 8 * c;
+    const __bf16* src = k + (crow * Hkv + item % Hkv) * D + 8 * c;
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(src);
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(src + HALF);
     bf16x8 xo, yo;
@@ -659,17 +709,121 @@ __global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restri
     *reinterpret_cast<bf16x8*>(dst + HALF) = yo;
 }
 
+// Log-sum-exp merge of the key splits of each row (§3.3 Eq. 6 with disjoint
+// key sets).  One workgroup of 256 threads per (batch, row, head): thread t
+// takes 4 output dimensions (t % (D/4)) of every split s = t / (D/4) + g *
+// (256 / (D/4)), so all of a row's partials are read in one round trip, and
+// the splits' maxima, sums and weighted rows are reduced through LDS.  The
+// maxima are in log2 units; splits without keys for the row (max -inf) weigh
+// nothing.  A NaN max (overflow, bad page or table) or a non-finite result
+// writes NaN in element 0, the mark the fixup pass recomputes.  The splits
+// are summed in split order.
+constexpr int kCombThreads = 256;
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kCombThreads) void split_combine_kernel(PrefillParams p) {
+    constexpr int D4 = D / 4;
+    constexpr int SG = kCombThreads / D4;             // split groups
+    constexpr int PER = kMaxKSplit / SG;              // splits per thread at most
+    static_assert(SG * PER == kMaxKSplit, "every split has a thread");
+    __shared__ float sM[kMaxKSplit], sL[kMaxKSplit];
+    __shared__ float4 sA[SG][D4];
+    __shared__ float sRow[2];
+    const int64_t r = blockIdx.x;                     // (b, row, head), head fastest
+    const int64_t rows = p.B * p.Lq * p.Hq;
+    const int64_t stride = rows * (D + 4);            // one split's partials
+    const float* base = p.part + r * (D + 4);
+    const int t = threadIdx.x, d4 = t % D4, sg = t / D4;
+    const int n = p.n_ksplit;
+    float4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int sp = sg + u * SG;
+        v[u] = sp < n ? *reinterpret_cast<const float4*>(base + sp * stride + 4 * d4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (t < n) {
+        sM[t] = base[t * stride + D];
+        sL[t] = base[t * stride + D + 1];
+    }
+    __syncthreads();
+    if (t == 0) {
+        float M = -INFINITY;
+        bool bad = false;
+        for (int sp = 0; sp < n; ++sp) {
+            bad = bad || (sM[sp] != sM[sp]);
+            M = fmaxf(M, sM[sp]);
+        }
+        float l = 0.f;
+        for (int sp = 0; sp < n; ++sp) {
+            const float w = (sM[sp] == -INFINITY) ? 0.f : fast_exp2(sM[sp] - M);
+            sM[sp] = w;   // the split's weight from here on
+            l += w * sL[sp];
+        }
+        sRow[0] = bad ? NAN : M;
+        sRow[1] = l;
+    }
+    __syncthreads();
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int sp = sg + u * SG;
+        if (sp < n) {
+            const float w = sM[sp];
+            a.x += w * v[u].x;
+            a.y += w * v[u].y;
+            a.z += w * v[u].z;
+            a.w += w * v[u].w;
+        }
+    }
+    sA[sg][d4] = a;
+    __syncthreads();
+    if (t >= D4) return;
+    a = sA[0][t];
+#pragma unroll
+    for (int g = 1; g < SG; ++g) {
+        const float4 b = sA[g][t];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    const float M = sRow[0], l = sRow[1];
+    const float inv = 1.f / l;
+    const float4 o = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    const bool ok = M == M && l > 0.f && l < INFINITY && fabsf(o.x) < INFINITY && fabsf(o.y) < INFINITY &&
+                    fabsf(o.z) < INFINITY && fabsf(o.w) < INFINITY;
+    // the D/4 threads left are lanes of one wave: any of them that finds its
+    // dims non-finite marks the row through element 0
+    const bool row_bad = __any(!ok);
+    const int64_t off = r * D + 4 * t;
+    if constexpr (OUT_BF16) {
+        bf16x4 w = {(__bf16)o.x, (__bf16)o.y, (__bf16)o.z, (__bf16)o.w};
+        if (t == 0 && row_bad) w[0] = (__bf16)NAN;
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.out) + off) = w;
+    } else {
+        float4 w = o;
+        if (t == 0 && row_bad) w.x = NAN;
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) = w;
+    }
+    if (t == 0 && p.lse) {
+        const int64_t h = r % p.Hq, row = (r / p.Hq) % p.Lq, b = r / (p.Hq * p.Lq);
+        p.lse[(b * p.Hq + h) * p.Lq + row] = (M + log2f(l)) * 0.69314718055994531f;
+    }
+}
+
 template <int D, bool OUT_BF16, int MODE, bool PAGED = false>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-    if (p.G > 1 && MODE != kLocalWindow && !p.krot_ready) {
-        const int64_t n_items = p.B * p.L * p.Hkv * (D / 16);
+    if (p.G > 1 && MODE != kLocalWindow && !p.krot_ready && p.rot_lo < p.L) {
+        const int64_t n_items = p.B * (p.L - p.rot_lo) * p.Hkv * (D / 16);
         hipLaunchKernelGGL((rotate_keys_kernel<D, PAGED>), dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0,
-                           stream, static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.krot), p.TF, n_items, p.L,
-                           p.Lkv, (int)p.Hkv, p.G, p);
+                           stream, static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.krot), p.TF, n_items,
+                           p.L - p.rot_lo, p.Lkv, (int)p.Hkv, p.G, p);
     }
-    const int64_t blocks = (int64_t)p.n_qtiles * p.Hkv * p.B;
+    const int64_t blocks = (int64_t)p.n_qtiles * p.Hkv * p.B * p.n_ksplit;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16, MODE, PAGED>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, p);
+    if (p.n_ksplit > 1)
+        hipLaunchKernelGGL((split_combine_kernel<D, OUT_BF16>), dim3((unsigned)(p.B * p.Lq * p.Hq)),
+                           dim3(kCombThreads), 0, stream, p);
     return hipGetLastError();
 }
 
