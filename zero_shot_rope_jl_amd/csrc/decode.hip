@@ -378,6 +378,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         }
 
         // ---- online softmax per head column: 8 values here, 4 quads per head --
+        // The reference m_run moves only when a score exceeds it by more than
+        // kLazy (log2 units): probabilities stay below 2^kLazy (exact in fp32
+        // and within bf16's range), and the accumulators are rescaled only on
+        // the rare steps where some column's reference moves (a wave-uniform
+        // branch).  The first step always sets it (m_run = -inf).
+        constexpr float kLazy = 8.f;
         float mx = -INFINITY;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
@@ -385,22 +391,26 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[blk][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);   // finite: key kbase is valid
-        const float alpha = fast_exp2(m_run - m_new);
+        const bool move = mx > m_run + kLazy;   // mx is finite: key kbase is valid
+        if (__any(move)) {
+            const float m_new = move ? mx : m_run;
+            const float alpha = fast_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+            m_run = m_new;
+        }
         float ls = 0.f;
         bf16x8 Bp;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pv = fast_exp2(s[blk][i] - m_new);
+                const float pv = fast_exp2(s[blk][i] - m_run);
                 ls += pv;
                 Bp[4 * blk + i] = (__bf16)pv;
             }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+        l_run += ls;
 
         // ---- O^T += V^T P^T ------------------------------------------------------
         wave_lds_sync();   // V^T written by the other lanes of this wave
