@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
     python -m zero_shot_rope_jl_amd.profiling stats KERNEL_STATS_CSV --title T --cmd C
+    python -m zero_shot_rope_jl_amd.profiling grid KERNEL_TRACE_CSV --title T --cmd C
     python -m zero_shot_rope_jl_amd.profiling traffic --fetch FETCH_CSV --write WRITE_CSV \
         --cmd-fetch C1 --cmd-write C2
 
@@ -62,6 +63,25 @@ def stats_markdown(path: str, title: str, cmd: str, other: int = 3) -> str:
         n = n if len(n) < 80 else n[:77] + "..."
         out.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                    f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def grid_markdown(path: str, title: str, cmd: str) -> str:
+    """Library kernels of a --kernel-trace kernel_trace.csv grouped by kernel
+    and grid size (which tells apart launches of one kernel for different
+    problem sizes), in order of first launch: count and average duration."""
+    groups = collections.OrderedDict()
+    for r in csv.DictReader(open(path)):
+        if "jl::" not in r["Kernel_Name"]:
+            continue
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+               int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = [f"# {title}", "", "Command (repository root on one MI355X):", "", "```", cmd, "```", "",
+           "| kernel | workgroups | calls | average (us) | min (us) |", "|---|---|---|---|---|"]
+    for (name, grid, wg), d in groups.items():
+        n = name if len(name) < 80 else name[:77] + "..."
+        out.append(f"| `{n}` | {grid // wg} | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} |")
     return "\n".join(out) + "\n"
 
 
@@ -163,12 +183,19 @@ def main(argv=None) -> int:
     t.add_argument("--write", required=True)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
+    g = sub.add_parser("grid")
+    g.add_argument("csv")
+    g.add_argument("--title", required=True)
+    g.add_argument("--cmd", required=True)
     m = sub.add_parser("pmc")
     m.add_argument("csv", nargs="+")
     m.add_argument("--kernel", required=True)
     m.add_argument("--title", required=True)
     m.add_argument("--cmd", action="append", default=[])
     a = ap.parse_args(argv)
+    if a.what == "grid":
+        sys.stdout.write(grid_markdown(a.csv, a.title, a.cmd))
+        return 0
     if a.what == "pmc":
         sys.stdout.write(pmc_markdown(a.csv, a.kernel, a.title, a.cmd))
         return 0
