@@ -223,11 +223,19 @@ JL_API int jl_bifocal_prefill_unfused(const void* q, const void* k, const void* 
  * remote view, [B, Lmax, Hkv, D] bf16 by position, and the partials of the
  * key splits: when the chunk's query tiles are few (short chunks), each
  * tile's keys are split over several workgroups and merged with the
- * log-sum-exp rule (§3.3 Eq. 6 with disjoint key sets).
+ * log-sum-exp rule (§3.3 Eq. 6 with disjoint key sets).  A bf16 chunk whose
+ * Lq positions give at most 64 (position, query head) pairs per KV head
+ * (Lq * Hq / Hkv <= 64, with B * Lq <= 65535 and Hkv dividing 8 or a multiple
+ * of 8) runs on the decode kernels instead: one pass over the cache serves
+ * every position, remote keys read from the workspace's rotated rows, and
+ * the splits' partials [B, Lq, Hq, splits, D + 2] fp32 go to the workspace.
  *
  * `state` (host, may be NULL) describes the workspace's rotated keys: with
  * state->G equal to this call's G, rows below state->rows are not rotated
  * again, only rows state->rows .. L-1; the call then sets state to {G, L}.
+ * A chunk on the decode kernels reads rotated rows only below L-1-w0: when
+ * the state (same G) already covers those, it rotates nothing and leaves
+ * the state as it is.
  * Pass the same workspace and state to the chunks of one sequence (start
  * from {0, 0}, and reset to {0, 0} after rewriting cached keys below
  * state->rows); a chunk then rotates only its own new keys, except when G
@@ -250,9 +258,11 @@ JL_API int jl_bifocal_prefill_chunk(const void* q, const void* k_cache, const vo
  * jl_bifocal_prefill_chunk, max_pages * page_size for the paged form): the
  * keys' remote view when G can exceed 1 (bf16 inputs, Lcap > w_pretrained),
  * B * Lcap * Hkv * D * 2 bytes rounded up to 256, then room for the split
- * partials of any chunk of up to Lq tokens, max(splits * Lq') * B * Hq *
- * (D + 4) fp32 over Lq' <= Lq (none when no such chunk is split).  The same
- * size serves every Lq' <= Lq and L <= Lcap.  Pure host call.
+ * partials of any chunk of up to Lq tokens: the larger of max(splits * Lq')
+ * * B * Hq * (D + 4) fp32 over the chunks Lq' <= Lq that the prefill kernels
+ * split, and B * Lq' * Hq * splits * (D + 2) fp32 over those that run on the
+ * decode kernels (none when neither applies).  The same size serves every
+ * Lq' <= Lq and L <= Lcap.  Pure host call.
  */
 JL_API int jl_bifocal_prefill_chunk_workspace(int in_dtype, int64_t B, int64_t Lq, int64_t Lcap, int64_t Hq,
                                               int64_t Hkv, int64_t D, int64_t w_pretrained, size_t* bytes);
@@ -278,7 +288,8 @@ JL_API int jl_bifocal_prefill_chunk_workspace(int in_dtype, int64_t B, int64_t L
  * jl_bifocal_prefill_chunk over the same keys held contiguously.  A block
  * table entry outside [0, n_pages) is never followed: every output row whose
  * workgroup needs that page (at least every row at or after the page's first
- * position) is written as NaN.
+ * position; on the decode kernels, every row of the chunk's heads that read
+ * it) is written as NaN.
  *
  * Errors: as for jl_bifocal_prefill_chunk, plus JL_EINVAL for a NULL or
  * misaligned block_table, a page_size that is not a positive multiple of 128,

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
                            "jl_bifocal_prefill_chunk_workspace"])
     for s in syms:
         assert hasattr(jl.lib, s), s
-    assert jl.jl_version() == 11
+    assert jl.jl_version() == 12
 
 
 def test_schedule_golden_and_table_size():
@@ -519,15 +519,13 @@ def test_decode_noalloc_validation_and_scratch_limit():
 
 def test_prefill_chunk_workspace_size():
     """Rotated keys [B, Lcap, Hkv, D] bf16 (when G can exceed 1), rounded up to
-    256 bytes, then the partials of the key splits: a chunk whose query tiles
-    give under 128 workgroups is split over ~512 (>= 4 key tiles each, <= 64)."""
+    256 bytes, then room for the larger of two partial sets: the prefill
+    kernels' key splits (a chunk whose query tiles give under 128 workgroups
+    is split over ~512, >= 4 key tiles each, <= 64), and the decode kernels'
+    splits for chunks of at most 64 (position, query head) columns per KV
+    head ([B, Lq, Hq, n_split, D + 2] fp32, about 256 workgroups)."""
     up = lambda x: (x + 255) // 256 * 256
-    # 131072-row cache, 16-token chunk, 32/8 heads: 8 workgroups -> 64 splits
-    n = jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 16, 131072, 32, 8, 128, 32768)
-    assert n == up(131072 * 8 * 128 * 2) + 64 * 16 * 32 * 132 * 4
-    # a 4096-token chunk fills 512 workgroups and is not split, but a workspace for
-    # chunks of up to 4096 tokens has room for the splits of shorter ones: the
-    # largest need is 5 splits x 960 rows (120 workgroups)
+
     def need_rows(lq_max, keys, R=4, Hkv=8):
         best = 0
         for lq in range(1, lq_max + 1):
@@ -538,6 +536,35 @@ def test_prefill_chunk_workspace_size():
             s = min(-(-512 // wgs), tiles // 4, 64)
             best = max(best, s * lq if s > 1 else 0)
         return best
+
+    def dec_bytes(lq_max, keys, Hq=32, Hkv=8, D=128, B=1):
+        # column groups of 16: 1, 2 or 4, each group count with its longest chunk.
+        # One group: the split kernel, up to 4 KV heads per workgroup, 32-key
+        # steps; 2 or 4: one KV head per workgroup, 64-key stages; ~256 workgroups
+        R, best = Hq // Hkv, 0
+        for ng in (1, 2, 4):
+            lq = min(lq_max, 16 * ng // R)
+            cols = lq * R
+            if lq < 1 or (1 if cols <= 16 else 2 if cols <= 32 else 4) != ng or B * lq > 65535:
+                continue
+            if ng == 1:
+                groups = B * Hkv // min(4, Hkv)
+                n_split = min(256 // groups if groups < 256 else 1, min(-(-keys // 32), 256))
+            else:
+                groups = B * Hkv
+                n_split = min(-(-256 // groups) if groups < 256 else 1, -(-keys // 64))
+            best = max(best, B * lq * Hq * n_split * (D + 2) * 4)
+        return best
+
+    # 131072-row cache, 16-token chunk, 32/8 heads: 8 workgroups -> 64 prefill
+    # splits, against 32 decode splits of 16 x 32 columns (4 groups, one KV head
+    # per workgroup): the prefill partials are the larger
+    assert dec_bytes(16, 131072) == 16 * 32 * 32 * 130 * 4
+    n = jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 16, 131072, 32, 8, 128, 32768)
+    assert n == up(131072 * 8 * 128 * 2) + 64 * 16 * 32 * 132 * 4
+    # a 4096-token chunk fills 512 workgroups and is not split, but a workspace for
+    # chunks of up to 4096 tokens has room for the splits of shorter ones: the
+    # largest need is 5 splits x 960 rows (120 workgroups)
     n = jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 4096, 131072, 32, 8, 128, 32768)
     assert need_rows(4096, 131072) == 5 * 960
     assert n == up(131072 * 8 * 128 * 2) + 5 * 960 * 32 * 132 * 4
@@ -548,11 +575,21 @@ def test_prefill_chunk_workspace_size():
     # the size never shrinks as the chunk bound grows
     sizes = [jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, lq, 1500, 8, 2, 128, 400) for lq in range(1, 300)]
     assert all(a <= b for a, b in zip(sizes, sizes[1:]))
-    # a cache within the pretrained window needs no rotated keys: 9 key tiles, 2 splits
+    # a cache within the pretrained window needs no rotated keys; 9 key tiles give
+    # 2 prefill splits, but the decode kernels' 18 splits (64-key stages) of 16 x 32
+    # columns are larger
+    assert dec_bytes(16, 1100) == 16 * 32 * 18 * 130 * 4
     assert jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 16, 1100, 32, 8, 128, 32768) == \
-        2 * 16 * 32 * 132 * 4
-    # fewer than 8 key tiles: no split
-    assert jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 16, 896, 32, 8, 128, 32768) == 0
+        16 * 32 * 18 * 130 * 4
+    # fewer than 8 key tiles: no prefill split; a 4-token chunk (16 columns, 4 heads
+    # per workgroup, 2 groups of them -> 128 splits, 28 at 896 keys)
+    assert jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 4, 896, 32, 8, 128, 32768) == \
+        4 * 32 * 28 * 130 * 4 == dec_bytes(4, 896)
+    # B * Lq above 65535 would overflow the decode combine's grid, so 1024 sequences
+    # of 64 tokens stay on the prefill kernels (unsplit at 8192 workgroups): the
+    # room is for chunks of up to 32 tokens on the decode kernels (one split each)
+    assert jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1024, 64, 896, 8, 8, 128, 32768) == \
+        1024 * 32 * 8 * 1 * 130 * 4 == dec_bytes(32, 896, Hq=8, Hkv=8, B=1024)
     # fp32 inputs: the generic kernel rotates its keys itself and does not split
     assert jl.jl_bifocal_prefill_chunk_workspace(jl.JL_F32, 1, 16, 131072, 32, 8, 128, 32768) == 0
     with pytest.raises(jl.JetLongError):

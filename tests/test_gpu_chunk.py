@@ -76,15 +76,17 @@ def test_chunk_fp32_matches_oracle_1e5():
 
 
 def test_unsplit_chunk_equals_full_prefill_rows():
-    """Below 8 key tiles a chunk is not split: it walks every row's key tiles in the
-    order of the full prefill, so the two agree bit for bit."""
+    """Below 8 key tiles a chunk on the prefill kernels is not split: it walks every
+    row's key tiles in the order of the full prefill, so the two agree bit for bit.
+    (Chunks of at most 64 columns, here 16 tokens, run on the decode kernels and are
+    checked against the oracle below.)"""
     require_gpu()
     w = _workload(896, 8, 2, 128, 256, 100, seed=9)
     x = si.make_prefill_inputs(w, want_f64=False)
     q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
     table = jl.alloc_table(w.L, w.D, w.rope_base)
     full, lse_full = prefill(q, k, v, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, torch.float32, table)
-    for Lq in (1, 64, 333, 896):
+    for Lq in (17, 64, 333, 896):
         _, out, lse = _run_chunk(w, Lq, w.L, torch.float32, x)
         d = max_err(out.cpu().numpy(), full[:, w.L - Lq:].cpu().numpy())
         dl = max_err(lse.cpu().numpy(), lse_full[:, :, w.L - Lq:].cpu().numpy())
@@ -94,7 +96,8 @@ def test_unsplit_chunk_equals_full_prefill_rows():
 
 def test_split_chunk_agrees_with_full_prefill_rows():
     """Short chunks over 16 key tiles are split over workgroups and merged by
-    log-sum-exp: the same rows as the full prefill up to fp32 rounding."""
+    log-sum-exp (on the prefill kernels, or for one token on the decode kernels):
+    the same rows as the full prefill up to rounding."""
     require_gpu()
     w = _workload(2000, 8, 2, 128, 512, 256, seed=9)
     x = si.make_prefill_inputs(w, want_f64=False)
@@ -112,7 +115,9 @@ def test_split_chunk_agrees_with_full_prefill_rows():
 def test_chunk_state_rotates_only_new_keys():
     """A sequence prefilled chunk by chunk with one workspace and its state:
     each chunk rotates only the key rows the state lacks (and all of them
-    when G changes), and every chunk equals the stateless call bit for bit."""
+    when G changes; a short chunk on the decode kernels none, when the state
+    covers the rows it reads rotated), and every chunk equals the stateless
+    call bit for bit."""
     require_gpu()
     w = _workload(1400, 8, 2, 128, 400, 100, seed=44)   # G = 1 up to 400, 2 to 800, 3 to 1200, then 4
     x = si.make_prefill_inputs(w, want_f64=False)
@@ -136,7 +141,13 @@ def test_chunk_state_rotates_only_new_keys():
         jl.jl_bifocal_prefill_chunk(qc, kc, vc, b, None, L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table)
         torch.cuda.synchronize()
         print(f"L={L} Lq={Lq} G={G} state {before} -> {(st.state.G, st.state.rows)}")
-        assert (st.state.G, st.state.rows) == (G, L if G > 1 else 0)
+        on_decode = Lq * (w.Hq // w.Hkv) <= 64
+        if G > 1 and on_decode and before[0] == G and L - 1 - w.w0 <= before[1] <= L:
+            # on the decode kernels, rows below L-1-w0 are all the chunk reads
+            # rotated: a state that covers them is left as it is
+            assert (st.state.G, st.state.rows) == before
+        else:
+            assert (st.state.G, st.state.rows) == (G, L if G > 1 else 0)
         assert torch.equal(a, b)
 
 
@@ -159,8 +170,9 @@ def test_one_token_chunk_equals_decode():
 @pytest.mark.timeout(600)
 def test_short_chunks_at_128k_match_oracle():
     """Chunks of 1, 16 and 256 tokens at the end of the 128K workload (G = 4),
-    in the split configuration the benchmark times, against the oracle on
-    every chunk row (up to 64 seeded rows of the 256-token chunk), all heads."""
+    in the configuration the benchmark times (1 and 16 tokens on the decode
+    kernels, 256 on the split prefill kernels), against the oracle on every
+    chunk row (up to 64 seeded rows of the 256-token chunk), all heads."""
     require_gpu()
     w = si.WORKLOADS["ext128k"]
     x = si.make_prefill_inputs(w, want_f64=False)
@@ -184,3 +196,58 @@ def test_short_chunks_at_128k_match_oracle():
         el = max_err(lse.cpu().numpy()[:, :, idx], ref_lse)
         print(f"[chunk128k] Lq={Lq}: {len(idx)} rows x {w.Hq} heads, err {e:.3e}, lse err {el:.3e}", flush=True)
         assert e <= TOL_BF16 and el <= TOL_BF16
+
+
+SHORT = [  # (B, L, Lq, Hq, Hkv, D, w_pre, w0): chunks of at most 64 columns per KV head
+    (1, 3000, 1, 32, 8, 128, 700, 300),    # one token, 4 of 16 columns, G = 5
+    (2, 2500, 3, 8, 2, 128, 600, 100),     # 12 columns, two sequences
+    (1, 2000, 7, 8, 2, 128, 512, 5),       # two groups (28 columns); w0 < Lq: the window edges differ per column
+    (1, 4100, 16, 32, 8, 128, 1024, 40),   # four groups of 16, the benchmark's shape on a shorter cache
+    (1, 1500, 13, 8, 2, 64, 400, 9),       # D = 64, 52 of 64 columns
+    (1, 20, 16, 4, 4, 128, 8, 2),          # the chunk is the whole sequence: early columns see few keys
+    (1, 900, 64, 8, 8, 128, 300, 50),      # GQA 1: 64 positions in four groups
+    (1, 1000, 8, 16, 2, 128, 256, 100),    # GQA 8: 64 columns
+    (1, 600, 10, 8, 2, 128, 4096, 50),     # G = 1
+]
+
+
+@pytest.mark.parametrize("case", SHORT, ids=[f"B{c[0]}_L{c[1]}_Lq{c[2]}_H{c[3]}x{c[4]}_D{c[5]}" for c in SHORT])
+def test_short_chunk_on_decode_kernels_matches_oracle(case):
+    """Short chunks run as decode steps with several query positions (one MFMA
+    column per (position, query head)): every row against the oracle, fp32 and
+    bf16 outputs, and the same call over a shuffled paged copy of the cache
+    bit for bit."""
+    require_gpu()
+    B, L, Lq, Hq, Hkv, D, w_pre, w0 = case
+    w = si.Workload(f"short{L}", "bf16", B, L, Hq, Hkv, D, w0, w_pre, 1e4, L + 7 * Lq)
+    x, o32, l32 = _run_chunk(w, Lq, L + 40, torch.float32)
+    _, o16, _ = _run_chunk(w, Lq, L + 40, torch.bfloat16, x)
+    rows = np.arange(L - Lq, L)
+    ref, ref_lse = oracle.bifocal_attention(x["q64"], x["k64"], x["v64"], w0, w_pre, w.rope_base, w.sm_scale,
+                                            rows=rows)
+    o32 = o32.cpu().numpy()
+    e, el = max_err(o32, ref), max_err(l32.cpu().numpy(), ref_lse)
+    print(f"[short chunk] {case} G {oracle.group_size(L, w_pre)}: err {e:.3e}, lse err {el:.3e}", flush=True)
+    assert np.all(np.isfinite(o32))
+    assert e <= TOL_BF16 and el <= TOL_BF16
+    assert_bf16_out_close(o16.float().cpu().numpy(), ref)
+    # the paged form: pages of 128 keys in a shuffled order
+    q, k, v = (to_dev(x[n], "bf16") for n in "qkv")
+    ps = 128
+    n_p = -(-L // ps)
+    perm = torch.randperm(B * n_p, generator=torch.Generator().manual_seed(L)).to(torch.int32)
+    kp = torch.zeros((B * n_p, ps, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    bt = perm.view(B, n_p).cuda()
+    for bb in range(B):
+        for j in range(n_p):
+            n = min(ps, L - j * ps)
+            kp[perm[bb * n_p + j], :n] = k[bb, j * ps:j * ps + n]
+            vp[perm[bb * n_p + j], :n] = v[bb, j * ps:j * ps + n]
+    out = torch.empty((B, Lq, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device="cuda")
+    table = jl.alloc_table(L, D, w.rope_base)
+    jl.jl_bifocal_prefill_chunk_paged(q[:, L - Lq:].contiguous(), kp, vp, bt, out, lse, L, w0, w_pre, w.rope_base,
+                                      w.sm_scale, table)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), o32) and np.array_equal(lse.cpu().numpy(), l32.cpu().numpy())

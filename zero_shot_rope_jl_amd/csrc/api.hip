@@ -95,7 +95,7 @@ JL_API int jl_device_info(int device, int* n_cu, int* max_clock_khz) {
     return JL_OK;
 }
 
-JL_API int jl_version(void) { return 11; }
+JL_API int jl_version(void) { return 12; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -290,10 +290,54 @@ int64_t chunk_ksplit(int in_dtype, int64_t B, int64_t Lq, int64_t L, int64_t Hq,
     return s < 1 ? 1 : s;
 }
 
+// Short chunks run on the decode kernels: when the chunk's Lq positions of
+// the R query heads of a KV head make at most 64 MFMA columns (bf16 caches),
+// a chunk is a decode step with several query positions, which reads the
+// cache once for all of them (and its remote keys from the chunk's rotated
+// keys) instead of walking 256-row query tiles.  Returns the column groups
+// of 16: 1 (the split kernel), 2 or 4 (the kernel that stages keys in LDS
+// for every group), or 0 for the prefill kernels.
+int chunk_decode_groups(int in_dtype, int64_t B, int64_t Lq, int64_t Hq, int64_t Hkv) {
+    if (in_dtype != JL_BF16) return 0;
+    if (Hkv % 8 != 0 && 8 % Hkv != 0) return 0;
+    if (B * Lq > 65535) return 0;   // the combine's grid holds (batch, position) in y
+    return jl::decode_groups(Lq, Hq / Hkv);
+}
+
+// Bytes of the decode kernels' split partials for chunks of up to Lq tokens
+// over up to Lcap keys, [B, lq, Hq, n_split, D + 2] fp32: for each column
+// group count, its longest chunk and the most splits its plan can give.
+size_t chunk_decode_part_bytes(int in_dtype, int64_t B, int64_t Lq, int64_t Lcap, int64_t Hq, int64_t Hkv,
+                               int64_t D) {
+    size_t best = 0;
+    const int64_t R = Hq / Hkv;
+    for (int ng = 1; ng <= 4; ng *= 2) {
+        int64_t lq = 16 * ng / R < Lq ? 16 * ng / R : Lq;
+        if (lq < 1 || chunk_decode_groups(in_dtype, B, lq, Hq, Hkv) != ng) continue;
+        int64_t n_split;
+        if (ng == 1) {
+            // the split kernel: up to 4 KV heads per workgroup
+            const int64_t groups = B * (Hkv / jl::decode_heads_per_wg(Hkv));
+            const int64_t n_target = groups >= jl::kDecodeTargetWGs ? 1 : jl::kDecodeTargetWGs / groups;
+            n_split = n_target < jl::decode_max_splits(Lcap) ? n_target : jl::decode_max_splits(Lcap);
+        } else {
+            // the staged kernel: one KV head per workgroup, 64-key stages
+            const int64_t groups = B * Hkv;
+            const int64_t n_target =
+                groups >= jl::kDecodeTargetWGs ? 1 : (jl::kDecodeTargetWGs + groups - 1) / groups;
+            const int64_t steps = (Lcap + jl::kMultiStageKeys - 1) / jl::kMultiStageKeys;
+            n_split = n_target < steps ? n_target : steps;
+        }
+        const size_t b = (size_t)B * (size_t)lq * (size_t)Hq * (size_t)n_split * (size_t)(D + 2) * sizeof(float);
+        if (b > best) best = b;
+    }
+    return best;
+}
+
 // Workspace of chunk calls of up to Lq tokens over a cache of Lcap rows per
 // sequence: the keys' remote view [B, Lcap, Hkv, D] bf16 by position (bf16
 // inputs, when a G > 1 is possible), then room for the split partials of any
-// such call.
+// such call (of the prefill kernels' key splits or of the decode kernels).
 struct ChunkLayout {
     size_t krot, part, total;
 };
@@ -321,7 +365,9 @@ ChunkLayout chunk_layout(int in_dtype, int64_t B, int64_t Lq, int64_t Lcap, int6
     c.krot = 0;
     c.part = jl::decode_align(rotated ? (size_t)B * (size_t)Lcap * (size_t)Hkv * (size_t)D * 2u : 0u);
     const int64_t rows = chunk_part_rows(in_dtype, B, Lq, Lcap, Hq, Hkv);
-    c.total = c.part + (size_t)rows * (size_t)B * (size_t)Hq * (size_t)(D + 4) * sizeof(float);
+    const size_t split_bytes = (size_t)rows * (size_t)B * (size_t)Hq * (size_t)(D + 4) * sizeof(float);
+    const size_t dec_bytes = chunk_decode_part_bytes(in_dtype, B, Lq, Lcap, Hq, Hkv, D);
+    c.total = c.part + (split_bytes > dec_bytes ? split_bytes : dec_bytes);
     return c;
 }
 
@@ -341,17 +387,75 @@ int setup_chunk(const char* who, jl::PrefillParams& p, int in_dtype, int64_t Lca
     p.krot = c.part > 0 ? w + c.krot : nullptr;
     p.krot_rows = Lcap;
     p.n_ksplit = (int)chunk_ksplit(in_dtype, p.B, p.Lq, p.L, p.Hq, p.Hkv);
-    p.part = p.n_ksplit > 1 ? reinterpret_cast<float*>(w + c.part) : nullptr;
+    const bool dec = chunk_decode_groups(in_dtype, p.B, p.Lq, p.Hq, p.Hkv) > 0;
+    p.part = (p.n_ksplit > 1 || dec) ? reinterpret_cast<float*>(w + c.part) : nullptr;
     p.rot_lo = 0;
     if (state && p.G > 1) {
         // rows below state->rows already hold their remote view under this G
-        if (state->G == p.G && state->rows <= p.L) p.rot_lo = state->rows;
-        state->G = p.G;
-        state->rows = p.L;
+        const bool kept = state->G == p.G && state->rows <= p.L;
+        // a chunk on the decode kernels reads rotated rows only below its last
+        // position's window edge, L-1-w0: when the state covers them, nothing
+        // is rotated now (a later chunk that needs more rotates every row it
+        // lacks, up to its own L, in one pass)
+        const int64_t need = p.L - 1 - p.w0 > 0 ? p.L - 1 - p.w0 : 0;
+        if (dec && kept && state->rows >= need) {
+            p.rot_lo = p.L;
+        } else {
+            if (kept) p.rot_lo = state->rows;
+            state->G = p.G;
+            state->rows = p.L;
+        }
     } else if (state) {
         state->G = p.G;
         state->rows = 0;   // G = 1: nothing rotated
     }
+    return JL_OK;
+}
+
+void set_decode_range(jl::DecodeParams& p, int64_t L, int mode);
+
+// A short chunk (chunk_decode_groups > 0) on the decode kernels: the keys the
+// state lacks are rotated as for the prefill kernels, then one split launch
+// scores every position's keys (remote ones read rotated from p.krot) and the
+// combine writes out [B, Lq, Hq, D] and lse [B, Hq, Lq].
+int chunk_on_decode(const char* who, const jl::PrefillParams& p, int out_dtype, hipStream_t stream) {
+    (void)hipGetLastError();
+    hipError_t e = jl::launch_rotate_keys(p, stream);
+    if (e != hipSuccess) return fail(JL_EHIP, "%s key rotation launch failed: %s", who, hipGetErrorString(e));
+    jl::DecodeParams d{};
+    d.q = p.q;
+    d.k = p.k;
+    d.v = p.v;
+    d.out = p.out;
+    d.lse = p.lse;
+    d.ws = p.part;
+    d.table = p.table;
+    d.TF = p.TF;
+    d.table_key = p.table_key;
+    d.B = p.B;
+    d.L = p.L;
+    d.Lmax = p.block_table ? 0 : p.Lkv;
+    d.block_table = p.block_table;
+    d.page_size = p.page_size;
+    d.max_pages = p.max_pages;
+    d.n_pages = p.n_pages;
+    d.Hq = p.Hq;
+    d.Hkv = p.Hkv;
+    d.R = p.R;
+    d.Lq = (int)p.Lq;
+    d.n_grp = chunk_decode_groups(JL_BF16, p.B, p.Lq, p.Hq, p.Hkv);
+    d.heads_per_wg = d.n_grp == 1 ? jl::decode_heads_per_wg(p.Hkv) : 1;
+    d.w0 = p.w0 < p.L ? p.w0 : p.L;
+    d.G = p.G;
+    d.sm_scale_log2 = p.sm_scale_log2;
+    d.rope_base = p.rope_base;
+    d.head_dim = p.head_dim;
+    d.krot = p.G > 1 ? p.krot : nullptr;
+    d.krot_rows = p.krot_rows;
+    d.rot_row = -1;
+    set_decode_range(d, p.L, jl::kFused);
+    e = jl::launch_decode(d, out_dtype, stream);
+    if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
     return JL_OK;
 }
 
@@ -382,6 +486,8 @@ int prefill_impl(const char* who, const void* q, const void* k, const void* v, v
         p.G = fi_group(L, w_pretrained);
         p.table_key = jl::TableKey{jl::kTableMagicFI, L, w_pretrained, fi->alpha, fi->beta};
     }
+    if (chunk && chunk_decode_groups(in_dtype, B, Lq, Hq, Hkv) > 0)
+        return chunk_on_decode(who, p, out_dtype, static_cast<hipStream_t>(hip_stream));
     (void)hipGetLastError();
     hipError_t e = jl::launch_prefill(p, in_dtype, out_dtype, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
@@ -555,6 +661,8 @@ JL_API int jl_bifocal_prefill_chunk_paged(const void* q, const void* k_pages, co
     p.page_size = page_size;
     p.max_pages = max_pages;
     p.n_pages = n_pages;
+    if (chunk_decode_groups(in_dtype, B, Lq, Hq, Hkv) > 0)
+        return chunk_on_decode(who, p, out_dtype, static_cast<hipStream_t>(hip_stream));
     (void)hipGetLastError();
     hipError_t e = jl::launch_prefill(p, in_dtype, out_dtype, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(JL_EHIP, "%s launch failed: %s", who, hipGetErrorString(e));
@@ -611,7 +719,8 @@ void set_decode_range(jl::DecodeParams& p, int64_t L, int mode) {
     case jl::kRemoteWindow: p.k_lo = kwin; p.kloc = none_stored; break;
     default: p.k_lo = 0; p.kloc = p.G == 1 ? 0 : kwin; break;
     }
-    jl::decode_split_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk);
+    if (p.n_grp > 1) jl::decode_multi_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk);
+    else jl::decode_split_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk);
 }
 
 // Both decode entry points.  Contiguous cache: block_table == NULL, k/v
@@ -689,6 +798,8 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.R = (int)R;
+    p.Lq = 1;
+    p.n_grp = 1;
     p.heads_per_wg = jl::decode_heads_per_wg(Hkv);
     p.w0 = w0 < L ? w0 : L;
     p.G = group_size(L, w_pretrained);
@@ -696,6 +807,7 @@ int decode_impl(const char* who, const void* q, const void* k_cache, const void*
     p.rope_base = rope_base;
     p.head_dim = (int)D;
     p.krot = krot;
+    p.krot_rows = Lmax;
     p.rot_row = -1;
     if (fi) {
         p.G = fi_group(L, w_pretrained);

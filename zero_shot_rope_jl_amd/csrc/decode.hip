@@ -29,6 +29,12 @@
 // combine kernel merges a head's partials with the log-sum-exp rule (§3.3
 // Eq. 6 with disjoint key sets).
 //
+// Several query positions (a short chunk of a chunked prefill, §3.2): the
+// Lq positions L-Lq .. L-1 of the R heads give Lq * R <= 16 MFMA columns.
+// A column keeps its own causal limit and window edge; the correction
+// offsets are shared, since G comes from L for every position of the call.
+// (More columns go to decode_multi_kernel below.)
+//
 // Pass modes (the unfused step): the same kernels read only the window's
 // keys in the stored view (pass A), every key in the corrected view (B), or
 // the window's keys in the corrected view (C); the merge kernel of the
@@ -42,6 +48,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -70,6 +77,7 @@ struct DecodeTile {
 // Cache reads are non-temporal: every byte is read once per step, and the
 // streaming hint gave ~13% more read bandwidth for this access shape than
 // ordinary loads.
+
 // `rbase` is the cache row of key kbase; the 32 keys of a step occupy the
 // consecutive rows from there (a page holds a multiple of 32 keys).
 template <int D>
@@ -155,17 +163,27 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const int Hq = (int)p.Hq;
     const int R = p.R;
     const int G = (int)p.G;
-    const int qpos = L - 1;
-    // keys >= kloc score in the stored view (q - k <= w0 in the fused step;
-    // G == 1 makes every key local)
-    const int kloc = (int)p.kloc;
+    const int Lq = p.Lq;
+    // this lane's column: query head rq at position L - Lq + jq (columns past
+    // the last position compute on a zero query and are not written)
+    const bool hvalid = colh < Lq * R;
+    const int jq = hvalid ? colh / R : Lq - 1;
+    const int rq = hvalid ? colh % R : 0;
+    const int qpos = L - Lq + jq;
+    // keys >= kloc score in the stored view: p.kloc is the last position's
+    // edge (q - k <= w0 in the fused step, 0 when G == 1 makes every key
+    // local), an earlier position's edge lies as many keys lower; kloc_lo
+    // and kloc_hi bound the columns' edges
+    const int kloc = p.kloc > 0 ? (int)p.kloc - (Lq - 1 - jq) : (int)p.kloc;
+    const int kloc_lo = p.kloc > 0 ? (int)p.kloc - (Lq - 1) : (int)p.kloc;
+    const int kloc_hi = (int)p.kloc;
     const float scale2 = p.sm_scale_log2;
     const __bf16* __restrict__ kc = static_cast<const __bf16*>(p.k);
-    // rotated-key cache (RKC): remote keys are read in their corrected view
-    // instead of being rotated here; a step is read from it when all of its
-    // keys are remote
+    // rotated keys (RKC): remote keys are read in their corrected view,
+    // [B, krot_rows, Hkv, D] by position, instead of being rotated here; a
+    // step is read from there when its keys are remote for every column
     const __bf16* __restrict__ krc = static_cast<const __bf16*>(p.krot);
-    auto ksrc = [&](int kb) -> const __bf16* { return (RKC && kb + kWaveKeys <= kloc) ? krc : kc; };
+    auto rkc_step = [&](int kb) { return RKC && kb + kWaveKeys <= kloc_lo; };
     const __bf16* __restrict__ vc = static_cast<const __bf16*>(p.v);
     const float2* __restrict__ TF = p.TF;
     // row n, pair i of the correction table (formed here for the
@@ -176,6 +194,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     };
     const int64_t row = p.Hkv * D;
     const int64_t cache_b = PAGED ? (int64_t)g * D : (int64_t)b * p.Lmax * row + (int64_t)g * D;
+    const int64_t krot_b = (int64_t)b * p.krot_rows * row + (int64_t)g * D;
 
     // Cache row of key kb (a multiple of 32), in two parts so that the
     // block-table read can be issued well before its value is needed:
@@ -216,7 +235,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     int pg_ahead = 0;     // block-table entry of the step after next
     if (wstart < wend0) {
         const int64_t r0 = row_of(wstart);
-        load_k<D>(cur, ksrc(wstart), cache_b, row, wstart, r0, wend0, colh, gq);
+        if (rkc_step(wstart)) load_k<D>(cur, krc, krot_b, row, wstart, wstart, wend0, colh, gq);
+        else load_k<D>(cur, kc, cache_b, row, wstart, r0, wend0, colh, gq);
         load_v<D>(cur, vc, cache_b, row, wstart, r0, wend0, lane);
         if (wstart + kWaveKeys < wend0) r_next = row_of(wstart + kWaveKeys);
         if (wstart + 2 * kWaveKeys < wend0) pg_ahead = page_of(wstart + 2 * kWaveKeys);
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     // rotated-key cache: one wave per (batch, KV head) reads the row that the
     // next step will need as remote (its wait falls in the first step's);
     // the rotated row is stored after the key loop
-    const bool write_ahead = RKC && p.rot_row >= 0 && split == 0 && sub == 0 && lane < HALF;
+    const bool write_ahead = RKC && !PAGED && p.rot_row >= 0 && split == 0 && sub == 0 && lane < HALF;
     float wa_x = 0.f, wa_y = 0.f;
     float2 wa_cs = make_float2(1.f, 0.f);
     int64_t wa_o = 0;
@@ -245,15 +265,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     __syncthreads();
     const bool bad = s_bad;
 
-    const bool hvalid = colh < R;
-    const int head = g * R + (hvalid ? colh : 0);
+    const int head = g * R + rq;
 
     // ---- query: stored fragments and the corrected view ---------------------
     // B operand of S^T = K Q^T: fragment c holds dims 32c + 8gq + [0, 8).  The
     // corrected view R(-n_q) q is kept in bf16 (the MFMA operand precision).
     bf16x8 qf[NC], qrem[NC];
     {
-        const __bf16* qp = static_cast<const __bf16*>(p.q) + ((int64_t)b * Hq + head) * D;
+        const __bf16* qp = static_cast<const __bf16*>(p.q) + ((int64_t)(b * Lq + jq) * Hq + head) * D;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             qf[c] = hvalid ? *reinterpret_cast<const bf16x8*>(qp + 32 * c + 8 * gq) : bf16x8{};
@@ -306,7 +325,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
                 qit[c + NC / 2][j] = (__bf16)(x * cs.y + y * cs.x);
             }
     };
-    if (!RKC && G > 1 && wstart < wend && wstart < kloc) rotate_query(wstart);
+    if (!RKC && G > 1 && wstart < wend && wstart < kloc_hi) rotate_query(wstart);
 
     // One register tile (loaded above): each part is reloaded for the next
     // step as soon as this step has consumed it (V after its transpose, each
@@ -330,8 +349,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         // V registers are free: start the next step's V loads
         if (knext < wend) load_v<D>(cur, vc, cache_b, row, knext, r_next, wend, lane);
 
-        const bool w_loc = (G == 1) || (kbase + kWaveKeys - 1 >= kloc);
-        const bool w_rem = (G > 1) && (kbase < kloc);
+        // some column scores a key of this step in the stored view / in the
+        // corrected view
+        const bool w_loc = (G == 1) || (kbase + kWaveKeys - 1 >= kloc_lo);
+        const bool w_rem = (G > 1) && (kbase < kloc_hi);
 
         float s[2][4];
 #pragma unroll
@@ -345,7 +366,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
             if (RKC && w_rem) {
                 // a step with local keys was read from the stored cache: read
                 // this half's rows again, rotated, for its remote keys
-                if (w_loc) load_k_blk<D>(cur, krc, cache_b, row, kbase, kbase, wend, colh, gq, blk);
+                if (w_loc) load_k_blk<D>(cur, krc, krot_b, row, kbase, kbase, wend, colh, gq, blk);
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
                     sr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[blk][c], qrem[c], sr, 0, 0, 0);
@@ -371,10 +392,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
                 float v;
                 if (w_loc && w_rem) v = kk >= kloc ? sl[i] : sr[i];
                 else v = w_loc ? sl[i] : sr[i];
-                s[blk][i] = kk < wend ? v * scale2 : -INFINITY;
+                s[blk][i] = (kk < wend && kk <= qpos) ? v * scale2 : -INFINITY;
             }
             // this half's K registers are free: start the next step's loads
-            if (knext < wend) load_k_blk<D>(cur, ksrc(knext), cache_b, row, knext, r_next, wend, colh, gq, blk);
+            if (knext < wend) {
+                if (rkc_step(knext)) load_k_blk<D>(cur, krc, krot_b, row, knext, knext, wend, colh, gq, blk);
+                else load_k_blk<D>(cur, kc, cache_b, row, knext, r_next, wend, colh, gq, blk);
+            }
         }
 
         // ---- online softmax per head column: 8 values here, 4 quads per head --
@@ -382,7 +406,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         // kLazy (log2 units): probabilities stay below 2^kLazy (exact in fp32
         // and within bf16's range), and the accumulators are rescaled only on
         // the rare steps where some column's reference moves (a wave-uniform
-        // branch).  The first step always sets it (m_run = -inf).
+        // branch).  A column's first step with a key in its causal range sets
+        // it (m_run = -inf before); with several positions a column can meet
+        // a step with none, whose probabilities must come out 0, not NaN.
         constexpr float kLazy = 8.f;
         float mx = -INFINITY;
 #pragma unroll
@@ -391,22 +417,24 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[blk][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool move = mx > m_run + kLazy;   // mx is finite: key kbase is valid
+        const bool move = mx > m_run + kLazy;
         if (__any(move)) {
-            const float m_new = move ? mx : m_run;
-            const float alpha = fast_exp2(m_run - m_new);
+            // a column that does not move keeps its scale (its m_run may still
+            // be -inf, which a subtraction would turn into NaN)
+            const float alpha = move ? fast_exp2(m_run - mx) : 1.f;
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-            m_run = m_new;
+            m_run = move ? mx : m_run;
         }
         float ls = 0.f;
         bf16x8 Bp;
+        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pv = fast_exp2(s[blk][i] - m_run);
+                const float pv = fast_exp2(s[blk][i] - m_sub);
                 ls += pv;
                 Bp[4 * blk + i] = (__bf16)pv;
             }
@@ -426,7 +454,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         }
         // the next step's corrected query, computed here so that it is off the
         // path from K's arrival to the next K loads
-        if (!RKC && G > 1 && knext < wend && knext < kloc) rotate_query(knext);
+        if (!RKC && G > 1 && knext < wend && knext < kloc_hi) rotate_query(knext);
         // rows of the step after next (its table entry was read a step ago);
         // then the table entry of the step after that
         r_next = knext + kWaveKeys < wend ? row_in(pg_ahead, knext + kWaveKeys) : 0;
@@ -439,15 +467,16 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         if (bad) wa_x = wa_y = NAN;
         else rotate_back(wa_x, wa_y, wa_cs);
         __bf16* kw = static_cast<__bf16*>(const_cast<void*>(p.krot));
-        kw[wa_o] = (__bf16)wa_x;
-        kw[wa_o + HALF] = (__bf16)wa_y;
+        const int64_t wo = krot_b + p.rot_row * row + lane;
+        kw[wo] = (__bf16)wa_x;
+        kw[wo + HALF] = (__bf16)wa_y;
     }
 
-    // ---- merge the NW waves of each head, write this split's partials -------
+    // ---- merge the NW waves of each head, write this split's partials ---------
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
     __syncthreads();   // every wave is done with its V^T slice
-    float* s_acc = reinterpret_cast<float*>(&sVt[0][0]);   // [wave][16 heads][D]
+    float* s_acc = reinterpret_cast<float*>(&sVt[0][0]);   // [wave][16 columns][D]
     if (gq == 0) {
         s_m[wave][colh] = m_run;
         s_l[wave][colh] = l_tot;
@@ -457,24 +486,25 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
 #pragma unroll
         for (int i = 0; i < 4; ++i) s_acc[(wave * 16 + colh) * D + 16 * db + 4 * gq + i] = acc[db][i];
     __syncthreads();
-    for (int idx = tid; idx < WH * R * D; idx += kDecThreads) {
-        const int hx = idx / (R * D), r = (idx / D) % R, d = idx % D;
+    const int ncol = Lq * R;   // valid columns per KV head
+    for (int idx = tid; idx < WH * ncol * D; idx += kDecThreads) {
+        const int hx = idx / (ncol * D), c = (idx / D) % ncol, d = idx % D;
         float M = -INFINITY;
-        for (int u = 0; u < NW; ++u) M = fmaxf(M, s_m[u * WH + hx][r]);
+        for (int u = 0; u < NW; ++u) M = fmaxf(M, s_m[u * WH + hx][c]);
         float a = 0.f, l = 0.f;
         if (!bad) {
             for (int u = 0; u < NW; ++u) {
                 const int w = u * WH + hx;
-                const float m = s_m[w][r];
-                const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);   // waves without keys
-                a += f * s_acc[(w * 16 + r) * D + d];
-                l += f * s_l[w][r];
+                const float m = s_m[w][c];
+                const float fw = (m == -INFINITY) ? 0.f : fast_exp2(m - M);   // waves without keys
+                a += fw * s_acc[(w * 16 + c) * D + d];
+                l += fw * s_l[w][c];
             }
         } else {
             a = l = M = NAN;
         }
-        const int hq = (blockIdx.y * WH + hx) * R + r;
-        float* o = p.ws + (((int64_t)b * Hq + hq) * p.n_split + split) * (D + 2);
+        const int hq = (blockIdx.y * WH + hx) * R + c % R;
+        float* o = p.ws + ((((int64_t)b * Lq + c / R) * Hq + hq) * p.n_split + split) * (D + 2);
         o[d] = a;
         if (d == 0) {
             o[D] = M;
@@ -498,12 +528,12 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
     __shared__ float sRed[kCombThreads];
     __shared__ float sM, sL;
     const int head = blockIdx.x;
-    const int b = blockIdx.y;
+    const int bj = blockIdx.y;   // (batch, query position)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int ns = p.n_split;
-    const float* base = p.ws + ((int64_t)b * p.Hq + head) * ns * (D + 2);
+    const float* base = p.ws + ((int64_t)bj * p.Hq + head) * ns * (D + 2);
     const int d = blockIdx.z * kCombDims + (tid % kCombDims);
     const int part = tid / kCombDims;   // 32 interleaved split groups
     // every load of the kernel goes out at once: this thread's partial sums
@@ -553,17 +583,414 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
 #pragma unroll
         for (int q = 0; q < 32; ++q) t += sRed[q * kCombDims + tid];
         const float lt = sL;
-        const int64_t o = ((int64_t)b * p.Hq + head) * D + d;
+        const int64_t o = ((int64_t)bj * p.Hq + head) * D + d;
         if constexpr (OUT_BF16) static_cast<__bf16*>(p.out)[o] = (__bf16)(t / lt);
         else static_cast<float*>(p.out)[o] = t / lt;
-        if (blockIdx.z == 0 && tid == 0 && p.lse) p.lse[(int64_t)b * p.Hq + head] = (sM + log2f(lt)) * 0.69314718055994531f;
+        if (blockIdx.z == 0 && tid == 0 && p.lse)
+            p.lse[((int64_t)(bj / p.Lq) * p.Hq + head) * p.Lq + bj % p.Lq] = (sM + log2f(lt)) * 0.69314718055994531f;
     }
+}
+
+// ---- several query positions: keys staged in LDS for every column group ----
+//
+// A short chunk of Lq positions (Jet-Long §3.2: the chunk's rows under G(L),
+// remote keys in their corrected view) with 2 or 4 groups of 16 (position,
+// query head) columns per KV head.  Workgroup = (key range, KV head, batch)
+// with two waves per column group; every 64-key step is copied HBM -> LDS
+// once (buffer loads into LDS, no registers), four steps deep, and each
+// wave scores one 32-key half of the step for its 16 columns with the
+// decode kernel's MFMA layout (K rows as A, queries as N columns; V^T
+// through the transposing LDS read).  The copies of all groups' keys are
+// then one HBM read, and the ring keeps ~100 KB per compute unit in flight
+// with no register cost.
+//
+// Remote keys are read rotated from p.krot (by position), stored keys from
+// the cache.  A step that holds some column's window edge is visited twice:
+// once in the corrected view (keys before each column's edge kept), once in
+// the stored view (the rest).
+constexpr int kMqKeys = 64;    // keys per stage
+constexpr int kMqStages = 4;   // LDS ring depth
+
+// 16-byte buffer -> LDS copy per lane (lane l writes bytes [16l, 16l + 16)
+// after the wave-uniform LDS base), issued so that the compiler does not
+// track it: the compiler cannot tell this kernel's four stages apart and
+// would make every LDS read wait for every copy in flight, which empties the
+// ring.  The kernel orders the copies itself: each stage is waited for with
+// s_waitcnt vmcnt (copies complete in issue order) and a barrier before any
+// wave reads it, and a stage is refilled only after a barrier that follows
+// every read of its previous contents.  The instruction writes no register;
+// M0 (the LDS base) needs one wait state before the copy reads it.
+__device__ inline void mq_copy16(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voff, uint32_t soff) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0v), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+
+template <int D>
+__device__ inline int mq_kswz(int row, int c) { return c ^ (row & (D / 8 - 1)); }
+template <int D>
+__device__ inline int mq_vswz(int row, int c) { return c ^ ((4 * (row & 3)) & (D / 8 - 1)); }
+
+template <int D, bool OUT_BF16, bool PAGED, int NG>
+__global__ __launch_bounds__(128 * NG) void decode_multi_kernel(DecodeParams p) {
+    constexpr int NWV = 2 * NG;           // waves: column group x key half
+    constexpr int NT = 64 * NWV;
+    constexpr int NC = D / 32;            // 32-dim chunks of the score MFMA
+    constexpr int NDB = D / 16;           // 16-dim blocks of O^T
+    constexpr int CH = D / 8;             // 16-byte chunks per row
+    constexpr int BK = kMqKeys;
+    constexpr int PU = BK * CH / NT;      // 16-byte copies per thread per operand and stage
+    constexpr int RU = NT / CH;           // rows per copy round
+    static_assert(PU * NT == BK * CH && RU % CH == 0 && RU % 4 == 0, "copy rounds keep lane-constant swizzles");
+    // four stages, K then V in each, separate objects selected at compile
+    // time so that the copies into one are not taken to alias reads of another
+    __shared__ __attribute__((aligned(16))) __bf16 sS0[2 * BK * D], sS1[2 * BK * D], sS2[2 * BK * D], sS3[2 * BK * D];
+    __shared__ float s_m[NG][16], s_l[NG][16];
+    __shared__ int s_bad;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int colh = lane & 15;
+    const int gq = lane >> 4;
+    const int grp = wave % NG;
+    const int sub = wave / NG;            // key half of each step
+    const int split = blockIdx.x;
+    const int g = blockIdx.y;
+    const int b = blockIdx.z;
+    const int L = (int)p.L;
+    const int Hq = (int)p.Hq;
+    const int R = p.R;
+    const int G = (int)p.G;
+    const int Lq = p.Lq;
+    const int fcol = grp * 16 + colh;
+    const bool hvalid = fcol < Lq * R;
+    const int jq = hvalid ? fcol / R : Lq - 1;
+    const int rq = hvalid ? fcol % R : 0;
+    const int qpos = L - Lq + jq;
+    const int kloc = p.kloc > 0 ? (int)p.kloc - (Lq - 1 - jq) : (int)p.kloc;
+    const int kloc_lo = p.kloc > 0 ? (int)p.kloc - (Lq - 1) : (int)p.kloc;
+    const int kloc_hi = (int)p.kloc;
+    const float scale2 = p.sm_scale_log2;
+    const int64_t kv_row = p.Hkv * D;
+    const uint32_t row_bytes = (uint32_t)(kv_row * 2);
+
+    // this workgroup's keys [kr0, kr1) in steps of BK; steps [t_rem, t_loc)
+    // hold a window edge and are visited twice
+    const int kr0 = split * p.wave_chunk;
+    const int kr1 = min(L, kr0 + p.wave_chunk);
+    const int n_steps = kr1 > kr0 ? (kr1 - kr0 + BK - 1) / BK : 0;
+    auto clampi = [](int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); };
+    const int t_rem = G > 1 ? clampi(kloc_lo - kr0 < 0 ? -1 : (kloc_lo - kr0) / BK, 0, n_steps) : 0;
+    const int t_loc = G > 1 ? clampi(kloc_hi - kr0 <= 0 ? 0 : (kloc_hi - kr0 + BK - 1) / BK, 0, n_steps) : 0;
+    const int n_twice = t_loc > t_rem ? t_loc - t_rem : 0;
+    const int NV = n_steps + n_twice;
+    // visit v: its step's first key and its view
+    auto visit_of = [&](int v, int& k0, bool& rem) __attribute__((always_inline)) {
+        int t;
+        if (v < t_rem) {
+            t = v;
+            rem = true;
+        } else if (v < t_rem + 2 * n_twice) {
+            t = t_rem + (v - t_rem) / 2;
+            rem = ((v - t_rem) & 1) == 0;
+        } else {
+            t = v - n_twice;
+            rem = false;
+        }
+        k0 = kr0 + t * BK;
+    };
+
+    // ---- staging -------------------------------------------------------------
+    // One copy fills 64 consecutive 16-byte LDS slots (one per lane): slot
+    // u * NT + tid holds row u * RU + tid / CH, physical chunk tid % CH, into
+    // which this lane copies logical chunk swz(row, tid % CH).  Rows past L
+    // (and every row of a visit past the last) read as zeros.
+    const __bf16* kc = static_cast<const __bf16*>(p.k);
+    const __bf16* vc = static_cast<const __bf16*>(p.v);
+    const __bf16* krc = static_cast<const __bf16*>(p.krot);
+    const int trow = tid / CH, tch = tid % CH;
+    const uint32_t k_voff = (uint32_t)trow * row_bytes + 16u * (uint32_t)mq_kswz<D>(trow, tch);
+    const uint32_t v_voff = (uint32_t)trow * row_bytes + 16u * (uint32_t)mq_vswz<D>(trow, tch);
+    bool bad_page = false;
+    auto cache_row = [&](int k0) __attribute__((always_inline)) -> int64_t {
+        if constexpr (!PAGED) {
+            return (int64_t)b * p.Lmax + k0;
+        } else {
+            typedef const __attribute__((address_space(4))) int32_t* ctab;
+            const int ps = (int)p.page_size;
+            int pg = ((ctab)(p.block_table + (int64_t)b * p.max_pages))[k0 / ps];
+            if (pg < 0 || pg >= p.n_pages) {
+                bad_page = true;
+                pg = 0;
+            }
+            return (int64_t)pg * ps + k0 % ps;
+        }
+    };
+    auto stage = [&](int v, __bf16* dK, __bf16* dV) __attribute__((always_inline)) {
+        int k0 = 0;
+        bool rem = false;
+        uint32_t bytes = 0;
+        const __bf16* ks = kc;
+        const __bf16* vs = vc;
+        if (v < NV) {
+            visit_of(v, k0, rem);
+            bytes = (uint32_t)min(L - k0, BK) * row_bytes;
+            const int64_t crow = cache_row(k0);
+            ks = rem ? krc + ((int64_t)b * p.krot_rows + k0) * kv_row + (int64_t)g * D
+                     : kc + crow * kv_row + (int64_t)g * D;
+            vs = vc + crow * kv_row + (int64_t)g * D;
+        }
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(ks, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vs, bytes);
+#pragma unroll
+        for (int u = 0; u < PU; ++u) {
+            mq_copy16(rk, dK + (u * NWV + wave) * 512, k_voff, (uint32_t)(u * RU) * row_bytes);
+            mq_copy16(rv, dV + (u * NWV + wave) * 512, v_voff, (uint32_t)(u * RU) * row_bytes);
+        }
+    };
+    // outstanding copies allowed while waiting for the oldest stage: those
+    // of the three stages issued after it (vmcnt field of s_waitcnt, expcnt
+    // and lgkmcnt left at their maxima)
+    constexpr int kAfter = 2 * PU * (kMqStages - 1);
+    static_assert(kAfter < 64, "vmcnt holds 6 bits");
+    constexpr int kWaitEnc = (kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8);
+
+    stage(0, sS0, sS0 + BK * D);
+    stage(1, sS1, sS1 + BK * D);
+    stage(2, sS2, sS2 + BK * D);
+
+    if (tid == 0) s_bad = !table_matches(p.table, p.table_key, D, p.rope_base, table_need(p.L, p.G));
+
+    // ---- queries: stored and corrected views (bf16, the MFMA operand) ----
+    const int head = g * R + rq;
+    bf16x8 qf[NC], qrem[NC];
+    {
+        const __bf16* qp = static_cast<const __bf16*>(p.q) + ((int64_t)(b * Lq + jq) * Hq + head) * D;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            qf[c] = hvalid ? *reinterpret_cast<const bf16x8*>(qp + 32 * c + 8 * gq) : bf16x8{};
+            qrem[c] = qf[c];
+        }
+        if (G > 1) {
+            const int nq = qpos - qpos / G;
+#pragma unroll
+            for (int c = 0; c < NC / 2; ++c)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float x = (float)qf[c][j], y = (float)qf[c + NC / 2][j];
+                    rotate_back(x, y, table_cs(p.TF, D / 2, nq, 32 * c + 8 * gq + j));
+                    qrem[c][j] = (__bf16)x;
+                    qrem[c + NC / 2][j] = (__bf16)y;
+                }
+        }
+    }
+
+    f32x4 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
+    float m_run = -INFINITY, l_run = 0.f;
+    // A-operand row of this lane in each 16-key block (C rows then give P^T
+    // in natural key order), and the transposing read's row and dims
+    const int dk0 = 8 * (colh >> 2) + (colh & 3);
+    const int tr_row = 8 * gq + (colh >> 2);
+    const int tr_dim = 4 * (colh & 3);
+
+    auto compute = [&](int v, const __bf16* K, const __bf16* V) __attribute__((always_inline)) {
+        int k0;
+        bool rem;
+        visit_of(v, k0, rem);
+        const int kb = k0 + 32 * sub;
+        float s[2][4];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int r = 32 * sub + dk0 + 4 * blk;
+            f32x4 sc = f32x4{};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(K + r * D + 8 * mq_kswz<D>(r, 4 * c + gq));
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rem ? qrem[c] : qf[c], sc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kk = kb + 8 * gq + 4 * blk + i;
+                const bool keep = kk < L && kk <= qpos && (rem ? kk < kloc : kk >= kloc);
+                s[blk][i] = keep ? sc[i] * scale2 : -INFINITY;
+            }
+        }
+        // online softmax per column (lazy reference max, as in the split kernel)
+        constexpr float kLazy = 8.f;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[blk][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool move = mx > m_run + kLazy;
+        if (__any(move)) {
+            const float alpha = move ? fast_exp2(m_run - mx) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+            m_run = move ? mx : m_run;
+        }
+        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+        float ls = 0.f;
+        bf16x8 Bp;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = fast_exp2(s[blk][i] - m_sub);
+                ls += pv;
+                Bp[4 * blk + i] = (__bf16)pv;
+            }
+        l_run += ls;
+        // O^T += V^T P^T: V^T rows (dims) through the transposing read
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int r0 = 32 * sub + tr_row;
+            const int lc = (16 * db + tr_dim) >> 3, wi = tr_dim & 7;
+            const bf16x4 lo = lds_read_tr16(V + r0 * D + 8 * mq_vswz<D>(r0, lc) + wi);
+            const bf16x4 hi = lds_read_tr16(V + (r0 + 4) * D + 8 * mq_vswz<D>(r0 + 4, lc) + wi);
+            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Bp, acc[db], 0, 0, 0);
+        }
+    };
+
+    // visit v computes from stage slot v % 4; first the slot that visit v - 1
+    // used is refilled with visit v + 3 (a visit past the last copies zeros),
+    // so that four stages are in flight while visit v's copies are awaited
+    auto step = [&](int v, auto slot) __attribute__((always_inline)) {
+        constexpr int S = decltype(slot)::value;
+        __bf16* const Ss[4] = {sS0, sS1, sS2, sS3};
+        __syncthreads();                         // visit v - 1 is done everywhere
+        stage(v + 3, Ss[(S + 3) & 3], Ss[(S + 3) & 3] + BK * D);
+        __builtin_amdgcn_s_waitcnt(kWaitEnc);   // this wave's copies of visit v have landed
+        __syncthreads();                         // and everyone's
+        compute(v, Ss[S], Ss[S] + BK * D);
+    };
+    for (int v = 0; v < NV; v += 4) {
+        step(v, std::integral_constant<int, 0>{});
+        if (v + 1 < NV) step(v + 1, std::integral_constant<int, 1>{});
+        if (v + 2 < NV) step(v + 2, std::integral_constant<int, 2>{});
+        if (v + 3 < NV) step(v + 3, std::integral_constant<int, 3>{});
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the zero copies past the last visit
+    __syncthreads();
+    const bool bad = s_bad || __any(bad_page);   // a bad page poisons every column of this workgroup
+
+    // ---- merge the two key halves of each column group, write the partials ----
+    // The second-half waves leave their state in LDS (the first two K
+    // stages, two groups each); the first-half waves merge it into theirs.
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    static_assert(2 * 16 * D * 4 <= BK * D * 2, "two groups' halves fit one K stage");
+    float* half1 = reinterpret_cast<float*>(grp < 2 ? sS0 : sS1) + (grp & 1) * 16 * D;
+    if (sub == 1) {
+        if (gq == 0) {
+            s_m[grp][colh] = m_run;
+            s_l[grp][colh] = l_tot;
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) half1[colh * D + 16 * db + 4 * gq + i] = acc[db][i];
+    }
+    __syncthreads();
+    if (sub == 0 && hvalid) {
+        const float m1 = s_m[grp][colh], l1 = s_l[grp][colh];
+        const float M = fmaxf(m_run, m1);
+        const float f0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
+        const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+        float* o = p.ws + ((((int64_t)b * Lq + jq) * Hq + head) * p.n_split + split) * (D + 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = 16 * db + 4 * gq + i;
+                o[d] = bad ? NAN : f0 * acc[db][i] + f1 * half1[colh * D + d];
+            }
+        if (gq == 0) {
+            o[D] = bad ? NAN : M;
+            o[D + 1] = bad ? NAN : f0 * l_tot + f1 * l1;
+        }
+    }
+}
+
+// Log-sum-exp merge of a (batch, position, head)'s split partials when the
+// splits are few (the kernel above leaves ~256 / (B * Hkv) of them):
+// workgroup of D threads, thread d sums dimension d over the splits in
+// split order with the weights 2^(m_s - M) held in LDS.  A NaN max (bad
+// table or page) makes its weight, and so the output, NaN.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(D) void decode_combine_few_kernel(DecodeParams p) {
+    __shared__ float sW[kDecodeMaxSplits];
+    __shared__ float sRed[D / 64];
+    const int head = blockIdx.x;
+    const int bj = blockIdx.y;   // (batch, query position)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int ns = p.n_split;
+    const float* base = p.ws + ((int64_t)bj * p.Hq + head) * ns * (D + 2);
+    float m = -INFINITY;
+    for (int s = tid; s < ns; s += D) m = fmaxf(m, base[s * (D + 2) + D]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) sRed[wave] = m;
+    __syncthreads();
+    float M = sRed[0];
+#pragma unroll
+    for (int w = 1; w < D / 64; ++w) M = fmaxf(M, sRed[w]);
+    __syncthreads();
+    float l = 0.f;
+    for (int s = tid; s < ns; s += D) {
+        const float ms = base[s * (D + 2) + D];
+        const float wgt = ms == -INFINITY ? 0.f : fast_exp2(ms - M);   // splits without keys
+        sW[s] = wgt;
+        l += wgt * base[s * (D + 2) + D + 1];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+    if (lane == 0) sRed[wave] = l;
+    __syncthreads();
+    float lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) lt += sRed[w];
+    float a = 0.f;
+    for (int s = 0; s < ns; ++s) a += sW[s] * base[s * (D + 2) + tid];
+    const int64_t o = ((int64_t)bj * p.Hq + head) * D + tid;
+    if constexpr (OUT_BF16) static_cast<__bf16*>(p.out)[o] = (__bf16)(a / lt);
+    else static_cast<float*>(p.out)[o] = a / lt;
+    if (tid == 0 && p.lse)
+        p.lse[((int64_t)(bj / p.Lq) * p.Hq + head) * p.Lq + bj % p.Lq] = (M + log2f(lt)) * 0.69314718055994531f;
+}
+
+template <int D, bool OUT_BF16, int NG>
+void launch_multi(const DecodeParams& p, hipStream_t stream) {
+    const dim3 grid(p.n_split, p.Hkv, p.B);
+    if (p.block_table)
+        hipLaunchKernelGGL((decode_multi_kernel<D, OUT_BF16, true, NG>), grid, dim3(128 * NG), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_multi_kernel<D, OUT_BF16, false, NG>), grid, dim3(128 * NG), 0, stream, p);
+    hipLaunchKernelGGL((decode_combine_few_kernel<D, OUT_BF16>), dim3(p.Hq, p.B * p.Lq), dim3(D), 0, stream, p);
 }
 
 template <int D, bool OUT_BF16>
 hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
     const dim3 grid(p.n_split, p.Hkv / p.heads_per_wg, p.B);
-    if (p.block_table)
+    if (p.n_grp > 1) {
+        if (p.n_grp == 2) launch_multi<D, OUT_BF16, 2>(p, stream);
+        else launch_multi<D, OUT_BF16, 4>(p, stream);
+        return hipGetLastError();
+    }
+    if (p.block_table && p.krot)
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, true, true, false>), grid, dim3(kDecThreads), 0,
+                           stream, p);
+    else if (p.block_table)
         hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, true, false, false>), grid, dim3(kDecThreads), 0,
                            stream, p);
     else if (p.krot)
@@ -577,8 +1004,8 @@ hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
                            stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(p.Hq, p.B, D / kCombDims), dim3(kCombThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((decode_combine_kernel<D, OUT_BF16>), dim3(p.Hq, p.B * p.Lq, D / kCombDims),
+                       dim3(kCombThreads), 0, stream, p);
     return hipGetLastError();
 }
 

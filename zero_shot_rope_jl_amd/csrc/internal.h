@@ -70,12 +70,14 @@ enum PrefillMode {
 };
 
 struct DecodeParams {
+    // Lq query positions per sequence, L - Lq .. L - 1 (1 for a decode step):
+    // q and out [B, Lq, Hq, D], lse [B, Hq, Lq]
     const void* q;
     const void* k;
     const void* v;
     void* out;
     float* lse;
-    float* ws;          // split partials (acc[D], max, sum) [B, Hq, n_split, D + 2]
+    float* ws;          // split partials (acc[D], max, sum) [B, Lq, Hq, n_split, D + 2]
     const TableHeader* table;
     const float2* TF;   // (cos, sin)(n theta_i) rows, n < coverage
     int64_t B, L, Lmax, Hq, Hkv;
@@ -85,9 +87,12 @@ struct DecodeParams {
     const int32_t* block_table;
     int64_t page_size, max_pages, n_pages;
     int R;
+    int Lq;             // query positions (R * Lq <= 16 * n_grp)
+    int n_grp;          // 16-column groups of (position, query head) per KV head: 1, 2 or 4
     int n_split;        // workgroups per (batch, KV-head group)
-    int wave_chunk;     // consecutive keys per wave (multiple of 32)
-    int heads_per_wg;   // KV heads per workgroup (waves per head = 8 / heads_per_wg)
+    int wave_chunk;     // consecutive keys per wave (multiple of 32); with 2 or 4
+                        // column groups, per workgroup (multiple of 64)
+    int heads_per_wg;   // KV heads per workgroup of the split kernel (waves per head = 8 / heads_per_wg)
     int64_t w0;
     int64_t G;
     // keys k_lo .. L-1 are read; those >= kloc score in the stored view, the
@@ -100,12 +105,14 @@ struct DecodeParams {
     float sm_scale_log2;
     double rope_base;
     int head_dim;
-    // contiguous caches only: [B, Lmax, Hkv, D] bf16 holding every remote
-    // key (rows < L-1-w0) already in its corrected view under this G, or null
+    // [B, krot_rows, Hkv, D] bf16 by position holding every remote key
+    // (rows below the first query's window) already in its corrected view
+    // under this G, or null
     const void* krot;
-    // with krot: the row to write into krot, rotated under this G, for the
-    // next step (the first local row, which the next step reads as remote
-    // when G stays); -1 for none
+    int64_t krot_rows;
+    // with krot (contiguous caches, Lq = 1): the row to write into krot,
+    // rotated under this G, for the next step (the first local row, which the
+    // next step reads as remote when G stays); -1 for none
     int64_t rot_row;
     TableKey table_key;
     // frequency-interpolation remote view: no table; the kernel forms the
@@ -147,6 +154,28 @@ inline size_t decode_partial_bytes(int64_t B, int64_t Hq, int64_t D, int64_t L) 
 
 inline int decode_heads_per_wg(int64_t Hkv) {
     return Hkv >= kDecodeMaxHeadsPerWG ? kDecodeMaxHeadsPerWG : (int)Hkv;
+}
+
+// Column groups for Lq query positions of R heads each: 16 columns per
+// group, rounded up to 1, 2 or 4 groups; 0 when they need more than 4.
+inline int decode_groups(int64_t Lq, int64_t R) {
+    const int64_t cols = Lq * R;
+    return cols <= 16 ? 1 : cols <= 32 ? 2 : cols <= 64 ? 4 : 0;
+}
+
+// Split plan of the kernel for 2 or 4 column groups: one KV head per
+// workgroup, about 256 workgroups, key ranges in multiples of 64 (its
+// stage).  The split count is at most ceil(256 / (B * Hkv)) and ceil(L / 64).
+constexpr int kMultiStageKeys = 64;
+inline void decode_multi_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* keys_per_wg) {
+    const int64_t groups = B * Hkv;
+    int64_t n = groups >= kDecodeTargetWGs ? 1 : (kDecodeTargetWGs + groups - 1) / groups;
+    const int64_t steps = (L + kMultiStageKeys - 1) / kMultiStageKeys;
+    if (n > steps) n = steps;
+    int64_t per = (L + n - 1) / n;
+    per = (per + kMultiStageKeys - 1) / kMultiStageKeys * kMultiStageKeys;
+    *n_split = (int)((L + per - 1) / per);
+    *keys_per_wg = (int)per;
 }
 
 inline void decode_split_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* wave_chunk) {
@@ -192,6 +221,9 @@ constexpr int kMaxKSplit = 64;
 hipError_t launch_prefill(const PrefillParams& p, int in_dtype, int out_dtype, hipStream_t stream);
 hipError_t launch_ie_merge(const MergeParams& p, int out_dtype, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillParams& p, int out_dtype, hipStream_t stream);
+// bf16 caches with G > 1: rows [rot_lo, L) of p's keys into their corrected
+// view in p.krot (nothing to do otherwise)
+hipError_t launch_rotate_keys(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int out_dtype, hipStream_t stream);
 
 // The fixed device scratch of jl_bifocal_decode_noalloc: its size, and its

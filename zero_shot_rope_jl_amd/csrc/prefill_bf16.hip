@@ -810,14 +810,18 @@ __global__ __launch_bounds__(kCombThreads) void split_combine_kernel(PrefillPara
     }
 }
 
+template <int D, bool PAGED>
+void rotate_keys(const PrefillParams& p, hipStream_t stream) {
+    if (p.G <= 1 || p.rot_lo >= p.L) return;
+    const int64_t n_items = p.B * (p.L - p.rot_lo) * p.Hkv * (D / 16);
+    hipLaunchKernelGGL((rotate_keys_kernel<D, PAGED>), dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.krot), p.TF, n_items, p.L - p.rot_lo,
+                       p.Lkv, (int)p.Hkv, p.G, p);
+}
+
 template <int D, bool OUT_BF16, int MODE, bool PAGED = false>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-    if (p.G > 1 && MODE != kLocalWindow && !p.krot_ready && p.rot_lo < p.L) {
-        const int64_t n_items = p.B * (p.L - p.rot_lo) * p.Hkv * (D / 16);
-        hipLaunchKernelGGL((rotate_keys_kernel<D, PAGED>), dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0,
-                           stream, static_cast<const __bf16*>(p.k), static_cast<__bf16*>(p.krot), p.TF, n_items,
-                           p.L - p.rot_lo, p.Lkv, (int)p.Hkv, p.G, p);
-    }
+    if (MODE != kLocalWindow && !p.krot_ready) rotate_keys<D, PAGED>(p, stream);
     const int64_t blocks = (int64_t)p.n_qtiles * p.Hkv * p.B * p.n_ksplit;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16, MODE, PAGED>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, p);
@@ -839,6 +843,17 @@ hipError_t launch_mode(const PrefillParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_rotate_keys(const PrefillParams& p, hipStream_t stream) {
+    if (p.head_dim == 128) {
+        if (p.block_table) rotate_keys<128, true>(p, stream);
+        else rotate_keys<128, false>(p, stream);
+    } else {
+        if (p.block_table) rotate_keys<64, true>(p, stream);
+        else rotate_keys<64, false>(p, stream);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int out_dtype, hipStream_t stream) {
     const bool ob = out_dtype == 1;
