@@ -130,7 +130,7 @@ __device__ inline float2 fi_cs(double phi, int64_t n) {
     return make_float2(cs, sn);
 }
 
-template <int D, bool OUT_BF16, bool PAGED, bool RKC, bool FI>
+template <int D, bool OUT_BF16, bool PAGED, bool RKC, bool FI, bool MQ = false>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeParams p) {
     constexpr int HALF = D / 2;
     constexpr int NC = D / 32;
@@ -163,12 +163,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     const int Hq = (int)p.Hq;
     const int R = p.R;
     const int G = (int)p.G;
-    const int Lq = p.Lq;
+    const int Lq = MQ ? p.Lq : 1;   // MQ: several query positions (a short chunk)
     // this lane's column: query head rq at position L - Lq + jq (columns past
     // the last position compute on a zero query and are not written)
     const bool hvalid = colh < Lq * R;
-    const int jq = hvalid ? colh / R : Lq - 1;
-    const int rq = hvalid ? colh % R : 0;
+    const int jq = MQ ? (hvalid ? colh / R : Lq - 1) : 0;
+    const int rq = hvalid ? (MQ ? colh % R : colh) : 0;
     const int qpos = L - Lq + jq;
     // keys >= kloc score in the stored view: p.kloc is the last position's
     // edge (q - k <= w0 in the fused step, 0 when G == 1 makes every key
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
                 float v;
                 if (w_loc && w_rem) v = kk >= kloc ? sl[i] : sr[i];
                 else v = w_loc ? sl[i] : sr[i];
-                s[blk][i] = (kk < wend && kk <= qpos) ? v * scale2 : -INFINITY;
+                s[blk][i] = (kk < wend && (!MQ || kk <= qpos)) ? v * scale2 : -INFINITY;
             }
             // this half's K registers are free: start the next step's loads
             if (knext < wend) {
@@ -429,7 +429,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
         }
         float ls = 0.f;
         bf16x8 Bp;
-        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+        // (one position: every step holds a key of every column, so m_run is set)
+        const float m_sub = (MQ && m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -987,7 +988,13 @@ hipError_t launch_dec(const DecodeParams& p, hipStream_t stream) {
         else launch_multi<D, OUT_BF16, 4>(p, stream);
         return hipGetLastError();
     }
-    if (p.block_table && p.krot)
+    if (p.Lq > 1 && p.block_table)   // a short chunk: rotated keys from the chunk workspace
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, true, true, false, true>), grid, dim3(kDecThreads), 0,
+                           stream, p);
+    else if (p.Lq > 1)
+        hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, false, true, false, true>), grid, dim3(kDecThreads),
+                           0, stream, p);
+    else if (p.block_table && p.krot)
         hipLaunchKernelGGL((decode_split_kernel<D, OUT_BF16, true, true, false>), grid, dim3(kDecThreads), 0,
                            stream, p);
     else if (p.block_table)
