@@ -75,7 +75,7 @@ def measured_traffic():
 # the kernels whose HBM traffic the roofline objects report (names as the
 # profiler prints them)
 PREFILL_KERNEL = "jl::prefill_bf16_kernel<128, true, 0, false>"
-DECODE_KERNELS = ("jl::decode_split_kernel<128, true, false, false, false>", "jl::decode_combine_kernel<128, true>")
+DECODE_KERNELS = ("jl::decode_split_kernel<128, true, false, false, false, false>", "jl::decode_combine_kernel<128, true>")
 
 
 def pick(traffic, *prefixes):
