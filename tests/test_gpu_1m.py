@@ -38,7 +38,20 @@ def test_1m_prefill_sampled_rows_and_decode_across_g():
     rows = si.sampled_rows(w.L, w.w0, w.w_pretrained, n_random=256, seed=w.seed)
     o_rows = out[:, rows].cpu().numpy()
     l_rows = lse[:, :, rows].cpu().numpy()
-    del out, lse, q
+    del out, lse
+
+    # the last 16 tokens as one chunk over the whole cache: 64 (position, query
+    # head) columns on the decode kernels' staged path, 256 key splits
+    print("[1m] 16-token chunk", flush=True)
+    Lq = 16
+    co = torch.empty((w.B, Lq, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    cl = torch.empty((w.B, w.Hq, Lq), dtype=torch.float32, device="cuda")
+    jl.jl_bifocal_prefill_chunk(q[:, w.L - Lq:].contiguous(), k, v, co, cl, w.L, w.w0, w.w_pretrained, w.rope_base,
+                                w.sm_scale, table)
+    torch.cuda.synchronize()
+    c_rows = np.arange(w.L - Lq, w.L)
+    co, cl = co.cpu().numpy(), cl.cpu().numpy()
+    del q
 
     print(f"[1m] oracle on {len(rows)} rows x {w.Hq} heads", flush=True)
     q64 = np.zeros((w.B, w.L, w.Hq, w.D))
@@ -51,6 +64,15 @@ def test_1m_prefill_sampled_rows_and_decode_across_g():
     e, el = max_err(o_rows, ref), max_err(l_rows, ref_lse)
     print(f"[1m] prefill err {e:.3e}, lse err {el:.3e}", flush=True)
     assert e <= TOL_BF16 and el <= TOL_BF16
+
+    q64 = np.zeros((w.B, w.L, w.Hq, w.D))
+    q64[:, c_rows] = si.f32_from_bf16_bits(x["q"][:, c_rows])
+    cref, cref_lse = oracle_rows_parallel(q64, k64, v64, c_rows, w.w0, w.w_pretrained, w.rope_base, w.sm_scale,
+                                          workers=8)
+    del q64
+    ce, cel = max_err(co, cref), max_err(cl, cref_lse)
+    print(f"[1m] 16-token chunk err {ce:.3e}, lse err {cel:.3e}", flush=True)
+    assert ce <= TOL_BF16 and cel <= TOL_BF16
 
     # two decode steps: a query at position 2^20 - 1 over the prefilled cache
     # (L = 2^20, G = 4), then one more key appended (L = 2^20 + 1, G = 5)

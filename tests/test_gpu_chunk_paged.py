@@ -116,3 +116,28 @@ def test_out_of_range_page_poisons_the_rows_that_need_it():
     keep = pos < first_wg                     # workgroups that never visit the page
     assert keep.any()
     assert np.array_equal(o[1][keep], good_o[1].cpu().numpy()[keep])
+
+
+@pytest.mark.parametrize("Lq", [2, 16])
+def test_out_of_range_page_on_the_decode_route(Lq):
+    """Short chunks run on the decode kernels (2 tokens: the split kernel, 8
+    columns; 16 tokens: the staged kernel, 4 column groups).  A block-table
+    entry outside the pages poisons every row of its sequence (each row's keys
+    include that page) and leaves the other sequence bit for bit as it was;
+    the rows past L in the last page hold NaN and must not leak either."""
+    require_gpu()
+    B, L, Hq, Hkv, D, ps, w_pre, w0 = 2, 1000, 8, 2, 128, 128, 300, 64
+    w, x, qc, k, v, table = _setup(B, L, Lq, Hq, Hkv, D, w_pre, w0, seed=321 + Lq)
+    kp, vp, bt = _paginate(k, v, L, ps, seed=322 + Lq)
+    good_o, good_l = _paged(w, qc, kp, vp, bt, table, Lq)
+    ref_o, ref_l = _contig(w, qc, k, v, table, Lq)
+    torch.cuda.synchronize()
+    assert torch.isfinite(good_o).all()
+    assert torch.equal(good_o, ref_o) and torch.equal(good_l, ref_l)
+    bad_bt = bt.clone()
+    bad_bt[1, 3] = kp.shape[0] + 7            # keys 384 .. 511, below every row of the chunk
+    out, lse = _paged(w, qc, kp, vp, bad_bt, table, Lq)
+    torch.cuda.synchronize()
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.array_equal(o[0], good_o[0].cpu().numpy()) and np.array_equal(l[0], good_l[0].cpu().numpy())
+    assert np.isnan(o[1]).all() and np.isnan(l[1]).all()
