@@ -208,6 +208,8 @@ SHORT = [  # (B, L, Lq, Hq, Hkv, D, w_pre, w0): chunks of at most 64 columns per
     (1, 900, 64, 8, 8, 128, 300, 50),      # GQA 1: 64 positions in four groups
     (1, 1000, 8, 16, 2, 128, 256, 100),    # GQA 8: 64 columns
     (1, 600, 10, 8, 2, 128, 4096, 50),     # G = 1
+    (1, 300, 16, 8, 2, 64, 1, 3),          # w_pre = 1: G = L, every remote key at position 0
+    (1, 500, 12, 8, 2, 128, 256, 600),     # w0 >= L: every key local although G = 2
 ]
 
 
