@@ -674,6 +674,10 @@ def main():
                          "traffic": pick(traffic, *DECODE_KERNELS),
                          "bytes_per_step": bytes_step},
         }
+    if "chunk" in result and "decode" in result and "lq16_ms" in result["chunk"]:
+        # a 16-token chunk against one decode step over the same 128K cache
+        result["chunk"]["lq16_over_decode_step"] = round(result["chunk"]["lq16_ms"] * 1e3 /
+                                                         result["decode"]["us_per_step"], 3)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
         result["cpu_baseline"] = cpu_baseline(si, w, x, args.cpu_rows)
