@@ -602,8 +602,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
 // wave scores one 32-key half of the step for its 16 columns with the
 // decode kernel's MFMA layout (K rows as A, queries as N columns; V^T
 // through the transposing LDS read).  The copies of all groups' keys are
-// then one HBM read, and the ring keeps ~100 KB per compute unit in flight
-// with no register cost.
+// then one HBM read, and the ring keeps up to 128 KB per compute unit in
+// flight with no register cost.
 //
 // Remote keys are read rotated from p.krot (by position), stored keys from
 // the cache.  A step that holds some column's window edge is visited twice:
@@ -645,8 +645,8 @@ __global__ __launch_bounds__(128 * NG) void decode_multi_kernel(DecodeParams p) 
     constexpr int PU = BK * CH / NT;      // 16-byte copies per thread per operand and stage
     constexpr int RU = NT / CH;           // rows per copy round
     static_assert(PU * NT == BK * CH && RU % CH == 0 && RU % 4 == 0, "copy rounds keep lane-constant swizzles");
-    // four stages, K then V in each, separate objects selected at compile
-    // time so that the copies into one are not taken to alias reads of another
+    // four stages, K then V in each, as separate objects selected at compile
+    // time (every LDS address of a step is then a constant offset)
     __shared__ __attribute__((aligned(16))) __bf16 sS0[2 * BK * D], sS1[2 * BK * D], sS2[2 * BK * D], sS3[2 * BK * D];
     __shared__ float s_m[NG][16], s_l[NG][16];
     __shared__ int s_bad;
