@@ -60,12 +60,12 @@ TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profile
 
 def measured_traffic():
     """HBM bytes per dispatch from the committed PMC summary, keyed by kernel;
-    empty if there is none or the library sources changed since it was taken."""
+    empty if there is none or the library differs from the one it measured."""
     try:
-        from zero_shot_rope_jl_amd.profiling import source_hash
+        from zero_shot_rope_jl_amd.profiling import library_hash
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        if t.get("source_sha256") != source_hash():
+        if t.get("library_sha256") != library_hash():
             return {}
         return {k: (v["fetch_bytes"] or 0.0) + (v["write_bytes"] or 0.0) for k, v in t["kernels"].items()}
     except (OSError, ValueError, KeyError):

@@ -29,18 +29,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CALIBRATION_BYTES = 512 << 20
 
 
-def source_hash() -> str:
-    """sha256 over the library's kernel and ABI sources (csrc/ and include/)."""
+def library_hash() -> str:
+    """sha256 of the built library (its GPU code objects and host code): the
+    counters describe this binary, and a rebuild from unchanged sources is
+    byte-identical, so edits that leave the code as it was keep the hash."""
     h = hashlib.sha256()
-    root = os.path.dirname(PKG)
-    files = sorted(os.path.join(PKG, "csrc", f) for f in os.listdir(os.path.join(PKG, "csrc"))
-                   if f.endswith((".hip", ".h")))
-    files += sorted(os.path.join(root, "include", f) for f in os.listdir(os.path.join(root, "include"))
-                    if f.endswith(".h"))
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+    with open(os.path.join(PKG, "libjetlong.so"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()
 
 
@@ -113,7 +108,7 @@ def traffic_summary(fetch_csv: str, write_csv: str, cmd_fetch: str, cmd_write: s
     return {
         "about": "HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by "
                  "what the counter reads for a plain copy of 512 MiB in the same run",
-        "source_sha256": source_hash(),
+        "library_sha256": library_hash(),
         "copy_calibration": {"bytes_each_way": CALIBRATION_BYTES, "fetch_kib": f_copy, "write_kib": w_copy,
                              "fetch_factor": f_fac, "write_factor": w_fac},
         "kernels": kernels,
