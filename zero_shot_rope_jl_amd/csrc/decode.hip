@@ -10,12 +10,14 @@
 // handles KV head w % WH over sub-range w / WH of the workgroup's keys, so the
 // waves of a workgroup read whole key rows (all heads are contiguous in the
 // cache) and the grid holds about one workgroup per compute unit.  A wave
-// streams its keys 32 per iteration with the next iteration's K and V in
-// flight (non-temporal loads).  K goes straight from HBM into MFMA
-// A-operand registers (rows = keys); V goes through wave-private LDS,
-// transposed, to be the A operand of O^T += V^T P^T.  The R query heads of
-// the KV head are the MFMA N columns (16x16x32 bf16), so each K/V byte is read
-// once per step for all R heads.
+// streams its keys 32 per step through two K register tiles and two LDS V
+// slots: step i + 2's loads go out as step i's tile and slot are consumed
+// (non-temporal loads).  K goes straight from HBM into MFMA A-operand
+// registers (rows = keys); V is copied HBM -> the wave's LDS by buffer loads
+// into LDS and read back transposed (ds_read_b64_tr_b16) as the A operand of
+// O^T += V^T P^T.  The R query heads of the KV head are the MFMA
+// N columns (16x16x32 bf16), so each K/V byte is read once per step for all R
+// heads.
 //
 // Correction without per-key table traffic: for the 32 keys starting at
 // kbase, n(k) = k - floor(k/G) = nb + dn with nb = n(kbase) and 0 <= dn < 32,
@@ -58,7 +60,6 @@ namespace {
 
 constexpr int kDecThreads = kDecodeWaves * 64;
 constexpr int kWaveKeys = 32;
-constexpr int VSTR = kWaveKeys + 8;   // V^T row stride (keys) in LDS
 constexpr int JROWS = kWaveKeys + 1;  // cos/sin(dn * theta) for dn = 0..32
 
 // LDS ordering between lanes of one wave (write -> read, read -> write):
@@ -69,9 +70,7 @@ __device__ inline void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" :::
 template <int D>
 struct DecodeTile {
     static constexpr int NC = D / 32;    // 32-dim K chunks of the QK^T MFMA
-    static constexpr int KPL = D / 16;   // keys per lane in the V transpose
     bf16x8 k[2][NC];                     // rows of the two 16-key blocks
-    bf16x8 v[KPL];                       // V rows for the transpose
 };
 
 // Cache reads are non-temporal: every byte is read once per step, and the
@@ -102,21 +101,6 @@ __device__ inline void load_k(DecodeTile<D>& t, const __bf16* __restrict__ kc, i
     for (int blk = 0; blk < 2; ++blk) load_k_blk<D>(t, kc, cache_b, row, kbase, rbase, kend, colh, gq, blk);
 }
 
-template <int D>
-__device__ inline void load_v(DecodeTile<D>& t, const __bf16* __restrict__ vc, int64_t cache_b, int64_t row,
-                              int kbase, int64_t rbase, int kend, int lane) {
-    constexpr int KPL = DecodeTile<D>::KPL;
-    const int dg = lane % (D / 8);
-    const int kg = lane / (D / 8);
-#pragma unroll
-    for (int e = 0; e < KPL; ++e) {
-        const int dk = kg * KPL + e;
-        t.v[e] = kbase + dk < kend
-                     ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(vc + cache_b + (rbase + dk) * row + dg * 8))
-                     : bf16x8{};
-    }
-}
-
 // (cos, sin)(n * phi) of the frequency-interpolation view, formed in the
 // kernel: the angle is reduced to [-pi, pi] in float64 (n * phi reaches
 // ~1e5 rad), then sin and cos are taken in fp32 (error ~2e-7 rad).
@@ -130,15 +114,20 @@ __device__ inline float2 fi_cs(double phi, int64_t n) {
     return make_float2(cs, sn);
 }
 
+// physical 16-byte chunk of logical chunk c in row `row` of a V slot
+template <int D>
+__device__ inline int dec_vswz(int row, int c) { return c ^ ((4 * (row & 3)) & (D / 8 - 1)); }
+// cache policy of the V copies: non-temporal (streaming)
+constexpr int kNtAux = 2;
+
 template <int D, bool OUT_BF16, bool PAGED, bool RKC, bool FI, bool MQ = false>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodeParams p) {
     constexpr int HALF = D / 2;
     constexpr int NC = D / 32;
     constexpr int NDB = D / 16;       // 16-dim blocks of O^T
-    constexpr int KPL = D / 16;
-    typedef __bf16 VW __attribute__((ext_vector_type(KPL)));
 
-    __shared__ __attribute__((aligned(16))) __bf16 sVt[kDecodeWaves][D * VSTR];
+    __shared__ __attribute__((aligned(16))) __bf16 sV0[kDecodeWaves][kWaveKeys * D];
+    __shared__ __attribute__((aligned(16))) __bf16 sV1[kDecodeWaves][kWaveKeys * D];
     constexpr int JSTR = HALF + 2;    // padded row: rows start on different LDS banks
     __shared__ __attribute__((aligned(16))) float2 sJ[JROWS * JSTR];
     __shared__ __attribute__((aligned(16))) float2 sBase[kDecodeWaves][HALF];
@@ -225,21 +214,46 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     };
     auto row_of = [&](int kb) -> int64_t { return row_in(page_of(kb), kb); };
 
-    // the first step's K and V go out before anything else (the set-up below
-    // waits on the table and q); they stay within the cache whatever the
-    // table check decides
+    // the first two steps' K and V go out before anything else (the set-up
+    // below waits on the table and q); they stay within the cache whatever
+    // the table check decides.  K goes HBM -> registers (two tiles, step i
+    // computes from tile i & 1); V goes HBM -> this wave's LDS slot i & 1 by
+    // buffer loads into LDS (no registers), 16-byte chunks XOR-swizzled by
+    // row for the transposing reads of the PV product.
     const int wstart = (int)p.k_lo + (split * NW + sub) * p.wave_chunk;
     const int wend0 = min(L, wstart + p.wave_chunk);
-    DecodeTile<D> cur;
-    int64_t r_next = 0;   // cache row of the next step's first key
-    int pg_ahead = 0;     // block-table entry of the step after next
+    constexpr int VCH = D / 8;                  // 16-byte chunks per V row
+    constexpr int VRU = 64 / VCH;               // V rows per copy
+    constexpr int VCOPIES = kWaveKeys / VRU;    // copies per step
+    const uint32_t row_bytes = (uint32_t)(row * 2);
+    const uint32_t v_voff =
+        (uint32_t)(lane / VCH) * row_bytes + 16u * (uint32_t)dec_vswz<D>(lane / VCH, lane % VCH);
+    auto stage_v = [&](int kb, int64_t rb, int kend, auto slot) __attribute__((always_inline)) {
+        __bf16* dst = decltype(slot)::value ? sV1[wave] : sV0[wave];
+        const int nrows = min(kend - kb, kWaveKeys);   // rows past the end read as zeros
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vc + cache_b + rb * row, (uint32_t)nrows * row_bytes);
+#pragma unroll
+        for (int u = 0; u < VCOPIES; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dst + u * 512), 16,
+                                                     v_voff, (uint32_t)(u * VRU) * row_bytes, 0, kNtAux);
+    };
+    using Slot0 = std::integral_constant<int, 0>;
+    using Slot1 = std::integral_constant<int, 1>;
+    DecodeTile<D> t0, t1;
+    int pg2 = 0;   // block-table entry of the step two ahead of the current one
     if (wstart < wend0) {
         const int64_t r0 = row_of(wstart);
-        if (rkc_step(wstart)) load_k<D>(cur, krc, krot_b, row, wstart, wstart, wend0, colh, gq);
-        else load_k<D>(cur, kc, cache_b, row, wstart, r0, wend0, colh, gq);
-        load_v<D>(cur, vc, cache_b, row, wstart, r0, wend0, lane);
-        if (wstart + kWaveKeys < wend0) r_next = row_of(wstart + kWaveKeys);
-        if (wstart + 2 * kWaveKeys < wend0) pg_ahead = page_of(wstart + 2 * kWaveKeys);
+        if (rkc_step(wstart)) load_k<D>(t0, krc, krot_b, row, wstart, wstart, wend0, colh, gq);
+        else load_k<D>(t0, kc, cache_b, row, wstart, r0, wend0, colh, gq);
+        stage_v(wstart, r0, wend0, Slot0{});
+        const int k1 = wstart + kWaveKeys;
+        if (k1 < wend0) {
+            const int64_t r1 = row_of(k1);
+            if (rkc_step(k1)) load_k<D>(t1, krc, krot_b, row, k1, k1, wend0, colh, gq);
+            else load_k<D>(t1, kc, cache_b, row, k1, r1, wend0, colh, gq);
+            stage_v(k1, r1, wend0, Slot1{});
+        }
+        if (PAGED && wstart + 2 * kWaveKeys < wend0) pg2 = page_of(wstart + 2 * kWaveKeys);
     }
 
     // rotated-key cache: one wave per (batch, KV head) reads the row that the
@@ -298,7 +312,6 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     float m_run = -INFINITY, l_run = 0.f;
 
     const int wend = bad ? wstart : wend0;
-    __bf16* myV = sVt[wave];
     float2* myBase = sBase[wave];
 
     // cos/sin(nb * theta_lane) of the current step's base offset nb = n(kbase):
@@ -327,27 +340,19 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     };
     if (!RKC && G > 1 && wstart < wend && wstart < kloc_hi) rotate_query(wstart);
 
-    // One register tile (loaded above): each part is reloaded for the next
-    // step as soon as this step has consumed it (V after its transpose, each
-    // 16-key half of K after its scores), so loads stay in flight during the
-    // compute.
-    for (int kbase = wstart; kbase < wend; kbase += kWaveKeys) {
+    // Step i computes from K tile i & 1 and V slot i & 1; as each part is
+    // consumed it is refilled with step i + 2 (each 16-key half of K after
+    // its scores, V after the PV product), so two steps of loads stay in
+    // flight during the compute.
+    const int tr_row = 8 * gq + (colh >> 2);   // transposing read: row and dims this lane addresses
+    const int tr_dim = 4 * (colh & 3);
+    auto step = [&](int kbase, DecodeTile<D>& cur, auto slot) __attribute__((always_inline)) {
         const int knext = kbase + kWaveKeys;
-        // ---- V rows -> V^T in this wave's LDS slice --------------------------
-        {
-            const int dg = lane % (D / 8);
-            const int kg = lane / (D / 8);
-            wave_lds_sync();   // previous iteration's V^T reads are done
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                VW w;
-#pragma unroll
-                for (int e = 0; e < KPL; ++e) w[e] = cur.v[e][d];
-                *reinterpret_cast<VW*>(&myV[(dg * 8 + d) * VSTR + kg * KPL]) = w;
-            }
-        }
-        // V registers are free: start the next step's V loads
-        if (knext < wend) load_v<D>(cur, vc, cache_b, row, knext, r_next, wend, lane);
+        const int k2 = kbase + 2 * kWaveKeys;
+        // rows of step i + 2 (its table entry was read a step ago), then the
+        // table entry of step i + 3
+        const int64_t r2 = k2 < wend ? row_in(pg2, k2) : 0;
+        if (PAGED && k2 + kWaveKeys < wend) pg2 = page_of(k2 + kWaveKeys);
 
         // some column scores a key of this step in the stored view / in the
         // corrected view
@@ -394,10 +399,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
                 else v = w_loc ? sl[i] : sr[i];
                 s[blk][i] = (kk < wend && (!MQ || kk <= qpos)) ? v * scale2 : -INFINITY;
             }
-            // this half's K registers are free: start the next step's loads
-            if (knext < wend) {
-                if (rkc_step(knext)) load_k_blk<D>(cur, krc, krot_b, row, knext, knext, wend, colh, gq, blk);
-                else load_k_blk<D>(cur, kc, cache_b, row, knext, r_next, wend, colh, gq, blk);
+            // this half's K registers are free: start step i + 2's loads
+            if (k2 < wend) {
+                if (rkc_step(k2)) load_k_blk<D>(cur, krc, krot_b, row, k2, k2, wend, colh, gq, blk);
+                else load_k_blk<D>(cur, kc, cache_b, row, k2, r2, wend, colh, gq, blk);
             }
         }
 
@@ -441,26 +446,33 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
             }
         l_run += ls;
 
-        // ---- O^T += V^T P^T ------------------------------------------------------
-        wave_lds_sync();   // V^T written by the other lanes of this wave
+        // ---- O^T += V^T P^T: V^T fragments by transposing reads of the slot ----
+        const __bf16* V = decltype(slot)::value ? sV1[wave] : sV0[wave];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const bf16x8 A = *reinterpret_cast<const bf16x8*>(&myV[(16 * db + colh) * VSTR + 8 * gq]);
+            const int lc = (16 * db + tr_dim) >> 3, wi = tr_dim & 7;
+            const bf16x4 lo = lds_read_tr16(V + tr_row * D + 8 * dec_vswz<D>(tr_row, lc) + wi);
+            const bf16x4 hi = lds_read_tr16(V + (tr_row + 4) * D + 8 * dec_vswz<D>(tr_row + 4, lc) + wi);
+            const bf16x8 A = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bp, acc[db], 0, 0, 0);
         }
+        // the slot is consumed: start step i + 2's V copies into it
+        if (k2 < wend) stage_v(k2, r2, wend, slot);
         if (!RKC && w_rem && knext < wend && lane < HALF) {
-            const int step = (knext - knext / G) - nb;   // 0 <= step <= 32, step < L
-            const float2 j2 = sJ[step * JSTR + lane];
+            const int stp = (knext - knext / G) - nb;   // 0 <= stp <= 32, stp < L
+            const float2 j2 = sJ[stp * JSTR + lane];
             base = make_float2(base.x * j2.x - base.y * j2.y, base.y * j2.x + base.x * j2.y);
         }
         // the next step's corrected query, computed here so that it is off the
         // path from K's arrival to the next K loads
         if (!RKC && G > 1 && knext < wend && knext < kloc_hi) rotate_query(knext);
-        // rows of the step after next (its table entry was read a step ago);
-        // then the table entry of the step after that
-        r_next = knext + kWaveKeys < wend ? row_in(pg_ahead, knext + kWaveKeys) : 0;
-        if (PAGED && knext + 2 * kWaveKeys < wend) pg_ahead = page_of(knext + 2 * kWaveKeys);
+    };
+    for (int kbase = wstart; kbase < wend; kbase += 2 * kWaveKeys) {
+        step(kbase, t0, Slot0{});
+        if (kbase + kWaveKeys < wend) step(kbase + kWaveKeys, t1, Slot1{});
     }
+    // every copy into the V slots has landed before they are reused below
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (bad_page) l_run = NAN;   // poisons this head's output through the merge
     if (write_ahead) {
         // a table that does not match the call leaves NaN in the cache, so
@@ -477,7 +489,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
     __syncthreads();   // every wave is done with its V^T slice
-    float* s_acc = reinterpret_cast<float*>(&sVt[0][0]);   // [wave][16 columns][D]
+    float* s_acc = reinterpret_cast<float*>(&sV0[0][0]);   // [wave][16 columns][D]
+    static_assert(kDecodeWaves * 16 * D * 4 <= kDecodeWaves * kWaveKeys * D * 2, "merge scratch fits");
     if (gq == 0) {
         s_m[wave][colh] = m_run;
         s_l[wave][colh] = l_tot;
@@ -620,13 +633,17 @@ constexpr int kMqStages = 4;   // LDS ring depth
 // s_waitcnt vmcnt (copies complete in issue order) and a barrier before any
 // wave reads it, and a stage is refilled only after a barrier that follows
 // every read of its previous contents.  The instruction writes no register;
-// M0 (the LDS base) needs one wait state before the copy reads it.
+// M0 (the LDS base) needs one wait state before the copy reads it.  The
+// copies are non-temporal (streaming): every byte is read once per call, and
+// the hint cut the 16-token chunk at 128K from 119.8 to 103.3 us.
 __device__ inline void mq_copy16(__amdgpu_buffer_rsrc_t r, const void* lds_base, uint32_t voff, uint32_t soff) {
     const uint32_t m0v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
+    uint32_t saved;   // M0 is reserved to the compiler: restored before the asm ends
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, %4 offen nt lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
                  : "s"(m0v), "v"(voff), "s"(r), "s"(soff)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 template <int D>
