@@ -165,6 +165,28 @@ def test_mismatched_table_poisons_output():
     assert torch.isnan(out).all() and torch.isnan(lse).all()
 
 
+
+@pytest.mark.parametrize("lq", [1, 4, 16])   # decode step; chunks on the decode split and staged kernels
+def test_mismatched_table_poisons_decode_kernels(lq):
+    """A table built for another RoPE base is refused by the decode kernels
+    too: every output element and log-sum-exp comes out NaN."""
+    require_gpu()
+    B, L, Hq, Hkv, D, w_pre, w0, base = 2, 517, 8, 2, 128, 256, 64, 1e4
+    rng = np.random.Generator(np.random.PCG64([L, lq]))
+    bits = lambda shape: si.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32))
+    q, kc, vc = (to_dev(bits(sh), "bf16") for sh in ((B, lq, Hq, D), (B, L, Hkv, D), (B, L, Hkv, D)))
+    wrong = jl.alloc_table(L, D, 5e5, w_pretrained=w_pre)
+    out = torch.empty((B, lq, Hq, D), dtype=torch.float32, device="cuda")
+    if lq == 1:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        ws = jl.alloc_decode_workspace(B, Hq, D, L)
+        jl.jl_bifocal_decode(q, kc, vc, out, lse, L, w0, w_pre, base, D ** -0.5, wrong, ws)
+    else:
+        lse = torch.empty((B, Hq, lq), dtype=torch.float32, device="cuda")
+        jl.jl_bifocal_prefill_chunk(q, kc, vc, out, lse, L, w0, w_pre, base, D ** -0.5, wrong)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all() and torch.isnan(lse).all()
+
 # ------------------------------------------------------- decode (small)
 def _bifocal_scores_log2(x64, L, Hq, Hkv, D, w_pre, w0, base, scale):
     """Dense bifocal score rows [L, Hq, L] in log2 units (-inf above the
