@@ -147,7 +147,11 @@ def build(verbose: bool = False) -> str:
             obj = os.path.join(BUILD, s[:-4] + ".o")
             objs.append(obj)
             extra = PER_FILE_FLAGS.get(s, [])
-            jobs.append(ex.submit(_run, [cc, *flags, *extra, "-c", os.path.join(CSRC, s), "-o", obj], verbose))
+            # a fixed compilation-unit id: by default hipcc hashes it from the
+            # source path, so the same sources built in another directory gave
+            # a library with other bytes
+            cuid = f"-cuid=jl_{s[:-4]}"
+            jobs.append(ex.submit(_run, [cc, *flags, *extra, cuid, "-c", os.path.join(CSRC, s), "-o", obj], verbose))
         cos = [ex.submit(device_code_object, os.path.join(CSRC, s), os.path.join(BUILD, s[:-4] + f".{ARCH}.co"),
                          PER_FILE_FLAGS.get(s, []), verbose) for s in srcs]
         for j in jobs:
