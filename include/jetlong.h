@@ -217,6 +217,8 @@ JL_API int jl_bifocal_prefill_unfused(const void* q, const void* k, const void* 
  *   out     [B, Lq,   Hq,  D]  out_dtype
  *   lse     [B, Hq,   Lq]      fp32, or NULL
  *
+ * Cache rows L..Lmax-1 are never read into the result (they may hold
+ * anything, NaN included).
  * dtypes, D, GQA ratios and table as for jl_bifocal_prefill.  `workspace`
  * must hold jl_bifocal_prefill_chunk_workspace(in_dtype, B, Lq, Lmax, Hq, Hkv,
  * D, w_pretrained) bytes (NULL when that is 0).  It holds the keys in their
@@ -327,7 +329,9 @@ JL_API int jl_bifocal_decode_workspace(int64_t B, int64_t Hq, int64_t D, int64_t
  *   lse      [B, Hq]            fp32 natural log, or NULL
  *
  * L counts every key including the new one; G = max(1, ceil(L/w_pretrained)).
- * Keys with (L-1) - k <= w0 are local, the rest remote.  `workspace` must
+ * Keys with (L-1) - k <= w0 are local, the rest remote.  Cache rows L..Lmax-1
+ * are never read into the result (they may hold anything, NaN included).
+ * `workspace` must
  * hold jl_bifocal_decode_workspace(B, Hq, D, L) bytes.  in_dtype must be
  * JL_BF16.  Errors as for prefill, plus L > Lmax -> JL_EINVAL and a short
  * workspace -> JL_ESPACE.
