@@ -521,7 +521,8 @@ def test_prefill_chunk_workspace_size():
     """Rotated keys [B, Lcap, Hkv, D] bf16 (when G can exceed 1), rounded up to
     256 bytes, then room for the larger of two partial sets: the prefill
     kernels' key splits (a chunk whose query tiles give under 128 workgroups
-    is split over ~512, >= 4 key tiles each, <= 64), and the decode kernels'
+    is split into as many parts as keep it within 256 workgroups, one per
+    compute unit, >= 4 key tiles each, <= 64), and the decode kernels'
     splits for chunks of at most 64 (position, query head) columns per KV
     head ([B, Lq, Hq, n_split, D + 2] fp32, about 256 workgroups)."""
     up = lambda x: (x + 255) // 256 * 256
@@ -533,7 +534,7 @@ def test_prefill_chunk_workspace_size():
             tiles = -(-keys // 128)
             if wgs >= 128 or tiles < 8:
                 continue
-            s = min(-(-512 // wgs), tiles // 4, 64)
+            s = min(256 // wgs, tiles // 4, 64)
             best = max(best, s * lq if s > 1 else 0)
         return best
 
@@ -556,22 +557,23 @@ def test_prefill_chunk_workspace_size():
             best = max(best, B * lq * Hq * n_split * (D + 2) * 4)
         return best
 
-    # 131072-row cache, 16-token chunk, 32/8 heads: 8 workgroups -> 64 prefill
+    # 131072-row cache, 16-token chunk, 32/8 heads: 8 workgroups -> 32 prefill
     # splits, against 32 decode splits of 16 x 32 columns (4 groups, one KV head
-    # per workgroup): the prefill partials are the larger
+    # per workgroup): the prefill partials (132 floats a row) are the larger
     assert dec_bytes(16, 131072) == 16 * 32 * 32 * 130 * 4
     n = jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 16, 131072, 32, 8, 128, 32768)
-    assert n == up(131072 * 8 * 128 * 2) + 64 * 16 * 32 * 132 * 4
+    assert n == up(131072 * 8 * 128 * 2) + 32 * 16 * 32 * 132 * 4
     # a 4096-token chunk fills 512 workgroups and is not split, but a workspace for
     # chunks of up to 4096 tokens has room for the splits of shorter ones: the
-    # largest need is 5 splits x 960 rows (120 workgroups)
+    # largest need is 32 splits x 64 rows (8 workgroups; 960 tokens need 2 x 960)
     n = jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 4096, 131072, 32, 8, 128, 32768)
-    assert need_rows(4096, 131072) == 5 * 960
-    assert n == up(131072 * 8 * 128 * 2) + 5 * 960 * 32 * 132 * 4
-    # up to 256 tokens: room for the largest need, 22 splits x 192 rows (24 workgroups
-    # at 129..192 tokens; 64 tokens need 64 x 64, 256 tokens 16 x 256)
+    assert need_rows(4096, 131072) == 32 * 64
+    assert n == up(131072 * 8 * 128 * 2) + 32 * 64 * 32 * 132 * 4
+    # up to 256 tokens: the same largest need (192 tokens need 10 x 192, 256 tokens
+    # 8 x 256)
+    assert need_rows(256, 131072) == 32 * 64
     n = jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 256, 131072, 32, 8, 128, 32768)
-    assert n == up(131072 * 8 * 128 * 2) + 22 * 192 * 32 * 132 * 4
+    assert n == up(131072 * 8 * 128 * 2) + 32 * 64 * 32 * 132 * 4
     # the size never shrinks as the chunk bound grows
     sizes = [jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, lq, 1500, 8, 2, 128, 400) for lq in range(1, 300)]
     assert all(a <= b for a, b in zip(sizes, sizes[1:]))

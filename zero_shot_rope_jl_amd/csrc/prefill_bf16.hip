@@ -557,6 +557,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
         bool any_msk = false, any_unset = false;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
+            // a block whose rows all lie past L (the last query tile of a call
+            // whose length is not a multiple of its rows) is never stored: it
+            // takes the unmasked path, whose values for it may come out
+            // non-finite and are never read.  Left to the masked path it never
+            // sets a reference max and so slowed every tile of its workgroup.
+            if (pj0[j] >= L) continue;
             bool act, msk;
             block_state(j, rem, k0, act, msk);
             any_msk = any_msk | msk;
