@@ -41,8 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query rows in the CPU-oracle sample")
     ap.add_argument("--skip-decode", action="store_true")
-    ap.add_argument("--chunk-steps", type=int, default=5,
-                    help="calls of the last-4096-token chunk timed, contiguous and paged (0 skips it)")
+    ap.add_argument("--chunk-steps", type=int, default=20,
+                    help="timed calls per chunk length, after 3 untimed ones (0 skips the chunk leg)")
     ap.add_argument("--fi-steps", type=int, default=3,
                     help="timed calls of the prefill with the frequency-interpolation view (0: skip)")
     ap.add_argument("--unfused-steps", type=int, default=3,
@@ -304,7 +304,8 @@ def bench_chunk(torch, jl, args, w, x, page_size=256):
             calls.append((f"lq{Lq}_paged_256_ms", lambda: jl.jl_bifocal_prefill_chunk_paged(
                 qc, kp, vp, bt, out, None, w.L, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table)))
         for name, call in calls:
-            call()
+            for _ in range(3):
+                call()
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             ev0.record(stream)
