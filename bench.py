@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=640, help="query rows in the CPU-oracle sample")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--chunk-steps", type=int, default=20,
-                    help="timed calls per chunk length, after 3 untimed ones (0 skips the chunk leg)")
+                    help="timed calls per chunk length, after 3 untimed ones, in up to 5 batches whose "
+                         "median mean is reported (0 skips the chunk leg)")
     ap.add_argument("--fi-steps", type=int, default=3,
                     help="timed calls of the prefill with the frequency-interpolation view (0: skip)")
     ap.add_argument("--unfused-steps", type=int, default=3,
@@ -306,14 +307,21 @@ def bench_chunk(torch, jl, args, w, x, page_size=256):
         for name, call in calls:
             for _ in range(3):
                 call()
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            # the timed calls in batches back to back: a batch's mean per call can
+            # swing by ~10% from one batch to the next, so the median batch is
+            # reported
+            batches = max(1, min(5, args.chunk_steps))
+            per = max(1, args.chunk_steps // batches)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
             torch.cuda.synchronize()
-            ev0.record(stream)
-            for _ in range(args.chunk_steps):
-                call()
-            ev1.record(stream)
+            evs[0].record(stream)
+            for i in range(batches):
+                for _ in range(per):
+                    call()
+                evs[i + 1].record(stream)
             torch.cuda.synchronize()
-            res[name] = round(ev0.elapsed_time(ev1) / args.chunk_steps, 4)
+            means = [evs[i].elapsed_time(evs[i + 1]) / per for i in range(batches)]
+            res[name] = round(float(np.median(means)), 4)
         del qc, out
     log("[bench] chunks over the 128K cache: " + ", ".join(f"{k} {v:.3f}" for k, v in res.items()))
     del q, k, v, kp, vp, st
