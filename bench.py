@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640, help="query rows in the CPU-oracle sample")
     ap.add_argument("--skip-decode", action="store_true")
-    ap.add_argument("--chunk-steps", type=int, default=20,
+    ap.add_argument("--chunk-steps", type=int, default=100,
                     help="timed calls per chunk length, after 3 untimed ones, in up to 5 batches whose "
                          "median mean is reported (0 skips the chunk leg)")
     ap.add_argument("--fi-steps", type=int, default=3,
