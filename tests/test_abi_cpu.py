@@ -596,3 +596,24 @@ def test_prefill_chunk_workspace_size():
     assert jl.jl_bifocal_prefill_chunk_workspace(jl.JL_F32, 1, 16, 131072, 32, 8, 128, 32768) == 0
     with pytest.raises(jl.JetLongError):
         jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, 1, 17, 16, 32, 8, 128, 32768)
+
+
+def test_prefill_chunk_workspace_is_monotone_over_random_shapes():
+    """The room a chunk workspace sizes for (Lq, Lcap) must cover every call
+    with a chunk of at most Lq tokens over at most Lcap keys: the size never
+    shrinks as either bound grows, over seeded random shapes (bf16, both
+    routes, split and unsplit plans)."""
+    rng = np.random.Generator(np.random.PCG64(99))
+    for _ in range(24):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        B, D, w_pre = int(rng.integers(1, 4)), int(rng.choice([64, 128])), int(rng.integers(16, 5000))
+        ws = lambda lq, cap: jl.jl_bifocal_prefill_chunk_workspace(jl.JL_BF16, B, lq, cap, Hq, Hkv, D, w_pre)
+        caps = sorted(set(int(c) for c in rng.integers(1, 40000, 6)))
+        lqs = sorted(set(int(x) for x in rng.integers(1, 1200, 6)))
+        for cap in caps:
+            sizes = [ws(lq, cap) for lq in lqs if lq <= cap]
+            assert all(a <= b for a, b in zip(sizes, sizes[1:])), (B, Hq, Hkv, D, w_pre, cap)
+        for lq in lqs:
+            sizes = [ws(lq, cap) for cap in caps if cap >= lq]
+            assert all(a <= b for a, b in zip(sizes, sizes[1:])), (B, Hq, Hkv, D, w_pre, lq)
