@@ -50,6 +50,9 @@ def parse():
                     help="calls of the unfused three-pass prefill timed (0 skips it)")
     ap.add_argument("--control-steps", type=int, default=5,
                     help="timed calls of the matched control (same inputs, every pair local); 0 skips it")
+    ap.add_argument("--ref-secs", type=float, default=2.0,
+                    help="seconds of each vendor reference (hipBLASLt bf16 GEMM, device copy) timed after the "
+                         "library's legs; 0 skips them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 512 MiB device-to-device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -600,6 +603,54 @@ def cpu_baseline_decode(si, n_steps=2):
                       f"cached key incl. its remote view), {sec:.1f} s; all {dw.steps} steps extrapolated"}
 
 
+def vendor_references(torch, secs: float) -> dict:
+    """What the vendor's own code reaches on this GPU in the same run: a
+    square bf16 GEMM (torch.matmul, i.e. hipBLASLt) on seeded N(0, 1) inputs
+    like the workload's, and on zeros, each sustained for `secs` so the clock
+    settles under load; and a 1 GiB device-to-device copy (read + write
+    bytes per second).  They frame the published peaks: on random operands the
+    shader clock is held down by power, on zeros it is not."""
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(7)
+    out = {}
+
+    def sustained(fn, work):
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        reps = max(3, int(secs / max(time.perf_counter() - t, 1e-4)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return work * reps / (e0.elapsed_time(e1) * 1e-3)
+
+    for kind in ("random", "zeros"):
+        if kind == "random":
+            a = torch.randn(n, n, device="cuda", generator=g).bfloat16()
+            b = torch.randn(n, n, device="cuda", generator=g).bfloat16()
+        else:
+            a = torch.zeros(n, n, device="cuda", dtype=torch.bfloat16)
+            b = torch.zeros_like(a)
+        c = torch.empty_like(a)
+        out[f"gemm_bf16_{kind}_tflops"] = round(sustained(lambda: torch.matmul(a, b, out=c), 2.0 * n ** 3) / 1e12, 1)
+        del a, b, c
+    nb = 1 << 30
+    src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    out["copy_gbs"] = round(sustained(lambda: dst.copy_(src), 2.0 * nb) / 1e9, 1)
+    del src, dst
+    out["what"] = (f"torch.matmul {n}x{n}x{n} bf16 (hipBLASLt) on seeded N(0,1) inputs and on zeros, and a "
+                   f"{nb >> 30} GiB device copy (read + write bytes), each sustained ~{secs:g} s after the "
+                   "library's legs")
+    log(f"[bench] vendor references: {out}")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -687,6 +738,13 @@ def main():
         # a 16-token chunk against one decode step over the same 128K cache
         result["chunk"]["lq16_over_decode_step"] = round(result["chunk"]["lq16_ms"] * 1e3 /
                                                          result["decode"]["us_per_step"], 3)
+    if args.ref_secs > 0:
+        ref = vendor_references(torch, args.ref_secs)
+        result["vendor_reference"] = ref
+        result["roofline"]["frac_of_vendor_gemm_random"] = round(tflops / ref["gemm_bf16_random_tflops"], 4)
+        if "decode" in result:
+            result["decode"]["roofline"]["frac_of_vendor_copy"] = round(
+                result["decode"]["roofline"]["achieved"] / ref["copy_gbs"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle sample")
         result["cpu_baseline"] = cpu_baseline(si, w, x, args.cpu_rows)
