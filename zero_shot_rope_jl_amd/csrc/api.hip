@@ -723,8 +723,9 @@ void set_decode_range(jl::DecodeParams& p, int64_t L, int mode) {
     case jl::kRemoteWindow: p.k_lo = kwin; p.kloc = none_stored; break;
     default: p.k_lo = 0; p.kloc = p.G == 1 ? 0 : kwin; break;
     }
-    if (p.n_grp > 1) jl::decode_multi_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk);
-    else jl::decode_split_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk);
+    p.wave_extra = 0;
+    if (p.n_grp > 1) jl::decode_multi_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk, &p.wave_extra);
+    else jl::decode_split_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk, &p.wave_extra);
 }
 
 // Both decode entry points.  Contiguous cache: block_table == NULL, k/v

@@ -220,8 +220,13 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     // computes from tile i & 1); V goes HBM -> this wave's LDS slot i & 1 by
     // buffer loads into LDS (no registers), 16-byte chunks XOR-swizzled by
     // row for the transposing reads of the PV product.
-    const int wstart = (int)p.k_lo + (split * NW + sub) * p.wave_chunk;
-    const int wend0 = min(L, wstart + p.wave_chunk);
+    // this wave's share of its head's steps, numbered split-fastest: the
+    // waves that take one step more (the first wave_extra) are the first
+    // waves of as many workgroups, so no compute unit holds more than one
+    // such wave per head, and the heads of a workgroup read the same rows
+    const int wj = sub * p.n_split + split;
+    const int wstart = (int)p.k_lo + wj * p.wave_chunk + 32 * min(wj, p.wave_extra);
+    const int wend0 = min(L, wstart + p.wave_chunk + (wj < p.wave_extra ? 32 : 0));
     constexpr int VCH = D / 8;                  // 16-byte chunks per V row
     constexpr int VRU = 64 / VCH;               // V rows per copy
     constexpr int VCOPIES = kWaveKeys / VRU;    // copies per step
@@ -623,6 +628,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
 // once in the corrected view (keys before each column's edge kept), once in
 // the stored view (the rest).
 constexpr int kMqKeys = 64;    // keys per stage
+static_assert(kMqKeys == kMultiStageKeys, "the host plan deals whole stages");
 constexpr int kMqStages = 4;   // LDS ring depth
 
 // 16-byte buffer -> LDS copy per lane (lane l writes bytes [16l, 16l + 16)
@@ -697,8 +703,8 @@ __global__ __launch_bounds__(128 * NG) void decode_multi_kernel(DecodeParams p) 
 
     // this workgroup's keys [kr0, kr1) in steps of BK; steps [t_rem, t_loc)
     // hold a window edge and are visited twice
-    const int kr0 = split * p.wave_chunk;
-    const int kr1 = min(L, kr0 + p.wave_chunk);
+    const int kr0 = split * p.wave_chunk + kMqKeys * min(split, p.wave_extra);
+    const int kr1 = min(L, kr0 + p.wave_chunk + (split < p.wave_extra ? kMqKeys : 0));
     const int n_steps = kr1 > kr0 ? (kr1 - kr0 + BK - 1) / BK : 0;
     auto clampi = [](int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); };
     const int t_rem = G > 1 ? clampi(kloc_lo - kr0 < 0 ? -1 : (kloc_lo - kr0) / BK, 0, n_steps) : 0;

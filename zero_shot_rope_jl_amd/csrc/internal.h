@@ -92,6 +92,9 @@ struct DecodeParams {
     int n_split;        // workgroups per (batch, KV-head group)
     int wave_chunk;     // consecutive keys per wave (multiple of 32); with 2 or 4
                         // column groups, per workgroup (multiple of 64)
+    int wave_extra;     // waves 0 .. wave_extra-1 of a head take one 32-key step more (split
+                        // kernel); with 2 or 4 column groups, workgroups 0 .. wave_extra-1
+                        // one 64-key stage more
     int heads_per_wg;   // KV heads per workgroup of the split kernel (waves per head = 8 / heads_per_wg)
     int64_t w0;
     int64_t G;
@@ -164,30 +167,37 @@ inline int decode_groups(int64_t Lq, int64_t R) {
 }
 
 // Split plan of the kernel for 2 or 4 column groups: one KV head per
-// workgroup, about 256 workgroups, key ranges in multiples of 64 (its
-// stage).  The split count is at most ceil(256 / (B * Hkv)) and ceil(L / 64).
+// workgroup, about 256 workgroups, key ranges in whole 64-key stages (its
+// step).  The split count is at most ceil(256 / (B * Hkv)) and ceil(L / 64);
+// the stages are dealt as in the split plan below: each workgroup takes
+// floor(stages / n) of them and the first stages % n one more.
 constexpr int kMultiStageKeys = 64;
-inline void decode_multi_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* keys_per_wg) {
+inline void decode_multi_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* keys_per_wg, int* wg_extra) {
     const int64_t groups = B * Hkv;
     int64_t n = groups >= kDecodeTargetWGs ? 1 : (kDecodeTargetWGs + groups - 1) / groups;
     const int64_t steps = (L + kMultiStageKeys - 1) / kMultiStageKeys;
     if (n > steps) n = steps;
-    int64_t per = (L + n - 1) / n;
-    per = (per + kMultiStageKeys - 1) / kMultiStageKeys * kMultiStageKeys;
-    *n_split = (int)((L + per - 1) / per);
-    *keys_per_wg = (int)per;
+    *n_split = (int)n;
+    *keys_per_wg = (int)(steps / n * kMultiStageKeys);
+    *wg_extra = (int)(steps % n);
 }
 
-inline void decode_split_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* wave_chunk) {
+inline void decode_split_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* wave_chunk, int* wave_extra) {
+    // The ceil(L/32) steps of 32 keys of each KV head are dealt over its
+    // waves: every wave takes floor(steps / waves) consecutive steps and the
+    // first steps % waves waves one more, so that every workgroup of the
+    // target grid gets keys (rounding each wave's share up to whole steps
+    // instead would leave some of them idle).
     const int64_t WH = decode_heads_per_wg(Hkv);
     const int64_t NW = kDecodeWaves / WH;
     const int64_t groups = B * (Hkv / WH);
     const int64_t n_target = groups >= kDecodeTargetWGs ? 1 : kDecodeTargetWGs / groups;
-    int64_t per_wave = (L + n_target * NW - 1) / (n_target * NW);
-    per_wave = (per_wave + 31) / 32 * 32;
-    const int64_t chunk = per_wave * NW;
-    *n_split = (int)((L + chunk - 1) / chunk);
-    *wave_chunk = (int)per_wave;
+    const int64_t steps = (L + 31) / 32;
+    const int64_t waves = n_target * NW < steps ? n_target * NW : steps;
+    *n_split = (int)((waves + NW - 1) / NW);
+    const int64_t all = (int64_t)*n_split * NW;
+    *wave_chunk = (int)(steps / all * 32);
+    *wave_extra = (int)(steps % all);
 }
 
 hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double rope_base,
