@@ -107,7 +107,7 @@ def bench_prefill(torch, jl, si, args, w, x):
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device="cuda")
     table = jl.alloc_table(w.L, w.D, w.rope_base)
-    ws = jl.alloc_prefill_workspace(k, w.w_pretrained)   # keys in their remote view, rewritten every step
+    ws = jl.alloc_prefill_workspace(k, w.w_pretrained)   # keys in their remote view (rewritten every step), tile counters
     torch.cuda.synchronize()
 
     def step():
@@ -148,9 +148,10 @@ def bench_control(torch, jl, args, w, x):
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.L), dtype=torch.float32, device="cuda")
     table = jl.alloc_table(w.L, w.D, w.rope_base)
+    ws = jl.alloc_prefill_workspace(k, w.L)   # G = 1: the tile counters only
 
     def step():
-        jl.jl_bifocal_prefill(q, k, v, out, lse, w.w0, w.L, w.rope_base, w.sm_scale, table)
+        jl.jl_bifocal_prefill(q, k, v, out, lse, w.w0, w.L, w.rope_base, w.sm_scale, table, ws)
 
     step()
     stream = torch.cuda.current_stream()

@@ -120,9 +120,12 @@ JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double
 
 /*
  * jl_bifocal_prefill_workspace -- device bytes of scratch jl_bifocal_prefill
- * needs: for bf16 inputs with G = max(1, ceil(L / w_pretrained)) > 1 the
- * keys in their remote view (§3.2 Eq. 5), B * L * Hkv * D bf16, laid out
- * like k; 0 otherwise (fp32 inputs, or every pair local).  Pure host call.
+ * (and jl_bifocal_prefill_fi) needs.  bf16 inputs: when G = max(1,
+ * ceil(L / w_pretrained)) > 1 the keys in their remote view (§3.2 Eq. 5),
+ * B * L * Hkv * D bf16 laid out like k; then, from the next 256-byte
+ * boundary (at offset 0 when G = 1), 1 KiB of counters through which the
+ * workgroups of the attention kernel share out its query tiles.  fp32
+ * inputs: 0.  Pure host call.
  *
  * Errors: bytes == NULL, B, L, Hkv < 1 or L > 2^30, w_pretrained < 1 ->
  * JL_EINVAL; D not in {64, 128} or in_dtype not JL_F32 / JL_BF16 ->
@@ -148,7 +151,8 @@ JL_API int jl_bifocal_prefill_workspace(int in_dtype, int64_t B, int64_t L, int6
  * coverage) the kernels write NaN to `out` (the host cannot read it).
  * `workspace` holds workspace_bytes >= jl_bifocal_prefill_workspace(...)
  * bytes of device scratch, owned by the caller; it may be NULL when that
- * size is 0.  Its contents on entry do not matter and are overwritten, so
+ * size is 0 (fp32 inputs).  Its contents on entry do not matter and are
+ * overwritten (the counters are cleared by a launch of the call itself), so
  * two calls in flight at once need two workspaces.
  *
  * Errors: JL_EINVAL for B, L, Hq, Hkv < 1, Hq % Hkv != 0, w0 < 0,

@@ -103,11 +103,13 @@ def test_prefill_validation(over, code):
 
 
 def test_prefill_workspace_size():
-    # bf16 with G = ceil(L / w_pretrained) > 1: the keys in their remote view, B*L*Hkv*D bf16
-    assert jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 1, 131072, 8, 128, 32768) == 131072 * 8 * 128 * 2
-    assert jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 2, 300, 2, 64, 256) == 2 * 300 * 2 * 64 * 2
-    # G == 1 (every pair local) or fp32 inputs: none
-    assert jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 1, 4096, 8, 128, 4096) == 0
+    up = lambda x: (x + 255) // 256 * 256
+    sched = 8 * 128   # eight tile counters of the bf16 kernel's dynamic grid, one 128-byte line each
+    # bf16 with G = ceil(L / w_pretrained) > 1: the keys in their remote view, B*L*Hkv*D bf16, then the counters
+    assert jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 1, 131072, 8, 128, 32768) == 131072 * 8 * 128 * 2 + sched
+    assert jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 2, 300, 2, 64, 256) == up(2 * 300 * 2 * 64 * 2) + sched
+    # bf16 with G == 1 (every pair local): the counters only; fp32 inputs: none
+    assert jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 1, 4096, 8, 128, 4096) == sched
     assert jl.jl_bifocal_prefill_workspace(jl.JL_F32, 1, 131072, 8, 128, 32768) == 0
     with pytest.raises(jl.JetLongError):
         jl.jl_bifocal_prefill_workspace(jl.JL_BF16, 1, 10, 1, 96, 4)

@@ -135,7 +135,8 @@ def test_prefill_workspace_holds_remote_keys_and_inputs_are_untouched():
     before = [t.clone() for t in (q, k, v)]
     table = jl.alloc_table(w.L, w.D, w.rope_base)
     ws = jl.alloc_prefill_workspace(k, w.w_pretrained)
-    assert ws is not None and ws.numel() == k.numel() * 2
+    nk = k.numel() * 2   # the rotated keys; then, from a 256-byte boundary, 1 KiB of tile counters
+    assert ws is not None and ws.numel() == (nk + 255) // 256 * 256 + 1024
     out1 = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     jl.jl_bifocal_prefill(q, k, v, out1, None, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table, ws)
     torch.cuda.synchronize()
@@ -143,16 +144,16 @@ def test_prefill_workspace_holds_remote_keys_and_inputs_are_untouched():
         assert torch.equal(a, b)
     kb = k.float().cpu().numpy().astype(np.float64)
     ref = oracle.remote_view(kb, np.arange(w.L), oracle.group_size(w.L, w.w_pretrained), w.rope_base)
-    got = ws.view(torch.bfloat16).view(k.shape).float().cpu().numpy().astype(np.float64)
+    got = ws[:nk].view(torch.bfloat16).view(k.shape).float().cpu().numpy().astype(np.float64)
     bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(kb).max()
     assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
-    ws.fill_(0xFF)   # every bf16 of the workspace becomes a NaN
+    ws.fill_(0xFF)   # every bf16 of the workspace becomes a NaN (and the counters 0xFFFFFFFF)
     out2 = torch.empty_like(out1)
     jl.jl_bifocal_prefill(q, k, v, out2, None, w.w0, w.w_pretrained, w.rope_base, w.sm_scale, table, ws)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
-    # every pair local (G == 1): no workspace
-    assert jl.alloc_prefill_workspace(k, w.L) is None
+    # every pair local (G == 1): the tile counters only
+    assert jl.alloc_prefill_workspace(k, w.L).numel() == 1024
 
 
 def test_mismatched_table_poisons_output():

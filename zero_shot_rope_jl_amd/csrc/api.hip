@@ -187,6 +187,20 @@ JL_API int jl_rope_interleaved_to_half(const void* x, void* out, int dtype, int6
     return JL_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// Layout of the whole-sequence prefill's workspace (bf16 inputs): the keys
+// in their corrected view [B, L, Hkv, D] bf16 when G > 1, then (from a
+// 256-byte boundary) the tile counters of the bf16 kernel's dynamic grid.
+size_t prefill_ws_sched_offset(int in_dtype, int64_t B, int64_t L, int64_t Hkv, int64_t D, int64_t w_pretrained) {
+    const bool rotated_keys = in_dtype == JL_BF16 && group_size(L, w_pretrained) > 1;
+    return rotated_keys ? jl::decode_align((size_t)B * (size_t)L * (size_t)Hkv * (size_t)D * 2u) : 0u;
+}
+}  // namespace
+
+extern "C" {
+
 JL_API int jl_bifocal_prefill_workspace(int in_dtype, int64_t B, int64_t L, int64_t Hkv, int64_t D,
                                         int64_t w_pretrained, size_t* bytes) {
     g_err.clear();
@@ -196,8 +210,8 @@ JL_API int jl_bifocal_prefill_workspace(int in_dtype, int64_t B, int64_t L, int6
     if (w_pretrained < 1) return fail(JL_EINVAL, "w_pretrained must be >= 1 (got %lld)", (long long)w_pretrained);
     if (D != 64 && D != 128) return fail(JL_EUNSUPPORTED, "head_dim %lld not supported", (long long)D);
     if (in_dtype != JL_F32 && in_dtype != JL_BF16) return fail(JL_EUNSUPPORTED, "unknown in_dtype %d", in_dtype);
-    const bool rotated_keys = in_dtype == JL_BF16 && group_size(L, w_pretrained) > 1;
-    *bytes = rotated_keys ? (size_t)B * (size_t)L * (size_t)Hkv * (size_t)D * 2u : 0u;
+    *bytes = prefill_ws_sched_offset(in_dtype, B, L, Hkv, D, w_pretrained) +
+             (in_dtype == JL_BF16 ? jl::kSchedBytes : 0u);
     return JL_OK;
 }
 
@@ -484,6 +498,9 @@ int prefill_impl(const char* who, const void* q, const void* k, const void* v, v
     }
     jl::PrefillParams p = make_prefill_params(q, k, v, out, lse, B, Lq, L, Lkv, Hq, Hkv, D, w0, w_pretrained,
                                               rope_base, sm_scale, table, workspace);
+    if (!chunk && in_dtype == JL_BF16)
+        p.sched = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                              prefill_ws_sched_offset(in_dtype, B, L, Hkv, D, w_pretrained));
     if (chunk)
         if (int rc = setup_chunk(who, p, in_dtype, Lkv, D, w_pretrained, workspace, workspace_bytes, state)) return rc;
     if (fi) {

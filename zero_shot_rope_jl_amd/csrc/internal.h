@@ -60,7 +60,21 @@ struct PrefillParams {
     // (then G is set to max(2, L) when L > w_pretrained, so that the row of
     // position p, p - floor(p/G), is p itself)
     TableKey table_key;
+    // bf16 kernel only, whole-sequence calls: non-null makes the grid one
+    // workgroup per compute unit, each taking query tiles from kSchedQueues
+    // counters (zeroed by a launch before the kernel) until all n_tiles are
+    // done; null gives one workgroup per query tile
+    uint32_t* sched;
+    int64_t n_tiles;
 };
+
+// Tile queues of the bf16 prefill's dynamic grid: tile t (in the static
+// grid's order, longest first) sits in queue t % kSchedQueues, which is the
+// XCD that the static grid's round-robin dispatch gives it; each counter on
+// its own 128-byte line.
+constexpr int kSchedQueues = 8;
+constexpr int kSchedStride = 32;
+constexpr size_t kSchedBytes = (size_t)kSchedQueues * kSchedStride * sizeof(uint32_t);
 
 enum PrefillMode {
     kFused = 0,        // q - k <= w0 in the stored view, the rest in the corrected view

@@ -89,8 +89,10 @@ __device__ inline int vswz(int row, int c) {
     return c ^ ((4 * (row & 3)) & (Lay5<D>::CH - 1));
 }
 
+// One query tile (one workgroup's share of the static grid, index `tile_id`
+// in its order): the whole body of the kernel below.
 template <int D, bool OUT_BF16, int MODE, bool PAGED>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p) {
+__device__ __attribute__((always_inline)) inline void prefill_tile(const PrefillParams& p, const int tile_id) {
     using Lay = Lay5<D>;
     constexpr int HALF = Lay::HALF;
     constexpr int NC = Lay::NC;
@@ -108,7 +110,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     __shared__ __attribute__((aligned(16))) __bf16 sV1[BN * D];
     __shared__ int s_bad;
 
-    const int tid = threadIdx.x;
+    // the thread index passes through an empty asm statement, so that the
+    // lane-constant offsets derived from it are formed inside each tile's
+    // body rather than hoisted out of the dynamic grid's loop and kept live
+    // (in registers the body needs) across every tile
+    int tid_opaque = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid_opaque));
+    const int tid = tid_opaque;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5;      // lane half
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
     // Heads vary fastest over the grid so that the workgroups of one KV head
     // land on one XCD (dispatch is round-robin over the 8 XCDs) and share its
     // L2; query tiles are issued longest (last) first.
-    int bid = blockIdx.x;
+    int bid = tile_id;
     const int g = (int)(bid % p.Hkv);
     bid /= (int)p.Hkv;
     const int b = (int)(bid % p.B);
@@ -666,6 +674,59 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p)
 // [B, krot_rows, Hkv, D] by position.  One thread per 8 rotation pairs of a
 // row; HBM-bound (one read and one write of K, table rows shared by the KV
 // heads of a position through L2).
+// The XCD (accelerator complex die, 0..7) the calling wave runs on.
+__device__ inline int xcd_index() {
+    uint32_t x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    return (int)(x & 7u);
+}
+
+// Dynamic grid: the next tile for the workgroup of the calling thread, from
+// the queue of its own XCD while that lasts (the tiles the static grid would
+// have sent there, longest first), then from the other queues in turn; -1
+// once every queue is empty.  The counters only grow, so an empty queue stays
+// empty.
+__device__ inline int next_tile(const PrefillParams& p, int& queue, int& left) {
+    while (left > 0) {
+        const uint32_t i = atomicAdd(p.sched + queue * kSchedStride, 1u);
+        const int64_t t = queue + (int64_t)kSchedQueues * i;
+        if (t < p.n_tiles) return (int)t;
+        queue = (queue + 1) % kSchedQueues;
+        --left;
+    }
+    return -1;
+}
+
+// Static grid (p.sched null): one workgroup per query tile.  Dynamic grid:
+// one workgroup per compute unit, each taking tiles until none is left, so
+// that an XCD that runs faster than another (their clocks differ under the
+// same load) takes over the other's last tiles instead of idling while it
+// finishes them.  Every tile is computed as in the static grid, so the
+// results are the same.
+template <int D, bool OUT_BF16, int MODE, bool PAGED>
+__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillParams p) {
+    __shared__ int s_tile;
+    const bool dyn = p.sched != nullptr;
+    int queue = 0, left = kSchedQueues;
+    if (dyn && threadIdx.x == 0) queue = xcd_index();
+    int tile = (int)blockIdx.x;
+    for (;;) {
+        if (dyn) {
+            if (threadIdx.x == 0) s_tile = next_tile(p, queue, left);
+            __syncthreads();
+            tile = __builtin_amdgcn_readfirstlane(s_tile);
+            __syncthreads();   // read by every wave before thread 0 writes the next one
+            if (tile < 0) break;
+        }
+        prefill_tile<D, OUT_BF16, MODE, PAGED>(p, tile);
+        if (!dyn) break;
+    }
+}
+
+__global__ __launch_bounds__(64) void sched_reset_kernel(uint32_t* s) {
+    if (threadIdx.x < kSchedQueues) s[threadIdx.x * kSchedStride] = 0u;
+}
+
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void rotate_keys_kernel(const __bf16* __restrict__ k, __bf16* __restrict__ kr,
                                                           const float2* __restrict__ TF, int64_t n_items,
@@ -829,8 +890,18 @@ template <int D, bool OUT_BF16, int MODE, bool PAGED = false>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
     if (MODE != kLocalWindow && !p.krot_ready) rotate_keys<D, PAGED>(p, stream);
     const int64_t blocks = (int64_t)p.n_qtiles * p.Hkv * p.B * p.n_ksplit;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16, MODE, PAGED>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, p);
+    // the dynamic grid (one workgroup per compute unit, a workgroup's LDS
+    // fills one) pays when the static grid takes more than two rounds
+    int dev = 0, n_cu = 0;
+    const bool dyn = p.sched && MODE == kFused && !PAGED && p.n_ksplit == 1 && hipGetDevice(&dev) == hipSuccess &&
+                     hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                     n_cu > 0 && blocks > 2 * (int64_t)n_cu;
+    PrefillParams pk = p;
+    pk.sched = dyn ? p.sched : nullptr;
+    pk.n_tiles = blocks;
+    if (dyn) hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, stream, p.sched);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, OUT_BF16, MODE, PAGED>), dim3((unsigned)(dyn ? n_cu : blocks)),
+                       dim3(kThreads), 0, stream, pk);
     if (p.n_ksplit > 1)
         hipLaunchKernelGGL((split_combine_kernel<D, OUT_BF16>), dim3((unsigned)(p.B * p.Lq * p.Hq)),
                            dim3(kCombThreads), 0, stream, p);
