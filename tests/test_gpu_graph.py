@@ -77,3 +77,49 @@ def test_graph_replays_equal_eager_calls():
         bad = [i for i, (g, w) in enumerate(zip(got, want)) if not torch.equal(g, w)]
         print("replay", r, "mismatched tensors", bad)
         assert not bad
+
+
+def test_graph_replays_of_a_prefill_on_the_dynamic_grid():
+    """A prefill large enough for the dynamic grid (its static grid would take
+    more than two rounds of workgroups: 1024 query tiles here) holds a launch
+    that clears its tile counters before the attention kernel; captured in a
+    graph, every replay must clear them again and compute every tile.  The
+    outputs are filled with NaN before each replay, so a replay that skipped
+    tiles would leave NaN behind; every replay must equal the eager call bit
+    for bit, with an eager call on the same workspace in between."""
+    require_gpu()
+    B, L, Hq, Hkv, D, w_pre, w0, base = 1, 8192, 32, 8, 128, 2048, 512, 1e6
+    scale = D ** -0.5
+    n_tiles = (L // (256 // (Hq // Hkv))) * Hkv * B
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"[graph] {n_tiles} query tiles over {n_cu} compute units", flush=True)
+    assert n_tiles > 2 * n_cu
+    rng = np.random.Generator(np.random.PCG64([2024, 2]))
+    bf = lambda *shape: to_dev(si.bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32)), "bf16")
+    q, k, v = bf(B, L, Hq, D), bf(B, L, Hkv, D), bf(B, L, Hkv, D)
+    table = jl.alloc_table(L, D, base)
+    ws = jl.alloc_prefill_workspace(k, w_pre)
+    out = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+
+    def call():
+        jl.jl_bifocal_prefill(q, k, v, out, lse, w0, w_pre, base, scale, table, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    want_out, want_lse = out.clone(), lse.clone()
+    assert torch.isfinite(want_out.float()).all() and torch.isfinite(want_lse).all()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for r in range(3):
+        call()   # eager work on the same workspace (its counters end exhausted)
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = torch.equal(out, want_out) and torch.equal(lse, want_lse)
+        print(f"[graph] dynamic-grid prefill replay {r}: equal to the eager call: {same}", flush=True)
+        assert same
