@@ -122,9 +122,10 @@ __device__ __attribute__((always_inline)) inline void prefill_tile(const Prefill
     const int hh = lane >> 5;      // lane half
     const int col = lane & 31;     // query column of the S^T / O^T tiles
 
-    // Heads vary fastest over the grid so that the workgroups of one KV head
-    // land on one XCD (dispatch is round-robin over the 8 XCDs) and share its
-    // L2; query tiles are issued longest (last) first.
+    // Heads vary fastest over the tile order so that the tiles of one KV head
+    // land on one XCD (the static grid's dispatch is round-robin over the 8
+    // XCDs; the dynamic grid's queues follow it) and share its L2; query
+    // tiles come longest (last) first.
     int bid = tile_id;
     const int g = (int)(bid % p.Hkv);
     bid /= (int)p.Hkv;
