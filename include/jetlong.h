@@ -173,7 +173,8 @@ JL_API int jl_bifocal_prefill(const void* q, const void* k, const void* v, void*
  * jl_bifocal_prefill_unfused needs: the keys in their remote view (bf16
  * inputs with G > 1, as for jl_bifocal_prefill), then three fp32 pass
  * outputs [B, L, Hq, D] and three fp32 log-sum-exps [B, Hq, L], each part at
- * a 256-byte boundary.  Pure host call.  Errors as for
+ * a 256-byte boundary, then (bf16 inputs) 1 KiB of tile counters as in
+ * jl_bifocal_prefill's workspace.  Pure host call.  Errors as for
  * jl_bifocal_prefill_workspace (Hq < 1 -> JL_EINVAL as well).
  */
 JL_API int jl_bifocal_prefill_unfused_workspace(int in_dtype, int64_t B, int64_t L, int64_t Hq,

@@ -95,7 +95,7 @@ JL_API int jl_device_info(int device, int* n_cu, int* max_clock_khz) {
     return JL_OK;
 }
 
-JL_API int jl_version(void) { return 12; }
+JL_API int jl_version(void) { return 13; }
 
 JL_API int jl_schedule(int64_t L, int64_t w_pretrained, int64_t head_dim, double rope_base, int64_t* G_out,
                        void* table, size_t table_bytes, size_t* table_bytes_needed, void* hip_stream) {
@@ -519,7 +519,7 @@ int prefill_impl(const char* who, const void* q, const void* k, const void* v, v
 // then the three passes' fp32 outputs and log-sum-exps, each at a 256-byte
 // boundary.
 struct UnfusedLayout {
-    size_t krot, o[3], l[3], total;
+    size_t krot, o[3], l[3], sched, total;
 };
 
 UnfusedLayout unfused_layout(int in_dtype, int64_t B, int64_t L, int64_t Hq, int64_t Hkv, int64_t D,
@@ -538,7 +538,10 @@ UnfusedLayout unfused_layout(int in_dtype, int64_t B, int64_t L, int64_t Hq, int
         u.l[i] = off;
         off = up(off + (size_t)B * (size_t)Hq * (size_t)L * 4u);
     }
-    u.total = off;
+    // bf16 inputs: the tile counters of the bf16 kernel's dynamic grid (each
+    // pass clears them before it runs)
+    u.sched = off;
+    u.total = off + (in_dtype == JL_BF16 ? jl::kSchedBytes : 0u);
     return u;
 }
 
@@ -628,6 +631,7 @@ JL_API int jl_bifocal_prefill_unfused(const void* q, const void* k, const void* 
                                                   ws + u.krot);
         p.mode = modes[i];
         p.krot_ready = i == 2;
+        if (in_dtype == JL_BF16) p.sched = reinterpret_cast<uint32_t*>(ws + u.sched);
         const hipError_t e = jl::launch_prefill(p, in_dtype, JL_F32, stream);
         if (e != hipSuccess) return fail(JL_EHIP, "%s pass %d launch failed: %s", who, i, hipGetErrorString(e));
     }

@@ -894,7 +894,7 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
     // the dynamic grid (one workgroup per compute unit, a workgroup's LDS
     // fills one) pays when the static grid takes more than two rounds
     int dev = 0, n_cu = 0;
-    const bool dyn = p.sched && MODE == kFused && !PAGED && p.n_ksplit == 1 && hipGetDevice(&dev) == hipSuccess &&
+    const bool dyn = p.sched && !PAGED && p.n_ksplit == 1 && hipGetDevice(&dev) == hipSuccess &&
                      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
                      n_cu > 0 && blocks > 2 * (int64_t)n_cu;
     PrefillParams pk = p;
