@@ -25,11 +25,11 @@ PROG = r"""
 int main() {
     long long B, Hkv, L;
     while (std::scanf("%lld %lld %lld", &B, &Hkv, &L) == 3) {
-        int ns, ch, ex, mns, mch, mex;
-        jl::decode_split_plan(B, Hkv, L, &ns, &ch, &ex);
+        int ns, ch, ex, sf, mns, mch, mex;
+        jl::decode_split_plan(B, Hkv, L, &ns, &ch, &ex, &sf);
         jl::decode_multi_plan(B, Hkv, L, &mns, &mch, &mex);
-        std::printf("%d %d %d %d %d %d %d %d\n", ns, ch, ex, jl::decode_heads_per_wg(Hkv), mns, mch, mex,
-                    jl::kDecodeWaves);
+        std::printf("%d %d %d %d %d %d %d %d %d\n", ns, ch, ex, jl::decode_heads_per_wg(Hkv), mns, mch, mex,
+                    jl::kDecodeWaves, sf);
     }
     return 0;
 }
@@ -63,15 +63,18 @@ def test_plans_cover_every_key_once(planner):
                        text=True, check=True)
     rows = [list(map(int, line.split())) for line in r.stdout.splitlines()]
     assert len(rows) == len(cases)
-    for (B, Hkv, L), (ns, ch, ex, wh, mns, mch, mex, nwaves) in zip(cases, rows):
-        # split kernel: wave (split, sub) of a head takes steps numbered sub * ns + split
+    for (B, Hkv, L), (ns, ch, ex, wh, mns, mch, mex, nwaves, sf) in zip(cases, rows):
+        # split kernel: wave (split, sub) of a head takes the steps numbered
+        # sub * ns + split (split-fastest, the dealt plan) or split * NW + sub
+        # (one KV head per workgroup: whole steps rounded up, no extra steps)
         NW = nwaves // wh
+        assert sf == (0 if wh == 1 else 1) and (sf or ex == 0), (B, Hkv, L)
         assert 1 <= ns <= 256 and ch % 32 == 0 and 0 <= ex < ns * NW, (B, Hkv, L)
         ranges, extra_per_wg = [], {}
         for split in range(ns):
             got = False
             for sub in range(NW):
-                j = sub * ns + split
+                j = sub * ns + split if sf else split * NW + sub
                 lo = j * ch + 32 * min(j, ex)
                 hi = min(L, lo + ch + (32 if j < ex else 0))
                 if lo < hi:

@@ -746,7 +746,8 @@ void set_decode_range(jl::DecodeParams& p, int64_t L, int mode) {
     }
     p.wave_extra = 0;
     if (p.n_grp > 1) jl::decode_multi_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk, &p.wave_extra);
-    else jl::decode_split_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk, &p.wave_extra);
+    else jl::decode_split_plan(p.B, p.Hkv, L - p.k_lo, &p.n_split, &p.wave_chunk, &p.wave_extra,
+                               &p.wave_split_fastest);
 }
 
 // Both decode entry points.  Contiguous cache: block_table == NULL, k/v

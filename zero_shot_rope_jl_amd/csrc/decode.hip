@@ -224,7 +224,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(DecodePara
     // waves that take one step more (the first wave_extra) are the first
     // waves of as many workgroups, so no compute unit holds more than one
     // such wave per head, and the heads of a workgroup read the same rows
-    const int wj = sub * p.n_split + split;
+    // (with one KV head per workgroup the plan numbers them sub-range-
+    // fastest instead, with no extra steps)
+    const int wj = p.wave_split_fastest ? sub * p.n_split + split : split * NW + sub;
     const int wstart = (int)p.k_lo + wj * p.wave_chunk + 32 * min(wj, p.wave_extra);
     const int wend0 = min(L, wstart + p.wave_chunk + (wj < p.wave_extra ? 32 : 0));
     constexpr int VCH = D / 8;                  // 16-byte chunks per V row

@@ -106,9 +106,9 @@ struct DecodeParams {
     int n_split;        // workgroups per (batch, KV-head group)
     int wave_chunk;     // consecutive keys per wave (multiple of 32); with 2 or 4
                         // column groups, per workgroup (multiple of 64)
-    int wave_extra;     // waves 0 .. wave_extra-1 of a head take one 32-key step more (split
-                        // kernel); with 2 or 4 column groups, workgroups 0 .. wave_extra-1
-                        // one 64-key stage more
+    int wave_extra;     // split kernel: waves 0 .. wave_extra-1 of a head take 32 keys more
+    int wave_split_fastest;   // split kernel: a head's waves numbered split-fastest (1) or
+                              // sub-range-fastest (0) along its keys
     int heads_per_wg;   // KV heads per workgroup of the split kernel (waves per head = 8 / heads_per_wg)
     int64_t w0;
     int64_t G;
@@ -196,22 +196,38 @@ inline void decode_multi_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, i
     *wg_extra = (int)(steps % n);
 }
 
-inline void decode_split_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* wave_chunk, int* wave_extra) {
-    // The ceil(L/32) steps of 32 keys of each KV head are dealt over its
-    // waves: every wave takes floor(steps / waves) consecutive steps and the
-    // first steps % waves waves one more, so that every workgroup of the
-    // target grid gets keys (rounding each wave's share up to whole steps
-    // instead would leave some of them idle).
+inline void decode_split_plan(int64_t B, int64_t Hkv, int64_t L, int* n_split, int* wave_chunk, int* wave_extra,
+                              int* wave_split_fastest) {
     const int64_t WH = decode_heads_per_wg(Hkv);
     const int64_t NW = kDecodeWaves / WH;
     const int64_t groups = B * (Hkv / WH);
     const int64_t n_target = groups >= kDecodeTargetWGs ? 1 : kDecodeTargetWGs / groups;
     const int64_t steps = (L + 31) / 32;
+    if (WH == 1) {
+        // One KV head per workgroup (256-byte rows at D = 128): every plan
+        // streams about the same rate, and the fastest measured rounds each
+        // wave's share up to whole steps, a workgroup's waves taking
+        // consecutive ranges.
+        int64_t per_wave = (L + n_target * NW - 1) / (n_target * NW);
+        per_wave = (per_wave + 31) / 32 * 32;
+        *n_split = (int)((L + per_wave * NW - 1) / (per_wave * NW));
+        *wave_chunk = (int)per_wave;
+        *wave_extra = 0;
+        *wave_split_fastest = 0;
+        return;
+    }
+    // The ceil(L/32) steps of 32 keys of each KV head are dealt over its
+    // waves: every wave takes floor(steps / waves) consecutive steps and the
+    // first steps % waves waves one more, so that every workgroup of the
+    // target grid gets keys (rounding each wave's share up to whole steps
+    // instead would leave some of them idle).  The waves are numbered
+    // split-fastest, so those extra steps fall on different workgroups.
     const int64_t waves = n_target * NW < steps ? n_target * NW : steps;
     *n_split = (int)((waves + NW - 1) / NW);
     const int64_t all = (int64_t)*n_split * NW;
     *wave_chunk = (int)(steps / all * 32);
     *wave_extra = (int)(steps % all);
+    *wave_split_fastest = 1;
 }
 
 hipError_t launch_table_fill(void* table, int64_t n_cover, int head_dim, double rope_base,
